@@ -1,0 +1,254 @@
+"""Plain fp64 oracle of the sparse MLA forward path, in numpy.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+CPU-baseline leg of the benchmark. The library and its Python binding never
+import it, and it shares no code with them.
+
+What is computed, with the passage each step follows:
+
+* ``convert_indices`` -- request-local top-k index -> global cache slot via
+  the block table: slot = block_table[req, idx // B] * B + idx % B, -1 stays
+  -1, and the per-row count of valid entries (vLLM "Sparse MLA on Hopper"
+  branch, test_cutlass_fa3_sparse_backend.py, TEST 2.5 "Valid Counts from
+  Index Conversion" and TEST 2.9 "Full fix flow"; cutlass_fa3_sparse.py,
+  ``forward_mqa`` step 2).
+* ``dequantize_rows`` -- cache rows to fp64: bf16 exactly; E4M3FN bytes times
+  the per-tensor scale or the per-token x 128-channel-group scale
+  (flashinfer_mla_sparse_sm90.py, module docstring).
+* ``attention`` -- per query token and head: scores over the token's valid
+  top-k slots, s = scale * q . k over all D channels, softmax, output
+  sum_j p_j * k[:512] in the 512-dim latent space, and LSE = ln sum exp(s)
+  (FA3 kernel test file, ``test_fa3_mla_correctness_vs_reference``: the
+  gathered K = [c_kv | k_rope], V = c_kv, SDPA with the given scale; FlashMLA
+  sparse API docs, ``_forward_fp8_kv_mixed_batch``: LSE per (token, head),
+  rows with no valid slot give (0, -inf)).
+* ``merge_partials`` -- combine partial (out, lse) pairs computed over
+  disjoint slices of a row: the identity element is (0, -inf) (FlashMLA
+  sparse API docs, ``_forward_fp8_kv_mixed_batch``, the cross-rank LSE merge).
+* ``cache_write`` -- write [kv_c(512) | k_pe(d_rope)] rows at slot_mapping,
+  negative slots skipped; bf16 copy, or E4M3 with a given per-tensor scale,
+  or E4M3 with per-token x 128-channel-group scales absmax/448 computed here
+  (branch diff, ``do_kv_cache_update`` / ``concat_and_cache_mla``;
+  flashinfer_mla_sparse_sm90.py docstring on the group-scale layout).
+
+Readings where the pages are silent (each also listed in the design notes):
+entries past the row length, negative entries, out-of-range local indices,
+negative block-table entries and global slots >= num_slots are all invalid
+and skipped; duplicates each count; LSE is the natural log of the scaled
+logits; the FP8 quantizer divides in fp32 and rounds to nearest even with
+saturation at 448.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+from . import e4m3
+
+KV_BF16 = 0
+KV_FP8_PER_TENSOR = 1
+KV_FP8_GROUP128 = 2
+D_V = 512
+GROUP = 128
+
+
+# ---------------------------------------------------------------------------
+# bf16 <-> float
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 is the upper half of an IEEE binary32: value = float32(bits << 16)."""
+    b = np.asarray(bits).view(np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    b = np.asarray(bits).view(np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# index conversion
+# ---------------------------------------------------------------------------
+
+def convert_indices(req_id: np.ndarray, block_table: np.ndarray, topk_local: np.ndarray,
+                    block_size: int, block_stride_rows: Optional[int] = None):
+    """Returns (global [T, K] int32, valid_counts [T] int32).
+
+    slot = block_table[req, l // block_size] * block_stride_rows + l % block_size
+    for every entry l >= 0 whose block number is inside the table and whose
+    table entry is >= 0; every other entry is -1. valid_counts[t] counts the
+    entries that are not -1."""
+    stride = block_size if block_stride_rows is None else block_stride_rows
+    req_id = np.asarray(req_id, dtype=np.int64)
+    bt = np.asarray(block_table, dtype=np.int64)
+    loc = np.asarray(topk_local, dtype=np.int64)
+    T, K = loc.shape
+    max_blocks = bt.shape[1]
+    out = np.full((T, K), -1, dtype=np.int64)
+    for t in range(T):
+        row = loc[t]
+        ok = row >= 0
+        blk = np.where(ok, row // block_size, 0)
+        ok &= blk < max_blocks
+        blk = np.where(ok, blk, 0)
+        entry = bt[req_id[t], blk]
+        ok &= entry >= 0
+        out[t] = np.where(ok, entry * stride + row % block_size, -1)
+    valid = (out >= 0).sum(axis=1)
+    return out.astype(np.int32), valid.astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# dequantization
+# ---------------------------------------------------------------------------
+
+def dequantize_rows(cache: np.ndarray, kv_format: int, slots: np.ndarray,
+                    k_scale: float = 1.0, group_scales: Optional[np.ndarray] = None,
+                    d: Optional[int] = None) -> np.ndarray:
+    """Rows ``slots`` of a flat cache ([S, D] uint16 bf16 bits, or [S, D] uint8
+    E4M3FN codes) as float64 values."""
+    slots = np.asarray(slots, dtype=np.int64)
+    if kv_format == KV_BF16:
+        return bf16_bits_to_f64(cache[slots])
+    vals = e4m3.decode(cache[slots])
+    if kv_format == KV_FP8_PER_TENSOR:
+        return vals * float(np.float32(k_scale))
+    if kv_format == KV_FP8_GROUP128:
+        D = vals.shape[1]
+        sc = np.asarray(group_scales, dtype=np.float32)[slots].astype(np.float64)
+        per_channel = np.repeat(sc, GROUP, axis=1)[:, :D]
+        return vals * per_channel
+    raise ValueError(kv_format)
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def valid_entries(idx_row: np.ndarray, length: Optional[int], num_slots: int) -> np.ndarray:
+    """Entries of one global index row that take part: position < length
+    (when a length is given) and 0 <= slot < num_slots."""
+    row = np.asarray(idx_row, dtype=np.int64)
+    n = row.shape[0] if length is None else max(0, min(int(length), row.shape[0]))
+    row = row[:n]
+    return row[(row >= 0) & (row < num_slots)]
+
+
+def attention_rows(q_t: np.ndarray, rows: np.ndarray, scale: float, d_v: int = D_V):
+    """One query token: q_t [h, D] and its gathered rows [v, D] (fp64).
+    Returns out [h, d_v], lse [h]."""
+    h = q_t.shape[0]
+    if rows.shape[0] == 0:
+        return np.zeros((h, d_v)), np.full(h, -np.inf)
+    s = scale * (q_t @ rows.T)                      # [h, v]
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    out = (p @ rows[:, :d_v]) / l
+    lse = (m + np.log(l))[:, 0]
+    return out, lse
+
+
+def attention(q: np.ndarray, cache: np.ndarray, kv_format: int, indices: np.ndarray,
+              softmax_scale: float, topk_length: Optional[np.ndarray] = None,
+              k_scale: float = 1.0, group_scales: Optional[np.ndarray] = None,
+              tokens: Optional[np.ndarray] = None, d_v: int = D_V):
+    """Sparse MLA forward over global slot indices.
+
+    q: [T, h, D] float64 (already the bf16 values); cache: flat [S, D] in the
+    storage format; indices: [T, K] global slots. Only the listed ``tokens``
+    (default all) are computed. Returns out [n, h, d_v], lse [n, h] fp64."""
+    tokens = np.arange(q.shape[0]) if tokens is None else np.asarray(tokens)
+    S = cache.shape[0]
+    outs, lses = [], []
+    for t in tokens:
+        length = None if topk_length is None else int(topk_length[t])
+        sel = valid_entries(indices[t], length, S)
+        rows = dequantize_rows(cache, kv_format, sel, k_scale, group_scales)
+        o, l = attention_rows(q[t], rows, softmax_scale, d_v)
+        outs.append(o)
+        lses.append(l)
+    h = q.shape[1]
+    if not outs:
+        return np.zeros((0, h, d_v)), np.zeros((0, h))
+    return np.stack(outs), np.stack(lses)
+
+
+def merge_partials(outs: np.ndarray, lses: np.ndarray):
+    """Merge P partial results over disjoint slices: outs [P, ..., d],
+    lses [P, ...]. lse = ln sum_p exp(lse_p); out = sum_p exp(lse_p - lse) out_p.
+    (0, -inf) is the identity; all-identity stays (0, -inf)."""
+    outs = np.asarray(outs, dtype=np.float64)
+    lses = np.asarray(lses, dtype=np.float64)
+    m = lses.max(axis=0)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    w = np.where(np.isfinite(lses), np.exp(lses - m_safe), 0.0)     # [P, ...]
+    tot = w.sum(axis=0)
+    lse = np.where(finite, m_safe + np.log(np.where(finite, tot, 1.0)), -np.inf)
+    out = np.where(finite[..., None],
+                   (w[..., None] * outs).sum(axis=0) / np.where(finite, tot, 1.0)[..., None],
+                   0.0)
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# FP8 quantizer and cache write
+# ---------------------------------------------------------------------------
+
+def quantize_per_tensor(x_bits: np.ndarray, k_scale: float) -> np.ndarray:
+    """bf16 rows -> E4M3FN codes of fl32(x / k_scale)."""
+    x = bf16_bits_to_f32(x_bits)
+    y = (x / np.float32(k_scale)).astype(np.float32)
+    return e4m3.encode_rne(y)
+
+
+def group_scale(absmax: np.ndarray) -> np.ndarray:
+    """fl32(absmax / 448), and 1.0 where a group is all zero."""
+    a = np.asarray(absmax, dtype=np.float32)
+    s = (a / np.float32(448.0)).astype(np.float32)
+    return np.where(a == 0, np.float32(1.0), s).astype(np.float32)
+
+
+def quantize_group128(x_bits: np.ndarray):
+    """bf16 rows [n, D] -> (codes [n, D] uint8, scales [n, ceil(D/128)] fp32).
+    Group g covers channels [128 g, min(128 g + 128, D))."""
+    x = bf16_bits_to_f32(x_bits)
+    n, D = x.shape
+    G = (D + GROUP - 1) // GROUP
+    codes = np.empty((n, D), dtype=np.uint8)
+    scales = np.empty((n, G), dtype=np.float32)
+    for g in range(G):
+        c0, c1 = g * GROUP, min(D, (g + 1) * GROUP)
+        xs = x[:, c0:c1]
+        sc = group_scale(np.abs(xs).max(axis=1))
+        scales[:, g] = sc
+        codes[:, c0:c1] = e4m3.encode_rne((xs / sc[:, None]).astype(np.float32))
+    return codes, scales
+
+
+def cache_write(kv_c_bits: np.ndarray, k_pe_bits: Optional[np.ndarray], slot_mapping: np.ndarray,
+                kv_format: int, cache: np.ndarray, k_scale: float = 1.0,
+                group_scales: Optional[np.ndarray] = None) -> None:
+    """Write rows [kv_c | k_pe] into ``cache`` (flat [S, D]: uint16 bf16 bits or
+    uint8 codes) at slot_mapping; slots < 0 are skipped. In group mode the
+    per-row scales go to ``group_scales`` [S, ceil(D/128)]."""
+    kv_c = np.asarray(kv_c_bits).view(np.uint16)
+    rows = kv_c if k_pe_bits is None or np.asarray(k_pe_bits).shape[-1] == 0 else \
+        np.concatenate([kv_c, np.asarray(k_pe_bits).view(np.uint16)], axis=1)
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    keep = slots >= 0
+    rows, slots = rows[keep], slots[keep]
+    if kv_format == KV_BF16:
+        cache[slots] = rows
+    elif kv_format == KV_FP8_PER_TENSOR:
+        cache[slots] = quantize_per_tensor(rows, k_scale)
+    elif kv_format == KV_FP8_GROUP128:
+        codes, sc = quantize_group128(rows)
+        cache[slots] = codes
+        group_scales[slots] = sc
+    else:
+        raise ValueError(kv_format)

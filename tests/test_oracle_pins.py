@@ -1,0 +1,372 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself:
+the pages' worked examples, library routines, closed forms, invariants and
+brute force on tiny inputs. CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import e4m3
+from oracle import sparse_mla as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _bits(x_f32: torch.Tensor) -> np.ndarray:
+    """bf16 bit patterns of fp32 values rounded by torch."""
+    return x_f32.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _rand_bf16(rng, shape):
+    return _bits(torch.from_numpy(rng.standard_normal(shape).astype(np.float32)))
+
+
+# ---------------------------------------------------------------------------
+# index conversion
+# ---------------------------------------------------------------------------
+
+def test_convert_worked_examples():
+    cases = json.load(open(os.path.join(GOLDEN, "convert_examples.json")))
+    for c in cases["cases"]:
+        g, v = O.convert_indices(np.array(c["req_id"]), np.array(c["block_table"]),
+                                 np.array(c["topk_local"]), c["block_size"])
+        assert g.tolist() == c["expect_global"], c["name"]
+        assert v.tolist() == c["expect_valid"], c["name"]
+
+
+def test_convert_valid_count_case():
+    c = json.load(open(os.path.join(GOLDEN, "convert_examples.json")))["valid_count_case"]
+    rng = np.random.default_rng(25)
+    T, K, NB, B = c["T"], c["topk"], c["num_blocks"], c["block_size"]
+    loc = np.full((T, K), -1, dtype=np.int32)
+    for i, nv in enumerate(c["expect_valid"]):
+        loc[i, :nv] = rng.integers(0, NB * B, nv)
+    g, v = O.convert_indices(np.zeros(T, np.int32), np.arange(NB)[None], loc, B)
+    assert v.tolist() == c["expect_valid"]
+    for i, nv in enumerate(c["expect_valid"]):
+        assert (g[i, nv:] == -1).all()
+        assert (g[i, :nv] == loc[i, :nv]).all()     # identity table
+
+
+def test_convert_brute_force_random_tables():
+    """Pure-Python per-entry evaluation, including invalid corners: negative
+    entries, local indices past the table, negative table entries."""
+    rng = np.random.default_rng(7)
+    R, MB, B, T, K = 3, 5, 16, 6, 12
+    bt = rng.permutation(R * MB).reshape(R, MB).astype(np.int32)
+    bt[1, 2] = -1
+    req = rng.integers(0, R, T).astype(np.int32)
+    loc = rng.integers(-3, MB * B + 10, (T, K)).astype(np.int32)
+    for stride in (B, 2 * B):
+        g, v = O.convert_indices(req, bt, loc, B, stride)
+        for t in range(T):
+            cnt = 0
+            for j in range(K):
+                l = int(loc[t, j])
+                if l < 0 or l // B >= MB or bt[req[t], l // B] < 0:
+                    want = -1
+                else:
+                    want = int(bt[req[t], l // B]) * stride + l % B
+                    cnt += 1
+                assert g[t, j] == want
+            assert v[t] == cnt
+
+
+# ---------------------------------------------------------------------------
+# E4M3FN format and quantizer
+# ---------------------------------------------------------------------------
+
+def test_e4m3_table_matches_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = e4m3.DECODE_TABLE
+    nan = np.isnan(ref)
+    assert (np.isnan(ours) == nan).all()
+    assert (ours[~nan] == ref[~nan]).all()
+    assert np.isnan(ours[0x7F]) and np.isnan(ours[0xFF])
+    assert ours[0x7E] == 448.0 and ours[0xFE] == -448.0
+    assert ours[0x01] == 2.0 ** -9 and ours[0x38] == 1.0
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    rng = np.random.default_rng(3)
+    y = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * 40,
+        rng.uniform(-447.9, 447.9, 50000).astype(np.float32),
+        (rng.standard_normal(20000) * 1e-3).astype(np.float32),
+        # exact midpoints between neighbouring codes (ties to even)
+        ((e4m3.DECODE_TABLE[1:0x7E] + e4m3.DECODE_TABLE[2:0x7F]) / 2).astype(np.float32),
+        e4m3.DECODE_TABLE[:0x7F].astype(np.float32),
+    ])
+    ours = e4m3.encode_rne(y)
+    ref = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (ours == ref).all()
+
+
+def test_e4m3_encode_saturates_and_nan():
+    y = np.array([448.0, 449.0, 463.9, 464.0, 1e6, np.inf, -1e6, -np.inf, np.nan], np.float32)
+    c = e4m3.encode_rne(y)
+    assert c[:6].tolist() == [0x7E] * 6
+    assert c[6:8].tolist() == [0xFE] * 2
+    assert c[8] & 0x7F == 0x7F
+
+
+def test_group_quantizer_roundtrip_bound():
+    """Every group's absmax element lands on +-448 and the decoded value is
+    within half an E4M3 ulp of x / scale."""
+    rng = np.random.default_rng(11)
+    x = _rand_bf16(rng, (64, 576))
+    codes, sc = O.quantize_group128(x)
+    assert sc.shape == (64, 5)
+    xf = O.bf16_bits_to_f32(x).astype(np.float64)
+    dec = e4m3.decode(codes)
+    for g in range(5):
+        c0, c1 = 128 * g, min(576, 128 * g + 128)
+        amax = np.abs(xf[:, c0:c1]).max(axis=1)
+        assert np.allclose(sc[:, g], (amax / 448.0).astype(np.float32), rtol=0, atol=0)
+        y = xf[:, c0:c1] / sc[:, g:g + 1]
+        assert (np.abs(dec[:, c0:c1]).max(axis=1) == 448.0).all()
+        # relative spacing of E4M3 normals is 1/8 -> error <= 1/16 relative (+ subnormal floor)
+        err = np.abs(dec[:, c0:c1] - y)
+        assert (err <= np.abs(y) / 16 + 2.0 ** -10 + 1e-12).all()
+
+
+def test_group_quantizer_zero_group_scale_is_one():
+    x = np.zeros((2, 512), np.uint16)
+    codes, sc = O.quantize_group128(x)
+    assert (sc == 1.0).all() and (codes == 0).all()
+
+
+def test_cache_write_bf16_roundtrip_and_skip():
+    """Cache write then read back equals the written rows, negative slots are
+    skipped (branch diff, test_kv_cache_write_read_consistency)."""
+    rng = np.random.default_rng(5)
+    S, T = 16, 5
+    kv_c, k_pe = _rand_bf16(rng, (T, 512)), _rand_bf16(rng, (T, 64))
+    slots = np.array([3, -1, 0, 15, 7])
+    cache = np.zeros((S, 576), np.uint16)
+    O.cache_write(kv_c, k_pe, slots, O.KV_BF16, cache)
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        assert (cache[s, :512] == kv_c[t]).all() and (cache[s, 512:] == k_pe[t]).all()
+    untouched = [s for s in range(S) if s not in slots]
+    assert (cache[untouched] == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def _setup(rng, T=3, h=4, D=576, S=200, K=40):
+    q = O.bf16_bits_to_f64(_rand_bf16(rng, (T, h, D)))
+    cache = _rand_bf16(rng, (S, D))
+    idx = np.stack([rng.permutation(S)[:K] for _ in range(T)]).astype(np.int32)
+    return q, cache, idx
+
+
+def test_dense_special_case_matches_sdpa():
+    """Index rows listing every context slot = dense attention (the pages'
+    kernel tests use SDPA as the reference)."""
+    rng = np.random.default_rng(1)
+    T, h, D, S = 2, 8, 576, 96
+    q = O.bf16_bits_to_f64(_rand_bf16(rng, (T, h, D)))
+    cache = _rand_bf16(rng, (S, D))
+    idx = np.stack([rng.permutation(S) for _ in range(T)]).astype(np.int32)
+    out, lse = O.attention(q, cache, O.KV_BF16, idx, 0.07)
+    kv = torch.from_numpy(O.bf16_bits_to_f64(cache))
+    for t in range(T):
+        qt = torch.from_numpy(q[t])[None, :, None, :]             # [1, h, 1, D]
+        k = kv[None, None].expand(1, h, S, D)
+        v = kv[None, None, :, :512].expand(1, h, S, 512)
+        ref = F.scaled_dot_product_attention(qt, k, v, scale=0.07)[0, :, 0]
+        assert np.abs(out[t] - ref.numpy()).max() < 1e-12
+        ref_lse = torch.logsumexp(0.07 * (torch.from_numpy(q[t]) @ kv.T), dim=-1)
+        assert np.abs(lse[t] - ref_lse.numpy()).max() < 1e-12
+
+
+def test_permutation_invariance():
+    rng = np.random.default_rng(2)
+    q, cache, idx = _setup(rng)
+    out, lse = O.attention(q, cache, O.KV_BF16, idx, 0.05)
+    perm = np.stack([rng.permutation(row) for row in idx])
+    out2, lse2 = O.attention(q, cache, O.KV_BF16, perm, 0.05)
+    assert np.abs(out - out2).max() < 1e-12 and np.abs(lse - lse2).max() < 1e-12
+
+
+def test_single_valid_slot_is_that_row():
+    rng = np.random.default_rng(3)
+    q, cache, idx = _setup(rng)
+    idx[:, 1:] = -1
+    out, lse = O.attention(q, cache, O.KV_BF16, idx, 0.05)
+    for t in range(q.shape[0]):
+        row = O.bf16_bits_to_f64(cache[idx[t, 0]])
+        assert (out[t] == row[None, :512]).all()
+        assert np.allclose(lse[t], 0.05 * q[t] @ row, rtol=0, atol=1e-12)
+
+
+def test_lse_closed_forms():
+    rng = np.random.default_rng(4)
+    q, cache, idx = _setup(rng, K=10)
+    # all entries the same slot: lse = s + ln v, out = that row
+    same = np.repeat(idx[:, :1], 10, axis=1)
+    out, lse = O.attention(q, cache, O.KV_BF16, same, 0.05)
+    for t in range(q.shape[0]):
+        row = O.bf16_bits_to_f64(cache[same[t, 0]])
+        assert np.allclose(lse[t], 0.05 * q[t] @ row + math.log(10), atol=1e-12)
+        assert np.allclose(out[t], row[None, :512], atol=1e-12)
+    # small logits: ln sum exp without max subtraction
+    out, lse = O.attention(q, cache, O.KV_BF16, idx, 1e-3)
+    for t in range(q.shape[0]):
+        rows = O.bf16_bits_to_f64(cache[idx[t]])
+        direct = np.log(np.exp(1e-3 * q[t] @ rows.T).sum(axis=1))
+        assert np.abs(lse[t] - direct).max() < 1e-12
+
+
+def test_minus_one_insensitivity_and_length_bound():
+    rng = np.random.default_rng(5)
+    q, cache, idx = _setup(rng, K=20)
+    out, lse = O.attention(q, cache, O.KV_BF16, idx, 0.05)
+    # scatter -1 (and other negatives, and out-of-range slots) between entries
+    wide = np.full((idx.shape[0], 50), -1, np.int32)
+    for t in range(idx.shape[0]):
+        pos = np.sort(rng.choice(50, 20, replace=False))
+        wide[t, pos] = idx[t]
+        holes = np.setdiff1d(np.arange(50), pos)
+        wide[t, holes[:3]] = [-7, 10 ** 6, cache.shape[0]]
+    out2, lse2 = O.attention(q, cache, O.KV_BF16, wide, 0.05)
+    assert np.abs(out - out2).max() < 1e-12 and np.abs(lse - lse2).max() < 1e-12
+    # a row length bounds the scan: the tail past it is ignored whatever it holds
+    tail = np.concatenate([idx, idx[:, :5]], axis=1)
+    out3, lse3 = O.attention(q, cache, O.KV_BF16, tail, 0.05,
+                             topk_length=np.full(idx.shape[0], 20))
+    assert np.abs(out - out3).max() < 1e-12 and np.abs(lse - lse3).max() < 1e-12
+
+
+def test_empty_row_is_merge_identity():
+    rng = np.random.default_rng(6)
+    q, cache, idx = _setup(rng)
+    idx[1, :] = -1
+    out, lse = O.attention(q, cache, O.KV_BF16, idx, 0.05, topk_length=np.array([40, 40, 0]))
+    assert (out[1] == 0).all() and np.isneginf(lse[1]).all()
+    assert (out[2] == 0).all() and np.isneginf(lse[2]).all()
+    assert np.isfinite(lse[0]).all()
+
+
+def test_brute_force_tiny():
+    """Nested Python loops over the definition softmax_j = exp(s_j)/sum exp(s)."""
+    rng = np.random.default_rng(8)
+    for h, K in ((1, 1), (2, 5), (2, 8)):
+        T, D, S = 2, 576, 30
+        q, cache, idx = _setup(rng, T=T, h=h, D=D, S=S, K=K)
+        idx[0, -1] = -1
+        out, lse = O.attention(q, cache, O.KV_BF16, idx, 0.04)
+        kv = O.bf16_bits_to_f64(cache)
+        for t in range(T):
+            for i in range(h):
+                ss = []
+                for j in range(K):
+                    g = int(idx[t, j])
+                    if g < 0:
+                        continue
+                    ss.append((0.04 * sum(q[t, i, d] * kv[g, d] for d in range(D)), g))
+                if not ss:
+                    assert np.isneginf(lse[t, i]) and (out[t, i] == 0).all()
+                    continue
+                tot = sum(math.exp(s) for s, _ in ss)
+                assert abs(lse[t, i] - math.log(tot)) < 1e-10
+                for c in range(0, 512, 37):
+                    want = sum(math.exp(s) * kv[g, c] for s, g in ss) / tot
+                    assert abs(out[t, i, c] - want) < 1e-10
+
+
+def test_heads_are_independent():
+    """A subset of heads gives the same result as the full set (head padding
+    with zero rows only adds heads that are then dropped)."""
+    rng = np.random.default_rng(9)
+    q, cache, idx = _setup(rng, h=6)
+    out, lse = O.attention(q, cache, O.KV_BF16, idx, 0.05)
+    out2, lse2 = O.attention(q[:, 2:5], cache, O.KV_BF16, idx, 0.05)
+    assert (out[:, 2:5] == out2).all() and (lse[:, 2:5] == lse2).all()
+    qp = np.concatenate([q, np.zeros((q.shape[0], 58, q.shape[2]))], axis=1)
+    out3, lse3 = O.attention(qp, cache, O.KV_BF16, idx, 0.05)
+    assert (out3[:, :6] == out).all() and (lse3[:, :6] == lse).all()
+
+
+def test_split_merge_identity():
+    rng = np.random.default_rng(10)
+    q, cache, idx = _setup(rng, K=40)
+    out, lse = O.attention(q, cache, O.KV_BF16, idx, 0.05)
+    parts_o, parts_l = [], []
+    for a, b in ((0, 7), (7, 7), (7, 30), (30, 40)):     # includes an empty slice
+        sl = np.full_like(idx, -1)
+        sl[:, a:b] = idx[:, a:b]
+        o, l = O.attention(q, cache, O.KV_BF16, sl, 0.05)
+        parts_o.append(o)
+        parts_l.append(l)
+    mo, ml = O.merge_partials(np.stack(parts_o), np.stack(parts_l))
+    assert np.abs(mo - out).max() < 1e-12 and np.abs(ml - lse).max() < 1e-12
+    eo, el = O.merge_partials(np.zeros((2, 1, 3)), np.full((2, 1), -np.inf))
+    assert (eo == 0).all() and np.isneginf(el).all()
+
+
+def test_fp8_per_tensor_dequant_is_code_times_scale():
+    rng = np.random.default_rng(12)
+    codes = rng.integers(0, 256, (8, 512)).astype(np.uint8)
+    codes[codes & 0x7F == 0x7F] = 0
+    v = O.dequantize_rows(codes, O.KV_FP8_PER_TENSOR, np.arange(8), k_scale=0.01)
+    ref = codes.view(np.uint8)
+    ref = torch.from_numpy(ref).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert (v == ref * float(np.float32(0.01))).all()
+
+
+def test_fp8_group_dequant_uses_row_group_scale():
+    rng = np.random.default_rng(13)
+    codes = rng.integers(0, 0x7E, (6, 576)).astype(np.uint8)
+    scales = rng.uniform(0.001, 0.02, (10, 5)).astype(np.float32)
+    slots = np.array([9, 0, 4])
+    v = O.dequantize_rows(np.concatenate([codes, codes[:4]]), O.KV_FP8_GROUP128, slots,
+                          group_scales=scales)
+    full = np.concatenate([codes, codes[:4]])
+    for r, s in enumerate(slots):
+        for c in (0, 127, 128, 300, 511, 512, 575):
+            assert v[r, c] == e4m3.DECODE_TABLE[full[s, c]] * float(scales[s, c // 128])
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must be caught by one of the pins above
+# ---------------------------------------------------------------------------
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    rng = np.random.default_rng(14)
+    q, cache, idx = _setup(rng, T=1, h=2, K=6)
+    kv = O.bf16_bits_to_f64(cache)
+
+    def brute(t, i):
+        ss = [(0.05 * float(q[t, i] @ kv[g]), g) for g in idx[t] if g >= 0]
+        tot = sum(math.exp(s) for s, _ in ss)
+        return math.log(tot), sum(math.exp(s) * kv[g, :512] for s, g in ss) / tot
+
+    good_out, good_lse = O.attention(q, cache, O.KV_BF16, idx, 0.05)
+    bl, bo = brute(0, 1)
+    assert abs(good_lse[0, 1] - bl) < 1e-10 and np.abs(good_out[0, 1] - bo).max() < 1e-10
+
+    real = O.attention_rows
+
+    def no_max_in_lse(q_t, rows, scale, d_v=512):       # dropped term
+        o, l = real(q_t, rows, scale, d_v)
+        s = scale * (q_t @ rows.T)
+        return o, l - s.max(axis=1)
+
+    def rope_dropped(q_t, rows, scale, d_v=512):         # wrong channel range
+        return real(q_t[:, :512], rows[:, :512], scale, d_v)
+
+    for bad in (no_max_in_lse, rope_dropped):
+        monkeypatch.setattr(O, "attention_rows", bad)
+        o, l = O.attention(q, cache, O.KV_BF16, idx, 0.05)
+        assert abs(l[0, 1] - bl) > 1e-6 or np.abs(o[0, 1] - bo).max() > 1e-6
+        monkeypatch.setattr(O, "attention_rows", real)
