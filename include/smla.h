@@ -1,0 +1,189 @@
+/*
+ * smla.h -- C ABI of the sparse multi-head latent attention (MLA) forward
+ * path on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes is fixed by the pages it follows:
+ *
+ *  - vLLM "Sparse MLA on Hopper" branch (compare bz/sleep-metric...
+ *    rebase-fa3-mla-sparse): backends/mla/cutlass_fa3_sparse.py
+ *    (CutlassFA3MLASparseImpl.forward_mqa, _forward_fa3, do_kv_cache_update)
+ *    and tests/v1/attention/test_cutlass_fa3_sparse_backend.py;
+ *  - the FA3 kernel test file of the same branch (compare rebase-fa3-mla-
+ *    sparse..cutlass_fa3_mla_sparse), test_fa3_mla_correctness_vs_reference;
+ *  - vLLM API docs, vllm.v1.attention.backends.mla.flashmla_sparse
+ *    (FlashMLASparseImpl: head padding, _forward_fp8_kv_mixed_batch LSE);
+ *  - flashinfer_mla_sparse_sm90.py (module docstring: NoPE, FP8 E4M3 cache
+ *    with per-tensor or per-token x 128-channel-group scales; forward_mqa).
+ *
+ * Every query token t has h heads q[t, i, 0:D] (D = 512 latent channels
+ * followed by d_rope = 64 rope channels, or d_rope = 0 for NoPE) and one
+ * row of top-k global cache slots shared by all of its heads. Over the
+ * valid entries j of that row (position j < topk_length[t] when a length
+ * array is given, and 0 <= slot < num_slots):
+ *     s_j   = softmax_scale * sum_d q[t,i,d] * kv[slot_j, d]      (d < D)
+ *     out   = sum_j softmax(s)_j * kv[slot_j, 0:512]               (latent)
+ *     lse   = ln sum_j exp(s_j)
+ * A row with no valid entry gives out = 0 and lse = -inf.
+ *
+ * Conventions for every entry point:
+ *  - All pointers are DEVICE pointers unless stated otherwise; the caller
+ *    owns every buffer. The library allocates nothing per call.
+ *  - Calls only enqueue work on `stream` (a hipStream_t, NULL = default
+ *    stream); they never synchronise the host, and the launch plan depends
+ *    on shapes only, so the calls can be captured in a HIP graph.
+ *  - Arguments are checked on the host; a bad argument returns
+ *    SMLA_ERR_INVALID_ARG or SMLA_ERR_UNSUPPORTED without launching
+ *    anything, and smla_last_error() describes it. A failed launch returns
+ *    SMLA_ERR_HIP. No C++ exception crosses this interface.
+ *  - bf16 tensors are passed as raw 16-bit storage; strides are in
+ *    ELEMENTS of the tensor's own type unless named *_bytes.
+ */
+#ifndef SMLA_H_
+#define SMLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SMLA_OK = 0,
+  SMLA_ERR_INVALID_ARG = -1,
+  SMLA_ERR_UNSUPPORTED = -2,
+  SMLA_ERR_WORKSPACE_TOO_SMALL = -3,
+  SMLA_ERR_HIP = -4
+} smla_status;
+
+/* Cache row storage formats (flashinfer_mla_sparse_sm90.py docstring;
+ * vLLM kv_cache_dtype "auto"/"bfloat16" and "fp8"/"fp8_e4m3"). */
+typedef enum {
+  /* row = D bf16 values */
+  SMLA_KV_BF16 = 0,
+  /* row = D OCP E4M3FN bytes; value = e4m3(byte) * k_scale */
+  SMLA_KV_FP8_E4M3_PER_TENSOR = 1,
+  /* row = D OCP E4M3FN bytes; value = e4m3(byte) * group_scales[slot][c/128]
+   * with group_scales a separate fp32 [num_slots][ceil(D/128)] array */
+  SMLA_KV_FP8_E4M3_GROUP128 = 2
+} smla_kv_format;
+
+/* Arguments of the attention entry points. */
+typedef struct {
+  /* Query, bf16. q_nope: [T][h][512]; q_rope: [T][h][d_rope], may be NULL
+   * iff d_rope == 0. Both may be views of one [T][h][576] tensor. */
+  const void* q_nope;
+  int64_t q_nope_stride_tok, q_nope_stride_head;
+  const void* q_rope;
+  int64_t q_rope_stride_tok, q_rope_stride_head;
+  int32_t num_tokens;   /* T >= 0 */
+  int32_t num_heads;    /* h, 1..128; padded internally to 64 or 128 with zero heads */
+  int32_t d_rope;       /* 64, or 0 for NoPE (D = 512 + d_rope) */
+
+  /* Latent cache: num_slots rows, kv_row_stride_bytes apart (a paged
+   * [num_blocks][block_size][D] cache is num_blocks*block_size rows). The
+   * row stride must be a multiple of 16 bytes and the base 16-byte aligned. */
+  const void* kv_cache;
+  int64_t num_slots;
+  int64_t kv_row_stride_bytes;
+  int32_t kv_format;            /* smla_kv_format */
+  float k_scale;                /* SMLA_KV_FP8_E4M3_PER_TENSOR */
+  const float* group_scales;    /* SMLA_KV_FP8_E4M3_GROUP128: [num_slots][ceil(D/128)] */
+
+  /* Global slot indices [T][topk] int32 (row stride indices_stride), as
+   * produced by smla_convert_indices; negative = invalid. */
+  const int32_t* indices;
+  int64_t indices_stride;
+  int32_t topk;                 /* 1..2048 */
+  /* Optional [T] int32: only entries j < topk_length[t] are read. NULL =
+   * the whole row. The valid_counts output of smla_convert_indices is a
+   * correct length when invalid entries form a tail. */
+  const int32_t* topk_length;
+
+  float softmax_scale;
+
+  /* Output bf16 [T][h][512]; LSE fp32 [T][h] natural log (NULL = not
+   * wanted). Only the h true heads are written. */
+  void* out;
+  int64_t out_stride_tok, out_stride_head;
+  float* lse;
+  int64_t lse_stride_tok;
+
+  /* Decode only: number of top-k splits, 0 = choose from the shapes. */
+  int32_t num_splits;
+} smla_attn_args;
+
+/*
+ * Request-local top-k indices -> global cache slots (vLLM "Sparse MLA on
+ * Hopper" branch, cutlass_fa3_sparse.py forward_mqa step 2 and the test
+ * file's TEST 2.5 / TEST 2.9): for entry l of row t, with r = req_id[t],
+ *     global[t][j] = block_table[r][l / block_size] * block_stride_rows
+ *                    + l % block_size
+ * if l >= 0, l / block_size < max_blocks and the table entry is >= 0; else
+ * -1. valid_counts[t] (optional, may be NULL) = number of entries != -1.
+ * Entries keep their positions (a -1 tail stays a -1 tail).
+ *   req_id          [T] int32, each in [0, num_reqs)
+ *   block_table     [num_reqs][bt_row_stride] int32, first max_blocks used
+ *   topk_local      [T][topk] int32 (row stride topk_local_stride)
+ *   global_out      [T][topk] int32 (row stride global_stride)
+ * block_stride_rows = 0 means block_size.
+ */
+int smla_convert_indices(const int32_t* req_id, const int32_t* block_table,
+                         int32_t num_reqs, int32_t max_blocks, int64_t bt_row_stride,
+                         const int32_t* topk_local, int64_t topk_local_stride,
+                         int32_t num_tokens, int32_t topk,
+                         int32_t block_size, int32_t block_stride_rows,
+                         int32_t* global_out, int64_t global_stride,
+                         int32_t* valid_counts, void* stream);
+
+/* Bytes of caller-owned device workspace smla_decode_fwd needs for these
+ * shapes (0 when no split is used). num_splits = 0 means automatic. */
+size_t smla_decode_workspace_size(int32_t num_tokens, int32_t num_heads, int32_t topk,
+                                  int32_t num_splits);
+
+/* Number of splits smla_decode_fwd will use for these shapes. */
+int32_t smla_decode_num_splits(int32_t num_tokens, int32_t num_heads, int32_t topk,
+                               int32_t num_splits);
+
+/*
+ * Decode forward: the sparse attention above, with the top-k row of each
+ * token optionally cut into splits processed in parallel and merged by
+ * their LSE (FA3's split-KV + combine; the merge rule is the one the
+ * FlashMLA sparse page uses across ranks, with (0, -inf) as identity).
+ * workspace: device buffer of at least smla_decode_workspace_size() bytes,
+ * contents need not be initialised; may be NULL when that size is 0.
+ */
+int smla_decode_fwd(const smla_attn_args* args, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Prefill forward: the same function without splitting (one workgroup per
+ * token); args->num_splits is ignored. */
+int smla_prefill_fwd(const smla_attn_args* args, void* stream);
+
+/*
+ * Cache write (vLLM concat_and_cache_mla as called by do_kv_cache_update):
+ * row slot_mapping[t] of the cache gets [kv_c[t][0:512] | k_pe[t][0:d_rope]].
+ * slot_mapping < 0 skips the token. Formats:
+ *   SMLA_KV_BF16                 bf16 copy;
+ *   SMLA_KV_FP8_E4M3_PER_TENSOR  byte = e4m3_rne(fl32(x / k_scale)), saturated at 448;
+ *   SMLA_KV_FP8_E4M3_GROUP128    per row and 128-channel group g:
+ *                                scale = fl32(absmax / 448) (1 if the group is all zero),
+ *                                written to group_scales[slot][g]; byte as above.
+ * Duplicate slots in one call are not allowed (which row lands is unspecified).
+ *   kv_c [T][512] bf16 (row stride kv_c_stride), k_pe [T][d_rope] bf16 or NULL.
+ */
+int smla_cache_write(const void* kv_c, int64_t kv_c_stride, const void* k_pe, int64_t k_pe_stride,
+                     const int64_t* slot_mapping, int32_t num_tokens, int32_t d_rope,
+                     int32_t kv_format, float k_scale, void* kv_cache, int64_t num_slots,
+                     int64_t kv_row_stride_bytes, float* group_scales, void* stream);
+
+/* Thread-local description of the last non-OK return ("" if none). */
+const char* smla_last_error(void);
+
+/* Library version string. */
+const char* smla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SMLA_H_ */

@@ -1,0 +1,517 @@
+// Sparse MLA forward kernel for gfx950 (MI355X).
+//
+// Computes, per query token t and head i, attention over the token's own
+// top-k cache slots (vLLM "Sparse MLA on Hopper" branch, cutlass_fa3_sparse.py
+// _forward_fa3: score = q_rope . k_rope + q_nope . c_kv, out = softmax(score *
+// scale) . c_kv; FlashMLA sparse API docs: heads padded to 64 or 128, LSE per
+// (token, head), empty rows give (0, -inf)).
+//
+// One workgroup = one (token, 64-head block, split), 4 waves. A token with
+// more than 64 heads takes two workgroups, dispatched to the same XCD so the
+// second gather of the same rows hits that XCD's L2. Per tile of 32 rows:
+//   gather : direct global->LDS 16-byte loads (global_load_lds_dwordx4) of the
+//            32 rows into a swizzled bf16 tile, two tiles in flight;
+//   S^T=K.Q^T: v_mfma_f32_16x16x32_bf16; wave (hg, rh) scores rows
+//            16rh..16rh+15 against heads 32hg..32hg+31, A = K from LDS,
+//            B = the wave's Q held in registers for the whole kernel;
+//   softmax: base 2 against a fixed per-head reference (see below), row
+//            reductions in-lane plus two lane shuffles;
+//   O += P.V : v_mfma_f32_16x16x32_bf16; wave w owns O for all 64 heads x
+//            latent channels 128w..128w+127 in accumulator registers, A = P
+//            (bf16) exchanged through LDS, B = V read with ds_read_b64_tr_b16
+//            from the same tile (V is the first 512 channels of the gathered
+//            row, no second gather).
+#include "smla_device.h"
+#include "smla_internal.h"
+
+#include <math.h>
+
+namespace smla {
+
+struct KParams {
+  const uint16_t* q_nope;
+  int64_t qn_st, qn_sh;
+  const uint16_t* q_rope;
+  int64_t qr_st, qr_sh;
+  const uint8_t* kv;
+  int64_t kv_row_stride, num_slots;
+  const int32_t* indices;
+  int64_t idx_stride;
+  int32_t topk;
+  const int32_t* topk_length;
+  int32_t num_tokens, num_heads;
+  float scale_log2;   // softmax scale * log2(e)
+  float out_mult;
+  int32_t splits, split_rows, longest_first;
+  int32_t head_blocks;  // 1 (<= 64 heads) or 2
+  int32_t num_items;    // num_tokens * splits
+  uint16_t* out;
+  int64_t out_st, out_sh;
+  float* lse;
+  int64_t lse_st;
+  float* part_o;
+  float* part_lse;
+};
+
+__device__ __forceinline__ bf16x8 lds_ld128(const lds_char* p) {
+  return *(const __attribute__((address_space(3))) bf16x8*)p;
+}
+__device__ __forceinline__ void lds_st64(lds_char* p, uint64_t v) {
+  *(__attribute__((address_space(3))) uint64_t*)p = v;
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Reference maximum policy. O and the running sum are accumulated against a
+// per-head reference m (base-2 units) fixed at the first tile that holds a
+// valid entry; p = 2^(t - m) stays finite in bf16/fp32 while t - m <= 64. If
+// a later score exceeds m + 64 the workgroup restarts: a max-only pass finds
+// the exact per-head maximum, then the full pass runs with it.
+constexpr float kRefHeadroom = 64.0f;
+
+template <int D>
+struct TileShape {
+  static constexpr int RB = 2 * D;                    // bytes of one staged row
+  static constexpr int NC = D / 8;                    // 16-byte chunks per row
+  static constexpr int QKS = D / 32;                  // k-steps of the QK contraction
+  static constexpr int TILE_BYTES = kTileRows * RB;
+  static constexpr int NBUF = 3;
+  static constexpr int PER = NC * kTileRows / 256;    // DMA instructions per wave per tile
+  static_assert(PER * 256 == NC * kTileRows, "tile must split evenly over 4 waves");
+};
+
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+smla_attn_bf16_kernel(KParams p) {
+  using TS = TileShape<D>;
+  constexpr int RB = TS::RB, NC = TS::NC, QKS = TS::QKS, TILE_BYTES = TS::TILE_BYTES;
+  constexpr int NBUF = TS::NBUF, PER = TS::PER;
+
+  __shared__ __attribute__((aligned(16))) char s_tiles[NBUF * TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char s_p[4 * 64 * 16];    // P as A operands [mblock][lane]
+  __shared__ int s_idx[kMaxTopk];
+  __shared__ float s_m[4 * 32];
+  __shared__ float s_l[4 * 32];
+  __shared__ float s_inv[64];
+  __shared__ int s_flag;
+
+  lds_char* tiles = (lds_char*)s_tiles;
+  lds_char* pbuf = (lds_char*)s_p;
+
+  const int w = threadIdx.x >> 6;
+  const int l = threadIdx.x & 63;
+  const int lg = l >> 4, li = l & 15;
+  const int hg = w & 1, rh = w >> 1;            // QK role: 32-head group, 16-row half
+  const int T = p.num_tokens, H = p.num_heads;
+
+  // ---- work item; with two head blocks, blocks b and b+8 (same XCD) share a token
+  int item, hblk;
+  {
+    const int b = blockIdx.x;
+    if (p.head_blocks == 2) {
+      item = (b >> 4) * 8 + (b & 7);
+      hblk = (b >> 3) & 1;
+    } else {
+      item = b;
+      hblk = 0;
+    }
+  }
+  if (item >= p.num_items) return;
+  int t, split;
+  if (p.splits == 1) {
+    t = p.longest_first ? (T - 1 - item) : item;
+    split = 0;
+  } else {
+    t = item / p.splits;
+    split = item - t * p.splits;
+  }
+  const int hb = 64 * hblk;
+  int len = p.topk;
+  if (p.topk_length) len = min(max(p.topk_length[t], 0), p.topk);
+  const int row0 = split * p.split_rows;
+  const int nrows = max(0, min(len, row0 + p.split_rows) - row0);
+  const int ntiles = (nrows + kTileRows - 1) / kTileRows;
+
+  // ---- Q^T as the B operand of 16x16x32: lane holds head hb + 32hg + 16nbq + li,
+  //      channels 32ks + 8lg .. +8 (ks < 16 latent, ks >= 16 rope)
+  bf16x8 q[2][QKS];
+#pragma unroll
+  for (int nbq = 0; nbq < 2; nbq++) {
+    const int head = hb + 32 * hg + 16 * nbq + li;
+    const bool valid = head < H;
+    const int hq = valid ? head : 0;
+    const uint16_t* qn = p.q_nope + t * p.qn_st + hq * p.qn_sh + 8 * lg;
+    const uint16_t* qr = p.q_rope + t * p.qr_st + hq * p.qr_sh + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < QKS; ks++)
+      q[nbq][ks] = ks < 16 ? *(const bf16x8*)(qn + 32 * ks) : *(const bf16x8*)(qr + 32 * (ks - 16));
+    if (!valid) {
+#pragma unroll
+      for (int ks = 0; ks < QKS; ks++) q[nbq][ks] = (bf16x8){};
+    }
+  }
+
+  // ---- the workgroup's index range -> LDS (-1 marks an entry that does not take part)
+  const int32_t* irow = p.indices + (int64_t)t * p.idx_stride + row0;
+  for (int j = threadIdx.x; j < ntiles * kTileRows; j += 256) {
+    int g = -1;
+    if (j < nrows) {
+      g = irow[j];
+      if (g < 0 || (int64_t)g >= p.num_slots) g = -1;
+    }
+    s_idx[j] = g;
+  }
+  if (threadIdx.x == 0) s_flag = 0;
+  // Q and the indices must be in registers/LDS before the tile DMAs start:
+  // later waits only count the DMAs.
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  // Instruction u of wave w fills the 16-byte LDS slots (4u + w)*64 + lane of
+  // the tile: slot s is row s / NC, physical chunk s % NC.
+  const uint32_t tiles_addr = (uint32_t)(uintptr_t)tiles;
+  auto issue_tile = [&](int tt, int b) {
+    int lo;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(lo) : "v"(l));   // keep the address math in the loop
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    int rr[PER], gg[PER];
+#pragma unroll
+    for (int u = 0; u < PER; u++) {
+      const int s = (4 * u + wu) * 64 + lo;
+      rr[u] = s / NC;
+      gg[u] = s_idx[tt * kTileRows + rr[u]];
+    }
+    const uint32_t tb = __builtin_amdgcn_readfirstlane(tiles_addr + b * TILE_BYTES);
+#pragma unroll
+    for (int u = 0; u < PER; u++) {
+      const int s = (4 * u + wu) * 64 + lo;
+      const int pc = s - rr[u] * NC;
+      const uint8_t* src = p.kv + (int64_t)max(gg[u], 0) * p.kv_row_stride + ((pc ^ swz(rr[u])) << 4);
+      dma_16b(src, tb + (4 * u + wu) * 1024);
+    }
+  };
+
+  // K reads (A operand of 16x16x32): row 16rh + li, logical chunk 4ks + lg. With
+  // ks = 2a + j the physical chunk is 8a + ((4j + lg) ^ swz(row)).
+  int kbase[2];
+  {
+    const int krow = 16 * rh + li, ksw = swz(krow);
+#pragma unroll
+    for (int j = 0; j < 2; j++) kbase[j] = krow * RB + (((4 * j + lg) ^ ksw) << 4);
+  }
+  // V transposing reads (B operand of P.V): in 16-lane group lg, lane li = 4e + q
+  // reads row 4lg + e (then 16 + 4lg + e), channels 128w + 16nb + 4q .. +3.
+  // Both rows have swizzle sw = swz(4lg + e); the physical chunk of
+  // 16w + 2nb + (q >> 1) is 16w + 8(nb >> 2) + 2((nb & 3) ^ (sw >> 1)) + ((q >> 1) ^ (sw & 1)).
+  int vbase[2][4];
+  {
+    const int e = li >> 2, q4 = li & 3;
+    const int sw = swz(4 * lg + e);
+#pragma unroll
+    for (int half = 0; half < 2; half++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const int row = 16 * half + 4 * lg + e;
+        const int chunk = 16 * w + 2 * (j ^ (sw >> 1)) + ((q4 >> 1) ^ (sw & 1));
+        vbase[half][j] = row * RB + chunk * 16 + 8 * (q4 & 1);
+      }
+  }
+
+  // S^T[16 rows x 32 heads] of the wave for tile buffer tb, base-2 units, masked.
+  // Lane holds rows 16rh + 4lg + r (r = 0..3) of heads 32hg + 16nbq + li.
+  auto scores = [&](const lds_char* tb, uint32_t vmask, float (&tv)[2][4]) {
+    f32x4 s0 = {}, s1 = {};
+    constexpr int PF = 4;                      // K operand reads kept in flight
+    bf16x8 a[PF];
+#pragma unroll
+    for (int ks = 0; ks < PF; ks++) a[ks] = lds_ld128(tb + kbase[ks & 1] + 128 * (ks >> 1));
+#pragma unroll
+    for (int ks = 0; ks < QKS; ks++) {
+      const bf16x8 cur = a[ks % PF];
+      if (ks + PF < QKS) a[ks % PF] = lds_ld128(tb + kbase[(ks + PF) & 1] + 128 * ((ks + PF) >> 1));
+      __builtin_amdgcn_sched_barrier(0);       // keep the read-ahead ahead of the MFMAs
+      s0 = mfma16x16x32(cur, q[0][ks], s0);
+      s1 = mfma16x16x32(cur, q[1][ks], s1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const bool ok = (vmask >> (16 * rh + 4 * lg + r)) & 1;
+      tv[0][r] = ok ? s0[r] * p.scale_log2 : -INFINITY;
+      tv[1][r] = ok ? s1[r] * p.scale_log2 : -INFINITY;
+    }
+  };
+  // maximum over the wave's 16 rows, per head
+  auto half_max = [&](const float (&tv)[2][4], float (&mx)[2]) {
+#pragma unroll
+    for (int nbq = 0; nbq < 2; nbq++) {
+      float m = fmaxf(fmaxf(tv[nbq][0], tv[nbq][1]), fmaxf(tv[nbq][2], tv[nbq][3]));
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      mx[nbq] = m;
+    }
+  };
+
+  float m_ref[2] = {-INFINITY, -INFINITY};
+  float l_lane[2];
+  f32x4 O[4][8];
+  bool have_ref = false;      // workgroup-uniform: a reference has been fixed
+
+  for (int attempt = 0; attempt < 2; attempt++) {
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+      for (int nb = 0; nb < 8; nb++) O[mb][nb] = (f32x4){};
+    l_lane[0] = l_lane[1] = 0.0f;
+    if (ntiles > 0) issue_tile(0, 0);
+    if (ntiles > 1) issue_tile(1, 1);
+    for (int tt = 0; tt < ntiles; tt++) {
+      if (tt + 1 < ntiles) wait_vmcnt<PER>(); else wait_vmcnt<0>();
+      lds_barrier();
+      if (tt + 2 < ntiles) issue_tile(tt + 2, (tt + 2) % NBUF);
+      const lds_char* tb = tiles + (tt % NBUF) * TILE_BYTES;
+      const uint32_t vmask = (uint32_t)__ballot((l < 32) ? (s_idx[tt * kTileRows + l] >= 0) : 0);
+
+      float tv[2][4];
+      scores(tb, vmask, tv);
+      float mx[2];
+      half_max(tv, mx);
+      if (!have_ref && vmask != 0) {                       // uniform: first tile with a valid row
+        if (lg == 0) {
+          s_m[w * 32 + li] = mx[0];
+          s_m[w * 32 + 16 + li] = mx[1];
+        }
+        lds_barrier();
+        m_ref[0] = fmaxf(mx[0], s_m[(w ^ 2) * 32 + li]);
+        m_ref[1] = fmaxf(mx[1], s_m[(w ^ 2) * 32 + 16 + li]);
+        have_ref = true;
+      }
+      if (fmaxf(mx[0] - m_ref[0], mx[1] - m_ref[1]) > kRefHeadroom) s_flag = 1;
+      uint64_t pk[2];
+#pragma unroll
+      for (int nbq = 0; nbq < 2; nbq++) {
+        const float msub = (m_ref[nbq] == -INFINITY) ? 0.0f : m_ref[nbq];
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; r++) pr[r] = fast_exp2(tv[nbq][r] - msub);
+        l_lane[nbq] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        pk[nbq] = (uint64_t)pack_bf16x2(pr[0], pr[1]) | ((uint64_t)pack_bf16x2(pr[2], pr[3]) << 32);
+        // A operand of m-block 2hg + nbq, elements 4rh .. 4rh+3
+        lds_st64(pbuf + ((2 * hg + nbq) * 64 + l) * 16 + 8 * rh, pk[nbq]);
+      }
+      lds_barrier();
+
+      bf16x8 pa[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; mb++) pa[mb] = lds_ld128(pbuf + (mb * 64 + l) * 16);
+
+      // O[64 heads x 128 ch] += P[64 x 32] . V[32 x 128]
+      s16x4 vr[2][2];
+      vr[0][0] = lds_read_tr16(tb + vbase[0][0]);
+      vr[0][1] = lds_read_tr16(tb + vbase[1][0]);
+#pragma unroll
+      for (int nb = 0; nb < 8; nb++) {
+        const s16x4 v0 = vr[nb & 1][0];
+        const s16x4 v1 = vr[nb & 1][1];
+        if (nb + 1 < 8) {
+          vr[(nb + 1) & 1][0] = lds_read_tr16(tb + vbase[0][(nb + 1) & 3] + 128 * ((nb + 1) >> 2));
+          vr[(nb + 1) & 1][1] = lds_read_tr16(tb + vbase[1][(nb + 1) & 3] + 128 * ((nb + 1) >> 2));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 bv = concat_bf16x4(v0, v1);
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) O[mb][nb] = mfma16x16x32(pa[mb], bv, O[mb][nb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    lds_barrier();
+    if (!s_flag) break;                                    // uniform
+    // exact per-head maximum, then the full pass again
+    float mx_all[2] = {-INFINITY, -INFINITY};
+    if (ntiles > 0) issue_tile(0, 0);
+    if (ntiles > 1) issue_tile(1, 1);
+    for (int tt = 0; tt < ntiles; tt++) {
+      if (tt + 1 < ntiles) wait_vmcnt<PER>(); else wait_vmcnt<0>();
+      lds_barrier();
+      if (tt + 2 < ntiles) issue_tile(tt + 2, (tt + 2) % NBUF);
+      const lds_char* tb = tiles + (tt % NBUF) * TILE_BYTES;
+      const uint32_t vmask = (uint32_t)__ballot((l < 32) ? (s_idx[tt * kTileRows + l] >= 0) : 0);
+      float tv[2][4];
+      scores(tb, vmask, tv);
+      float mx[2];
+      half_max(tv, mx);
+      mx_all[0] = fmaxf(mx_all[0], mx[0]);
+      mx_all[1] = fmaxf(mx_all[1], mx[1]);
+    }
+    if (lg == 0) {
+      s_m[w * 32 + li] = mx_all[0];
+      s_m[w * 32 + 16 + li] = mx_all[1];
+    }
+    lds_barrier();
+    m_ref[0] = fmaxf(mx_all[0], s_m[(w ^ 2) * 32 + li]);
+    m_ref[1] = fmaxf(mx_all[1], s_m[(w ^ 2) * 32 + 16 + li]);
+    if (threadIdx.x == 0) s_flag = 0;
+    lds_barrier();
+  }
+
+  // ---- epilogue: row sums, normalise, LSE, write
+#pragma unroll
+  for (int nbq = 0; nbq < 2; nbq++) {
+    float v = l_lane[nbq];
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    l_lane[nbq] = v;
+  }
+  if (lg == 0) {
+    s_l[w * 32 + li] = l_lane[0];
+    s_l[w * 32 + 16 + li] = l_lane[1];
+  }
+  __syncthreads();
+  if (rh == 0 && lg == 0) {
+#pragma unroll
+    for (int nbq = 0; nbq < 2; nbq++) {
+      const float lt = s_l[w * 32 + 16 * nbq + li] + s_l[(w ^ 2) * 32 + 16 * nbq + li];
+      const int hl = 32 * hg + 16 * nbq + li;        // head within the block
+      s_inv[hl] = (lt > 0.0f) ? p.out_mult / lt : 0.0f;
+      const float lse_v = (lt > 0.0f) ? (m_ref[nbq] + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+      const int head = hb + hl;
+      if (head < H) {
+        if (p.splits == 1) {
+          if (p.lse) p.lse[(int64_t)t * p.lse_st + head] = lse_v;
+        } else {
+          p.part_lse[((int64_t)split * T + t) * H + head] = lse_v;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // O lane layout: m-block mb, n-block nb: heads 16mb + 4lg + r, channel 128w + 16nb + li
+#pragma unroll
+  for (int mb = 0; mb < 4; mb++) {
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      const int hl = 16 * mb + 4 * lg + r;
+      const int head = hb + hl;
+      if (head < H) {
+        const float sc = s_inv[hl];
+#pragma unroll
+        for (int nb = 0; nb < 8; nb++) {
+          const int col = 128 * w + 16 * nb + li;
+          const float o = O[mb][nb][r] * sc;
+          if (p.splits == 1) {
+            p.out[(int64_t)t * p.out_st + (int64_t)head * p.out_sh + col] = f32_to_bf16_rne(o);
+          } else {
+            p.part_o[(((int64_t)split * T + t) * H + head) * kDLatent + col] = o;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Merge split partials by their LSE: lse = ln sum_s exp(lse_s),
+// out = sum_s exp(lse_s - lse) * O_s; (0, -inf) is the identity.
+__global__ void __launch_bounds__(256)
+smla_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse, int splits,
+                    int T, int H, uint16_t* __restrict__ out, int64_t out_st, int64_t out_sh,
+                    float* __restrict__ lse, int64_t lse_st) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one thread = 4 channels
+  const int64_t total = (int64_t)T * H * (kDLatent / 4);
+  if (gid >= total) return;
+  const int c4 = (int)(gid % (kDLatent / 4));
+  const int64_t th = gid / (kDLatent / 4);
+  const int head = (int)(th % H);
+  const int t = (int)(th / H);
+  float m = -INFINITY;
+  for (int s = 0; s < splits; s++) m = fmaxf(m, part_lse[((int64_t)s * T + t) * H + head]);
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float tot = 0.0f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < splits; s++) {
+      const float ls = part_lse[((int64_t)s * T + t) * H + head];
+      const float wgt = (ls == -INFINITY) ? 0.0f : expf(ls - m);
+      tot += wgt;
+      const f32x4 o = *(const f32x4*)(part_o + (((int64_t)s * T + t) * H + head) * kDLatent + 4 * c4);
+      acc += wgt * o;
+    }
+    acc *= 1.0f / tot;
+  }
+  uint16_t* dst = out + (int64_t)t * out_st + (int64_t)head * out_sh + 4 * c4;
+  const uint32_t lo = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
+  const uint32_t hi = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
+  dst[0] = (uint16_t)lo; dst[1] = (uint16_t)(lo >> 16);
+  dst[2] = (uint16_t)hi; dst[3] = (uint16_t)(hi >> 16);
+  if (c4 == 0 && lse) lse[(int64_t)t * lse_st + head] = (m == -INFINITY) ? -INFINITY : m + logf(tot);
+}
+
+int32_t plan_splits(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t requested) {
+  (void)num_heads;
+  const int32_t max_splits = max(1, (topk + kTileRows - 1) / kTileRows);
+  if (requested > 0) return min(requested, max_splits);
+  if (num_tokens <= 0) return 1;
+  const int32_t target_wgs = 256;              // one workgroup per CU fills the chip
+  int32_t s = (target_wgs + num_tokens - 1) / num_tokens;
+  const int32_t min_rows = 256;                // keep >= 8 tiles per split
+  s = min(s, max(1, topk / min_rows));
+  return max(1, min(s, max_splits));
+}
+
+static int32_t split_rows_for(int32_t topk, int32_t splits) {
+  int32_t r = (topk + splits - 1) / splits;
+  return (r + kTileRows - 1) / kTileRows * kTileRows;
+}
+
+size_t workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t splits) {
+  (void)topk;
+  if (splits <= 1) return 0;
+  const size_t n = (size_t)splits * num_tokens * num_heads;
+  return n * kDLatent * sizeof(float) + n * sizeof(float);
+}
+
+template <int D>
+static void launch_kernel(const KParams& kp, int grid, hipStream_t stream) {
+  smla_attn_bf16_kernel<D><<<grid, 256, 0, stream>>>(kp);
+}
+
+hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, bool longest_first,
+                            hipStream_t stream) {
+  if (a.num_tokens == 0) return hipSuccess;
+  KParams kp;
+  kp.q_nope = a.q_nope; kp.qn_st = a.qn_st; kp.qn_sh = a.qn_sh;
+  kp.q_rope = a.d_rope ? a.q_rope : a.q_nope; kp.qr_st = a.qr_st; kp.qr_sh = a.qr_sh;
+  kp.kv = a.kv; kp.kv_row_stride = a.kv_row_stride; kp.num_slots = a.num_slots;
+  kp.indices = a.indices; kp.idx_stride = a.idx_stride; kp.topk = a.topk;
+  kp.topk_length = a.topk_length;
+  kp.num_tokens = a.num_tokens; kp.num_heads = a.num_heads;
+  kp.scale_log2 = a.softmax_scale * 1.4426950408889634f;
+  kp.out_mult = 1.0f;
+  kp.splits = splits;
+  kp.split_rows = split_rows_for(a.topk, splits);
+  kp.longest_first = longest_first ? 1 : 0;
+  kp.head_blocks = a.num_heads > 64 ? 2 : 1;
+  kp.num_items = a.num_tokens * splits;
+  kp.out = a.out; kp.out_st = a.out_st; kp.out_sh = a.out_sh;
+  kp.lse = a.lse; kp.lse_st = a.lse_st;
+  kp.part_o = nullptr; kp.part_lse = nullptr;
+  if (splits > 1) {
+    const size_t n = (size_t)splits * a.num_tokens * a.num_heads;
+    kp.part_o = (float*)workspace;
+    kp.part_lse = (float*)((char*)workspace + n * kDLatent * sizeof(float));
+  }
+  const int grid = kp.head_blocks == 2 ? ((kp.num_items + 7) / 8) * 16 : kp.num_items;
+  if (a.kv_format != 0) return hipErrorInvalidValue;
+  if (a.d_rope == 64) launch_kernel<576>(kp, grid, stream); else launch_kernel<512>(kp, grid, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  const int64_t total = (int64_t)a.num_tokens * a.num_heads * (kDLatent / 4);
+  smla_combine_kernel<<<(int)((total + 255) / 256), 256, 0, stream>>>(
+      kp.part_o, kp.part_lse, splits, a.num_tokens, a.num_heads, a.out, a.out_st, a.out_sh, a.lse, a.lse_st);
+  return hipGetLastError();
+}
+
+}  // namespace smla

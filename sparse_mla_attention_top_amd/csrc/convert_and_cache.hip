@@ -1,0 +1,169 @@
+// Index conversion and cache write kernels (gfx950).
+//
+// Conversion: vLLM "Sparse MLA on Hopper" branch, cutlass_fa3_sparse.py
+// forward_mqa step 2 and test_cutlass_fa3_sparse_backend.py TEST 2.5/2.9:
+// global = block_table[req][l / B] * stride + l % B, -1 stays -1, plus the
+// per-row count of valid entries.
+// Cache write: the same branch's do_kv_cache_update (concat_and_cache_mla),
+// with the FP8 E4M3 per-tensor and per-token x 128-channel-group formats of
+// flashinfer_mla_sparse_sm90.py.
+#include "smla_device.h"
+#include "smla_internal.h"
+
+namespace smla {
+
+// One workgroup per token row; entries are independent, the count is a
+// workgroup reduction (deterministic, no atomics).
+__global__ void __launch_bounds__(256)
+convert_indices_kernel(const int32_t* __restrict__ req_id, const int32_t* __restrict__ block_table,
+                       int32_t num_reqs, int32_t max_blocks, int64_t bt_row_stride,
+                       const int32_t* __restrict__ topk_local, int64_t loc_stride, int32_t topk,
+                       int32_t block_size, int32_t block_stride_rows,
+                       int32_t* __restrict__ global_out, int64_t out_stride,
+                       int32_t* __restrict__ valid_counts) {
+  const int t = blockIdx.x;
+  const int r = req_id[t];
+  const bool req_ok = (r >= 0) && (r < num_reqs);
+  const int32_t* bt = block_table + (int64_t)(req_ok ? r : 0) * bt_row_stride;
+  const int32_t* src = topk_local + (int64_t)t * loc_stride;
+  int32_t* dst = global_out + (int64_t)t * out_stride;
+  int cnt = 0;
+  for (int j = threadIdx.x; j < topk; j += 256) {
+    int l = src[j];
+    int g = -1;
+    if (req_ok && l >= 0) {
+      int blk = l / block_size;
+      if (blk < max_blocks) {
+        int e = bt[blk];
+        if (e >= 0) g = e * block_stride_rows + (l - blk * block_size);
+      }
+    }
+    dst[j] = g;
+    cnt += (g >= 0);
+  }
+  if (valid_counts) {
+    // wave reduction then across the 4 waves
+    for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+    __shared__ int part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) valid_counts[t] = part[0] + part[1] + part[2] + part[3];
+  }
+}
+
+// E4M3FN code of an fp32 value: round to nearest, ties to even, |y| >= 448
+// saturates to 448, NaN -> 0x7F (sign kept). Integer implementation of the
+// OCP E4M3 format (bias 7, 3 mantissa bits, min normal 2^-6, step 2^-9 below).
+__device__ __forceinline__ uint32_t e4m3_encode(float y) {
+  uint32_t u = __builtin_bit_cast(uint32_t, y);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t au = u & 0x7fffffffu;
+  if (au > 0x7f800000u) return sign | 0x7fu;
+  float a = __builtin_bit_cast(float, au);
+  if (a >= 448.0f) return sign | 0x7eu;
+  int exp = (int)(au >> 23) - 127;
+  uint32_t code;
+  if (exp < -6) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);  // subnormal steps of 2^-9, RNE
+  } else {
+    uint32_t mant = au & 0x7fffffu;
+    uint32_t m3 = mant >> 20, rem = mant & 0xfffffu;
+    uint32_t up = (rem > 0x80000u) || (rem == 0x80000u && (m3 & 1u));
+    code = ((uint32_t)(exp + 7) << 3) + m3 + up;
+    if (code > 0x7eu) code = 0x7eu;
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
+
+// One wave per token. Lane c8 handles channels [8*c8, 8*c8 + 8).
+template <int FMT>
+__global__ void __launch_bounds__(256)
+cache_write_kernel(const uint16_t* __restrict__ kv_c, int64_t kv_c_stride,
+                   const uint16_t* __restrict__ k_pe, int64_t k_pe_stride,
+                   const int64_t* __restrict__ slot_mapping, int32_t num_tokens, int32_t d_rope,
+                   float k_scale, uint8_t* __restrict__ cache, int64_t num_slots,
+                   int64_t row_stride, float* __restrict__ group_scales) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= num_tokens) return;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int D = kDLatent + d_rope;
+  const int nchunk = D / 8;            // 8-channel chunks (D is 512 or 576)
+  const int G = (D + 127) / 128;
+  // lanes 0..63 take chunks 0..63 (latent); lanes 0..7 also take chunks 64..71 (rope)
+  for (int pass = 0; pass < 2; pass++) {
+    int c8 = lane + pass * 64;
+    bool active = c8 < nchunk;
+    uint32_t w[4] = {0, 0, 0, 0};
+    if (active) {
+      const uint16_t* src = c8 < 64 ? kv_c + (int64_t)t * kv_c_stride + c8 * 8
+                                    : k_pe + (int64_t)t * k_pe_stride + (c8 - 64) * 8;
+      for (int i = 0; i < 4; i++) w[i] = (uint32_t)src[2 * i] | ((uint32_t)src[2 * i + 1] << 16);
+    }
+    if (FMT == 0) {
+      if (active) {
+        u32x4 v = {w[0], w[1], w[2], w[3]};
+        *(u32x4*)(cache + slot * row_stride + c8 * 16) = v;
+      }
+      continue;
+    }
+    float x[8];
+    for (int i = 0; i < 8; i++) x[i] = bf16_bits_to_f32((w[i / 2] >> (16 * (i % 2))) & 0xffffu);
+    float sc = k_scale;
+    if (FMT == 2) {
+      // group of 128 channels = 16 consecutive chunks = 16 consecutive lanes
+      float m = 0.0f;
+      for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(x[i]));
+      for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      sc = (m == 0.0f) ? 1.0f : m / 448.0f;
+      int g = c8 / 16;
+      if (active && (c8 % 16) == 0 && g < G) group_scales[slot * G + g] = sc;
+    }
+    if (active) {
+      uint32_t b[8];
+      for (int i = 0; i < 8; i++) b[i] = e4m3_encode(x[i] / sc);
+      uint32_t lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+      uint32_t hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+      uint32_t* dst = (uint32_t*)(cache + slot * row_stride + c8 * 8);
+      dst[0] = lo;
+      dst[1] = hi;
+    }
+  }
+}
+
+hipError_t launch_convert(const ConvertArgs& a, hipStream_t stream) {
+  if (a.num_tokens == 0) return hipSuccess;
+  convert_indices_kernel<<<a.num_tokens, 256, 0, stream>>>(
+      a.req_id, a.block_table, a.num_reqs, a.max_blocks, a.bt_row_stride, a.topk_local,
+      a.topk_local_stride, a.topk, a.block_size, a.block_stride_rows, a.global_out,
+      a.global_stride, a.valid_counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream) {
+  if (a.num_tokens == 0) return hipSuccess;
+  dim3 grid((a.num_tokens + 3) / 4);
+  switch (a.kv_format) {
+    case 0:
+      cache_write_kernel<0><<<grid, 256, 0, stream>>>(a.kv_c, a.kv_c_stride, a.k_pe, a.k_pe_stride,
+                                                      a.slot_mapping, a.num_tokens, a.d_rope, a.k_scale,
+                                                      a.cache, a.num_slots, a.row_stride, a.group_scales);
+      break;
+    case 1:
+      cache_write_kernel<1><<<grid, 256, 0, stream>>>(a.kv_c, a.kv_c_stride, a.k_pe, a.k_pe_stride,
+                                                      a.slot_mapping, a.num_tokens, a.d_rope, a.k_scale,
+                                                      a.cache, a.num_slots, a.row_stride, a.group_scales);
+      break;
+    default:
+      cache_write_kernel<2><<<grid, 256, 0, stream>>>(a.kv_c, a.kv_c_stride, a.k_pe, a.k_pe_stride,
+                                                      a.slot_mapping, a.num_tokens, a.d_rope, a.k_scale,
+                                                      a.cache, a.num_slots, a.row_stride, a.group_scales);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace smla

@@ -1,0 +1,201 @@
+// C ABI of the sparse MLA library: argument checks, error reporting and
+// dispatch to the gfx950 kernel launchers. No allocation, no host sync.
+#include "../../include/smla.h"
+#include "smla_internal.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return SMLA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(SMLA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_attn(const smla_attn_args* a, bool decode) {
+  if (!a) return fail(SMLA_ERR_INVALID_ARG, "args is NULL");
+  if (a->num_tokens < 0) return fail(SMLA_ERR_INVALID_ARG, "num_tokens < 0");
+  if (a->num_heads < 1 || a->num_heads > 128)
+    return fail(SMLA_ERR_UNSUPPORTED, "num_heads=%d outside 1..128", a->num_heads);
+  if (a->d_rope != 0 && a->d_rope != 64)
+    return fail(SMLA_ERR_UNSUPPORTED, "d_rope=%d (only 0 or 64)", a->d_rope);
+  if (a->topk < 1 || a->topk > smla::kMaxTopk)
+    return fail(SMLA_ERR_UNSUPPORTED, "topk=%d outside 1..%d", a->topk, smla::kMaxTopk);
+  if (a->kv_format < SMLA_KV_BF16 || a->kv_format > SMLA_KV_FP8_E4M3_GROUP128)
+    return fail(SMLA_ERR_INVALID_ARG, "unknown kv_format %d", a->kv_format);
+  if (!std::isfinite(a->softmax_scale)) return fail(SMLA_ERR_INVALID_ARG, "softmax_scale not finite");
+  if (a->num_tokens == 0) return SMLA_OK;
+  if (!a->q_nope || !a->kv_cache || !a->indices || !a->out)
+    return fail(SMLA_ERR_INVALID_ARG, "q_nope, kv_cache, indices and out must be non-NULL");
+  if (a->d_rope > 0 && !a->q_rope) return fail(SMLA_ERR_INVALID_ARG, "q_rope is NULL with d_rope=64");
+  if (a->num_slots < 1 || a->num_slots > INT32_MAX)
+    return fail(SMLA_ERR_INVALID_ARG, "num_slots=%lld outside 1..2^31-1", (long long)a->num_slots);
+  const int D = 512 + a->d_rope;
+  const int64_t row_bytes = a->kv_format == SMLA_KV_BF16 ? 2 * D : D;
+  if (a->kv_row_stride_bytes < row_bytes || a->kv_row_stride_bytes % 16 != 0)
+    return fail(SMLA_ERR_INVALID_ARG, "kv_row_stride_bytes=%lld must be >= %lld and a multiple of 16",
+                (long long)a->kv_row_stride_bytes, (long long)row_bytes);
+  if (!aligned16(a->kv_cache)) return fail(SMLA_ERR_INVALID_ARG, "kv_cache must be 16-byte aligned");
+  if (!aligned16(a->q_nope) || (a->d_rope && !aligned16(a->q_rope)))
+    return fail(SMLA_ERR_INVALID_ARG, "q_nope/q_rope must be 16-byte aligned");
+  if (a->q_nope_stride_tok % 8 || a->q_nope_stride_head % 8 ||
+      (a->d_rope && (a->q_rope_stride_tok % 8 || a->q_rope_stride_head % 8)))
+    return fail(SMLA_ERR_INVALID_ARG, "query strides must be multiples of 8 elements");
+  if (a->indices_stride < a->topk) return fail(SMLA_ERR_INVALID_ARG, "indices_stride < topk");
+  if (a->out_stride_head < 512 && a->num_heads > 1)
+    return fail(SMLA_ERR_INVALID_ARG, "out_stride_head < 512");
+  if (a->lse && a->lse_stride_tok < a->num_heads) return fail(SMLA_ERR_INVALID_ARG, "lse_stride_tok < num_heads");
+  if (a->kv_format == SMLA_KV_FP8_E4M3_GROUP128 && !a->group_scales)
+    return fail(SMLA_ERR_INVALID_ARG, "group_scales is NULL for the group-scaled FP8 format");
+  if (a->kv_format == SMLA_KV_FP8_E4M3_PER_TENSOR && !(std::isfinite(a->k_scale) && a->k_scale > 0))
+    return fail(SMLA_ERR_INVALID_ARG, "k_scale must be finite and > 0");
+  if (a->kv_format != SMLA_KV_BF16)
+    return fail(SMLA_ERR_UNSUPPORTED, "FP8 cache formats are not built yet");
+  if (decode && a->num_splits < 0) return fail(SMLA_ERR_INVALID_ARG, "num_splits < 0");
+  return SMLA_OK;
+}
+
+smla::AttnArgs to_internal(const smla_attn_args* a) {
+  smla::AttnArgs r;
+  r.q_nope = (const uint16_t*)a->q_nope;
+  r.qn_st = a->q_nope_stride_tok;
+  r.qn_sh = a->q_nope_stride_head;
+  r.q_rope = (const uint16_t*)a->q_rope;
+  r.qr_st = a->q_rope_stride_tok;
+  r.qr_sh = a->q_rope_stride_head;
+  r.num_tokens = a->num_tokens;
+  r.num_heads = a->num_heads;
+  r.d_rope = a->d_rope;
+  r.kv = (const uint8_t*)a->kv_cache;
+  r.num_slots = a->num_slots;
+  r.kv_row_stride = a->kv_row_stride_bytes;
+  r.kv_format = a->kv_format;
+  r.k_scale = a->k_scale;
+  r.group_scales = a->group_scales;
+  r.indices = a->indices;
+  r.idx_stride = a->indices_stride;
+  r.topk = a->topk;
+  r.topk_length = a->topk_length;
+  r.softmax_scale = a->softmax_scale;
+  r.out = (uint16_t*)a->out;
+  r.out_st = a->out_stride_tok;
+  r.out_sh = a->out_stride_head;
+  r.lse = a->lse;
+  r.lse_st = a->lse_stride_tok;
+  return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* smla_last_error(void) { return g_err; }
+
+const char* smla_version(void) { return "smla 0.1 gfx950"; }
+
+int smla_convert_indices(const int32_t* req_id, const int32_t* block_table, int32_t num_reqs,
+                         int32_t max_blocks, int64_t bt_row_stride, const int32_t* topk_local,
+                         int64_t topk_local_stride, int32_t num_tokens, int32_t topk, int32_t block_size,
+                         int32_t block_stride_rows, int32_t* global_out, int64_t global_stride,
+                         int32_t* valid_counts, void* stream) {
+  if (num_tokens < 0 || topk < 0) return fail(SMLA_ERR_INVALID_ARG, "num_tokens/topk < 0");
+  if (block_size < 1) return fail(SMLA_ERR_INVALID_ARG, "block_size=%d must be >= 1", block_size);
+  if (block_stride_rows < 0) return fail(SMLA_ERR_INVALID_ARG, "block_stride_rows < 0");
+  if (num_reqs < 1 || max_blocks < 1 || bt_row_stride < max_blocks)
+    return fail(SMLA_ERR_INVALID_ARG, "block table shape invalid (num_reqs=%d max_blocks=%d stride=%lld)",
+                num_reqs, max_blocks, (long long)bt_row_stride);
+  if (topk_local_stride < topk || global_stride < topk)
+    return fail(SMLA_ERR_INVALID_ARG, "row strides must be >= topk");
+  if (num_tokens == 0) return ok();
+  if (!req_id || !block_table || (topk > 0 && (!topk_local || !global_out)))
+    return fail(SMLA_ERR_INVALID_ARG, "NULL pointer argument");
+  smla::ConvertArgs a{req_id, block_table, num_reqs, max_blocks, bt_row_stride, topk_local,
+                      topk_local_stride, num_tokens, topk, block_size,
+                      block_stride_rows == 0 ? block_size : block_stride_rows, global_out, global_stride,
+                      valid_counts};
+  return hip_status(smla::launch_convert(a, (hipStream_t)stream), "convert_indices launch");
+}
+
+int32_t smla_decode_num_splits(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t num_splits) {
+  return smla::plan_splits(num_tokens, num_heads, topk, num_splits);
+}
+
+size_t smla_decode_workspace_size(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t num_splits) {
+  if (num_tokens <= 0 || num_heads <= 0 || topk <= 0) return 0;
+  const int32_t s = smla::plan_splits(num_tokens, num_heads, topk, num_splits);
+  return smla::workspace_bytes(num_tokens, num_heads, topk, s);
+}
+
+int smla_decode_fwd(const smla_attn_args* args, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_attn(args, true);
+  if (rc != SMLA_OK) return rc;
+  if (args->num_tokens == 0) return ok();
+  const int32_t s = smla::plan_splits(args->num_tokens, args->num_heads, args->topk, args->num_splits);
+  const size_t need = smla::workspace_bytes(args->num_tokens, args->num_heads, args->topk, s);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(SMLA_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes, need %zu", workspace_bytes, need);
+  if (need > 0 && !aligned16(workspace)) return fail(SMLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return hip_status(smla::launch_attention(to_internal(args), s, workspace, false, (hipStream_t)stream),
+                    "decode launch");
+}
+
+int smla_prefill_fwd(const smla_attn_args* args, void* stream) {
+  int rc = check_attn(args, false);
+  if (rc != SMLA_OK) return rc;
+  if (args->num_tokens == 0) return ok();
+  return hip_status(smla::launch_attention(to_internal(args), 1, nullptr, true, (hipStream_t)stream),
+                    "prefill launch");
+}
+
+int smla_cache_write(const void* kv_c, int64_t kv_c_stride, const void* k_pe, int64_t k_pe_stride,
+                     const int64_t* slot_mapping, int32_t num_tokens, int32_t d_rope, int32_t kv_format,
+                     float k_scale, void* kv_cache, int64_t num_slots, int64_t kv_row_stride_bytes,
+                     float* group_scales, void* stream) {
+  if (num_tokens < 0) return fail(SMLA_ERR_INVALID_ARG, "num_tokens < 0");
+  if (d_rope != 0 && d_rope != 64) return fail(SMLA_ERR_UNSUPPORTED, "d_rope=%d (only 0 or 64)", d_rope);
+  if (kv_format < SMLA_KV_BF16 || kv_format > SMLA_KV_FP8_E4M3_GROUP128)
+    return fail(SMLA_ERR_INVALID_ARG, "unknown kv_format %d", kv_format);
+  if (num_tokens == 0) return ok();
+  if (!kv_c || !slot_mapping || !kv_cache) return fail(SMLA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (d_rope && !k_pe) return fail(SMLA_ERR_INVALID_ARG, "k_pe is NULL with d_rope=64");
+  if (kv_c_stride < 512 || (d_rope && k_pe_stride < d_rope))
+    return fail(SMLA_ERR_INVALID_ARG, "source row strides too small");
+  const int D = 512 + d_rope;
+  const int64_t row_bytes = kv_format == SMLA_KV_BF16 ? 2 * D : D;
+  if (kv_row_stride_bytes < row_bytes || kv_row_stride_bytes % 16 != 0 || !aligned16(kv_cache))
+    return fail(SMLA_ERR_INVALID_ARG, "cache row stride must be >= %lld and a multiple of 16, base 16-byte aligned",
+                (long long)row_bytes);
+  if (num_slots < 1) return fail(SMLA_ERR_INVALID_ARG, "num_slots < 1");
+  if (kv_format == SMLA_KV_FP8_E4M3_PER_TENSOR && !(std::isfinite(k_scale) && k_scale > 0))
+    return fail(SMLA_ERR_INVALID_ARG, "k_scale must be finite and > 0");
+  if (kv_format == SMLA_KV_FP8_E4M3_GROUP128 && !group_scales)
+    return fail(SMLA_ERR_INVALID_ARG, "group_scales is NULL for the group-scaled FP8 format");
+  smla::CacheWriteArgs a{(const uint16_t*)kv_c, kv_c_stride, (const uint16_t*)k_pe, k_pe_stride, slot_mapping,
+                         num_tokens, d_rope, kv_format, k_scale, (uint8_t*)kv_cache, num_slots,
+                         kv_row_stride_bytes, group_scales};
+  return hip_status(smla::launch_cache_write(a, (hipStream_t)stream), "cache_write launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,71 @@
+// Host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+struct ConvertArgs {
+  const int32_t* req_id;
+  const int32_t* block_table;
+  int32_t num_reqs, max_blocks;
+  int64_t bt_row_stride;
+  const int32_t* topk_local;
+  int64_t topk_local_stride;
+  int32_t num_tokens, topk, block_size, block_stride_rows;
+  int32_t* global_out;
+  int64_t global_stride;
+  int32_t* valid_counts;
+};
+
+struct CacheWriteArgs {
+  const uint16_t* kv_c;
+  int64_t kv_c_stride;
+  const uint16_t* k_pe;
+  int64_t k_pe_stride;
+  const int64_t* slot_mapping;
+  int32_t num_tokens, d_rope, kv_format;
+  float k_scale;
+  uint8_t* cache;
+  int64_t num_slots, row_stride;
+  float* group_scales;
+};
+
+// Attention launch description (validated by the ABI layer).
+struct AttnArgs {
+  const uint16_t* q_nope;
+  int64_t qn_st, qn_sh;
+  const uint16_t* q_rope;
+  int64_t qr_st, qr_sh;
+  int32_t num_tokens, num_heads, d_rope;
+  const uint8_t* kv;
+  int64_t num_slots, kv_row_stride;
+  int32_t kv_format;
+  float k_scale;
+  const float* group_scales;
+  const int32_t* indices;
+  int64_t idx_stride;
+  int32_t topk;
+  const int32_t* topk_length;
+  float softmax_scale;
+  uint16_t* out;
+  int64_t out_st, out_sh;
+  float* lse;
+  int64_t lse_st;
+};
+
+constexpr int kTileRows = 32;
+constexpr int kMaxTopk = 2048;
+
+// Split plan from shapes only.
+int32_t plan_splits(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t requested);
+size_t workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t splits);
+
+hipError_t launch_convert(const ConvertArgs& a, hipStream_t stream);
+hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
+// splits == 1: direct output. splits > 1: partials into workspace + combine.
+hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, bool longest_first,
+                            hipStream_t stream);
+
+}  // namespace smla

@@ -142,9 +142,11 @@ def per_tensor_scale_from_absmax(kv_src: torch.Tensor) -> float:
     return float(np.float32(amax) / np.float32(448.0))
 
 
-def generate(spec: WorkloadSpec, device="cpu", kv_device=None) -> Workload:
+def generate(spec: WorkloadSpec, device="cpu", kv_device=None, with_values: bool = True) -> Workload:
     """Draw one workload. Index structures are drawn on the CPU (they are small);
-    Q and the cache rows on ``kv_device`` (defaults to ``device``)."""
+    Q and the cache rows on ``kv_device`` (defaults to ``device``). With
+    ``with_values=False`` only the index structures are drawn (q and kv_src
+    are empty placeholders)."""
     kv_device = device if kv_device is None else kv_device
     T, R, K = spec.num_tokens, spec.num_requests, spec.topk
     gi = _gen(spec.seed, 1, "cpu")
@@ -174,9 +176,14 @@ def generate(spec: WorkloadSpec, device="cpu", kv_device=None) -> Workload:
         topk_local[t, :v] = torch.randperm(visible, generator=gi)[:v].to(torch.int32)
         valid[t] = v
 
-    q = _bf16_normal((T, spec.heads, spec.d), spec.seed, 3, kv_device)
-    kv_src = _bf16_normal((spec.num_slots, spec.d), spec.seed, 4, kv_device)
-    k_scale = per_tensor_scale_from_absmax(kv_src) if spec.kv_format == KV_FP8_PER_TENSOR else 1.0
+    if with_values:
+        q = _bf16_normal((T, spec.heads, spec.d), spec.seed, 3, kv_device)
+        kv_src = _bf16_normal((spec.num_slots, spec.d), spec.seed, 4, kv_device)
+        k_scale = per_tensor_scale_from_absmax(kv_src) if spec.kv_format == KV_FP8_PER_TENSOR else 1.0
+    else:
+        q = torch.empty((0,), dtype=torch.bfloat16)
+        kv_src = torch.empty((0,), dtype=torch.bfloat16)
+        k_scale = 1.0
     return Workload(spec, q, kv_src, k_scale, req_id.to(device), bt.to(device),
                     topk_local.to(device), positions, valid.to(device))
 
@@ -193,3 +200,30 @@ def kv_row_bytes(spec: WorkloadSpec) -> int:
     if spec.kv_format == KV_FP8_PER_TENSOR:
         return spec.d
     return spec.d + 4 * math.ceil(spec.d / 128)
+
+
+@dataclasses.dataclass
+class RandomCase:
+    q: torch.Tensor          # [T, h, 512 + d_rope] bf16
+    kv_src: torch.Tensor     # [S, 512 + d_rope] bf16
+    indices: torch.Tensor    # [T, topk] int32 global slots, -1 = invalid
+    lengths: torch.Tensor    # [T] int32, length of each row's valid prefix
+
+
+def random_case(T: int, h: int, d_rope: int, topk: int, num_slots: int, seed: int,
+                lengths=None, device="cpu") -> RandomCase:
+    """Small synthetic case with global slot indices: row t lists lengths[t]
+    distinct uniform slots (random order) followed by -1. ``lengths`` defaults
+    to topk for every row (capped at num_slots)."""
+    g = torch.Generator().manual_seed(seed)
+    D = D_LATENT + d_rope
+    q = torch.randn((T, h, D), generator=g).to(torch.bfloat16)
+    kv = torch.randn((num_slots, D), generator=g).to(torch.bfloat16)
+    if lengths is None:
+        lengths = [min(topk, num_slots)] * T
+    lengths = [int(v) for v in lengths]
+    idx = torch.full((T, topk), -1, dtype=torch.int32)
+    for t, v in enumerate(lengths):
+        idx[t, :v] = torch.randperm(num_slots, generator=g)[:v].to(torch.int32)
+    return RandomCase(q.to(device), kv.to(device), idx.to(device),
+                      torch.tensor(lengths, dtype=torch.int32).to(device))

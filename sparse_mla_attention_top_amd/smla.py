@@ -1,0 +1,272 @@
+"""ctypes binding of libsmla.so (the gfx950 sparse MLA library).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/smla.h. PyTorch provides device
+memory and the current stream. If the library is missing the calls raise;
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsmla.so")
+
+KV_BF16 = 0
+KV_FP8_PER_TENSOR = 1
+KV_FP8_GROUP128 = 2
+
+SMLA_OK = 0
+
+EXPORTED = (
+    "smla_convert_indices",
+    "smla_decode_workspace_size",
+    "smla_decode_num_splits",
+    "smla_decode_fwd",
+    "smla_prefill_fwd",
+    "smla_cache_write",
+    "smla_last_error",
+    "smla_version",
+)
+
+
+class SmlaError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("q_nope", ctypes.c_void_p),
+        ("q_nope_stride_tok", ctypes.c_int64),
+        ("q_nope_stride_head", ctypes.c_int64),
+        ("q_rope", ctypes.c_void_p),
+        ("q_rope_stride_tok", ctypes.c_int64),
+        ("q_rope_stride_head", ctypes.c_int64),
+        ("num_tokens", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("d_rope", ctypes.c_int32),
+        ("kv_cache", ctypes.c_void_p),
+        ("num_slots", ctypes.c_int64),
+        ("kv_row_stride_bytes", ctypes.c_int64),
+        ("kv_format", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("group_scales", ctypes.c_void_p),
+        ("indices", ctypes.c_void_p),
+        ("indices_stride", ctypes.c_int64),
+        ("topk", ctypes.c_int32),
+        ("topk_length", ctypes.c_void_p),
+        ("softmax_scale", ctypes.c_float),
+        ("out", ctypes.c_void_p),
+        ("out_stride_tok", ctypes.c_int64),
+        ("out_stride_head", ctypes.c_int64),
+        ("lse", ctypes.c_void_p),
+        ("lse_stride_tok", ctypes.c_int64),
+        ("num_splits", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libsmla.so (built in-tree by ``python -m sparse_mla_attention_top_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m sparse_mla_attention_top_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    lib.smla_convert_indices.argtypes = [vp, vp, i32, i32, i64, vp, i64, i32, i32, i32, i32, vp, i64, vp, vp]
+    lib.smla_convert_indices.restype = ctypes.c_int
+    lib.smla_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.smla_decode_workspace_size.restype = sz
+    lib.smla_decode_num_splits.argtypes = [i32, i32, i32, i32]
+    lib.smla_decode_num_splits.restype = i32
+    lib.smla_decode_fwd.argtypes = [ctypes.POINTER(AttnArgs), vp, sz, vp]
+    lib.smla_decode_fwd.restype = ctypes.c_int
+    lib.smla_prefill_fwd.argtypes = [ctypes.POINTER(AttnArgs), vp]
+    lib.smla_prefill_fwd.restype = ctypes.c_int
+    lib.smla_cache_write.argtypes = [vp, i64, vp, i64, vp, i32, i32, i32, f32, vp, i64, i64, vp, vp]
+    lib.smla_cache_write.restype = ctypes.c_int
+    lib.smla_last_error.argtypes = []
+    lib.smla_last_error.restype = ctypes.c_char_p
+    lib.smla_version.argtypes = []
+    lib.smla_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != SMLA_OK:
+        raise SmlaError(fn, rc, load().smla_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+# ---------------------------------------------------------------------------
+# index conversion
+# ---------------------------------------------------------------------------
+
+def convert_indices(req_id: torch.Tensor, block_table: torch.Tensor, topk_local: torch.Tensor,
+                    block_size: int = 64, block_stride_rows: int = 0,
+                    out: Optional[torch.Tensor] = None, valid_counts: Optional[torch.Tensor] = None,
+                    want_valid_counts: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Request-local top-k indices -> global cache slots (+ valid counts)."""
+    _need(topk_local.dtype == torch.int32 and req_id.dtype == torch.int32 and block_table.dtype == torch.int32,
+          "int32 tensors expected")
+    _need(topk_local.dim() == 2 and topk_local.stride(1) == 1, "topk_local must be [T, K] with unit column stride")
+    _need(block_table.dim() == 2 and block_table.stride(1) == 1, "block_table must be [R, max_blocks]")
+    T, K = topk_local.shape
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.int32, device=topk_local.device)
+    if valid_counts is None and want_valid_counts:
+        valid_counts = torch.empty((T,), dtype=torch.int32, device=topk_local.device)
+    rc = load().smla_convert_indices(_ptr(req_id), _ptr(block_table), block_table.shape[0], block_table.shape[1],
+                                     block_table.stride(0), _ptr(topk_local), topk_local.stride(0), T, K,
+                                     block_size, block_stride_rows, _ptr(out), out.stride(0), _ptr(valid_counts),
+                                     _stream(stream))
+    _check("smla_convert_indices", rc)
+    return out, valid_counts
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+def _kv_geometry(kv_cache: torch.Tensor):
+    """(num_slots, row_stride_bytes, row_width) of a [..., S, D] or [blocks, B, D] cache."""
+    if kv_cache.dim() == 3:
+        nb, bs, d = kv_cache.shape
+        _need(kv_cache.stride(2) == 1 and kv_cache.stride(0) == bs * kv_cache.stride(1),
+              "paged cache must be [num_blocks, block_size, D] with contiguous blocks")
+        return nb * bs, kv_cache.stride(1) * kv_cache.element_size(), d
+    _need(kv_cache.dim() == 2 and kv_cache.stride(1) == 1, "cache must be [S, D] or [blocks, B, D]")
+    return kv_cache.shape[0], kv_cache.stride(0) * kv_cache.element_size(), kv_cache.shape[1]
+
+
+def _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk_length, k_scale,
+               group_scales, out, lse, num_splits) -> Tuple[AttnArgs, torch.Tensor, Optional[torch.Tensor]]:
+    _need(q_nope.dtype == torch.bfloat16 and q_nope.dim() == 3 and q_nope.shape[2] == 512 and q_nope.stride(2) == 1,
+          "q_nope must be bf16 [T, h, 512] with unit channel stride")
+    T, H, _ = q_nope.shape
+    d_rope = 0 if q_rope is None else q_rope.shape[2]
+    if q_rope is not None:
+        _need(q_rope.dtype == torch.bfloat16 and q_rope.shape[:2] == (T, H) and q_rope.stride(2) == 1,
+              "q_rope must be bf16 [T, h, d_rope]")
+    _need(indices.dtype == torch.int32 and indices.dim() == 2 and indices.shape[0] == T and indices.stride(1) == 1,
+          "indices must be int32 [T, topk]")
+    if topk_length is not None:
+        _need(topk_length.dtype == torch.int32 and topk_length.numel() == T, "topk_length must be int32 [T]")
+    S, row_stride, _ = _kv_geometry(kv_cache)
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q_nope.device)
+    _need(out.dtype == torch.bfloat16 and out.shape == (T, H, 512) and out.stride(2) == 1, "out must be bf16 [T, h, 512]")
+    a = AttnArgs()
+    a.q_nope = _ptr(q_nope)
+    a.q_nope_stride_tok, a.q_nope_stride_head = q_nope.stride(0), q_nope.stride(1)
+    a.q_rope = _ptr(q_rope)
+    a.q_rope_stride_tok = q_rope.stride(0) if q_rope is not None else 0
+    a.q_rope_stride_head = q_rope.stride(1) if q_rope is not None else 0
+    a.num_tokens, a.num_heads, a.d_rope = T, H, d_rope
+    a.kv_cache = _ptr(kv_cache)
+    a.num_slots = S
+    a.kv_row_stride_bytes = row_stride
+    a.kv_format = kv_format
+    a.k_scale = float(k_scale)
+    a.group_scales = _ptr(group_scales)
+    a.indices = _ptr(indices)
+    a.indices_stride = indices.stride(0)
+    a.topk = indices.shape[1]
+    a.topk_length = _ptr(topk_length)
+    a.softmax_scale = float(softmax_scale)
+    a.out = _ptr(out)
+    a.out_stride_tok, a.out_stride_head = out.stride(0), out.stride(1)
+    a.lse = _ptr(lse)
+    a.lse_stride_tok = lse.stride(0) if lse is not None else 0
+    a.num_splits = int(num_splits)
+    return a, out, lse
+
+
+def decode_workspace_size(num_tokens: int, num_heads: int, topk: int, num_splits: int = 0) -> int:
+    return int(load().smla_decode_workspace_size(num_tokens, num_heads, topk, num_splits))
+
+
+def decode_num_splits(num_tokens: int, num_heads: int, topk: int, num_splits: int = 0) -> int:
+    return int(load().smla_decode_num_splits(num_tokens, num_heads, topk, num_splits))
+
+
+def decode_fwd(q_nope, q_rope, kv_cache, indices, softmax_scale, kv_format=KV_BF16, topk_length=None,
+               k_scale=1.0, group_scales=None, out=None, lse=None, return_lse=True, num_splits=0,
+               workspace=None, stream=None):
+    """Sparse MLA decode forward. Returns (out [T,h,512] bf16, lse [T,h] fp32 or None)."""
+    T, H = q_nope.shape[:2]
+    if lse is None and return_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q_nope.device)
+    a, out, lse = _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk_length,
+                             k_scale, group_scales, out, lse, num_splits)
+    need = decode_workspace_size(T, H, indices.shape[1], num_splits) if T > 0 else 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load().smla_decode_fwd(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream))
+    _check("smla_decode_fwd", rc)
+    return out, lse
+
+
+def prefill_fwd(q_nope, q_rope, kv_cache, indices, softmax_scale, kv_format=KV_BF16, topk_length=None,
+                k_scale=1.0, group_scales=None, out=None, lse=None, return_lse=False, stream=None):
+    """Sparse MLA prefill forward (no split). Returns (out, lse or None)."""
+    T, H = q_nope.shape[:2]
+    if lse is None and return_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=q_nope.device)
+    a, out, lse = _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk_length,
+                             k_scale, group_scales, out, lse, 0)
+    rc = load().smla_prefill_fwd(ctypes.byref(a), _stream(stream))
+    _check("smla_prefill_fwd", rc)
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# cache write
+# ---------------------------------------------------------------------------
+
+def cache_write(kv_c: torch.Tensor, k_pe: Optional[torch.Tensor], slot_mapping: torch.Tensor,
+                kv_cache: torch.Tensor, kv_format: int = KV_BF16, k_scale: float = 1.0,
+                group_scales: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Write [kv_c | k_pe] rows into the cache at slot_mapping (negative = skip)."""
+    _need(kv_c.dtype == torch.bfloat16 and kv_c.dim() == 2 and kv_c.shape[1] == 512 and kv_c.stride(1) == 1,
+          "kv_c must be bf16 [T, 512]")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == kv_c.shape[0], "slot_mapping must be int64 [T]")
+    d_rope = 0 if k_pe is None else k_pe.shape[1]
+    if k_pe is not None:
+        _need(k_pe.dtype == torch.bfloat16 and k_pe.stride(1) == 1, "k_pe must be bf16 [T, d_rope]")
+    S, row_stride, _ = _kv_geometry(kv_cache)
+    rc = load().smla_cache_write(_ptr(kv_c), kv_c.stride(0), _ptr(k_pe), k_pe.stride(0) if k_pe is not None else 0,
+                                 _ptr(slot_mapping), kv_c.shape[0], d_rope, kv_format, float(k_scale),
+                                 _ptr(kv_cache), S, row_stride, _ptr(group_scales), _stream(stream))
+    _check("smla_cache_write", rc)
+
+
+def version() -> str:
+    return load().smla_version().decode()

@@ -1,0 +1,68 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+and the fp64 oracle on the same seeded inputs, and compare."""
+from __future__ import annotations
+
+import sys
+from typing import Optional
+
+import numpy as np
+import torch
+
+from oracle import sparse_mla as O
+from sparse_mla_attention_top_amd import smla
+
+OUT_TOL = 1e-2      # max-abs on the bf16 output vs the fp64 oracle ...
+OUT_REL = 2.0 ** -8  # ... plus the bf16 rounding allowance: the output is stored in
+                     # bf16 (half-ulp 2^-9 |x|) and P enters the P.V product in bf16
+                     # (2^-9 relative), so |gpu - ref| <= 1e-2 + 2^-8 |ref|. Outputs
+                     # below ~2.5 in magnitude (every row with more than a few valid
+                     # slots) are held to the plain 1e-2.
+LSE_TOL = 1e-3      # max-abs on the LSE
+
+
+def say(msg: str) -> None:
+    """Name the case before a GPU step (flushed, so a fault still shows it)."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """bf16 tensor -> numpy uint16 bit patterns (CPU)."""
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def q_f64(q: torch.Tensor) -> np.ndarray:
+    return O.bf16_bits_to_f64(bits(q))
+
+
+def compare(out_gpu: torch.Tensor, lse_gpu: Optional[torch.Tensor], out_ref: np.ndarray,
+            lse_ref: Optional[np.ndarray], what: str):
+    o = out_gpu.float().cpu().numpy().astype(np.float64)
+    assert o.shape == out_ref.shape, (what, o.shape, out_ref.shape)
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    diff = np.abs(o - out_ref)
+    err = diff.max() if o.size else 0.0
+    excess = (diff - (OUT_TOL + OUT_REL * np.abs(out_ref))).max() if o.size else 0.0
+    assert excess <= 0, (f"{what}: out err {err:.3e} exceeds 1e-2 + 2^-8|ref| "
+                         f"(worst excess {excess:.3e})")
+    lerr = 0.0
+    if lse_gpu is not None and lse_ref is not None:
+        l = lse_gpu.float().cpu().numpy().astype(np.float64)
+        assert l.shape == lse_ref.shape
+        inf_ref = np.isneginf(lse_ref)
+        assert (np.isneginf(l) == inf_ref).all(), f"{what}: -inf pattern of LSE differs"
+        if (~inf_ref).any():
+            lerr = np.abs(l[~inf_ref] - lse_ref[~inf_ref]).max()
+        assert lerr <= LSE_TOL, f"{what}: lse max-abs err {lerr:.3e} > {LSE_TOL}"
+    return err, lerr
+
+
+def oracle_for(q: torch.Tensor, cache_bits: np.ndarray, global_idx: np.ndarray, scale: float,
+               lengths: Optional[np.ndarray] = None, tokens=None, kv_format: int = O.KV_BF16,
+               k_scale: float = 1.0, group_scales: Optional[np.ndarray] = None):
+    sel = np.arange(q.shape[0]) if tokens is None else np.asarray(tokens)
+    qf = q_f64(q[torch.as_tensor(sel)])
+    idx = global_idx[sel]
+    ln = None if lengths is None else np.asarray(lengths)[sel]
+    return O.attention(qf, cache_bits, kv_format, idx, scale, topk_length=ln, k_scale=k_scale,
+                       group_scales=group_scales)

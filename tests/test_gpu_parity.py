@@ -1,0 +1,243 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Bit-exact for index conversion; max-abs 1e-2 on the bf16 output and 1e-3 on
+the LSE for attention (the tolerances the build targets state)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sparse_mla as O
+from parity_util import LSE_TOL, OUT_TOL, bits, compare, oracle_for, q_f64, say
+from sparse_mla_attention_top_amd import inputs as I
+from sparse_mla_attention_top_amd import smla
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gpu_convert(req, bt, loc, block_size=64, stride=0):
+    g, v = smla.convert_indices(req.to(DEV), bt.to(DEV), loc.to(DEV), block_size=block_size,
+                                block_stride_rows=stride)
+    torch.cuda.synchronize()
+    return g.cpu().numpy(), v.cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# index conversion (bit-exact)
+# ---------------------------------------------------------------------------
+
+def test_convert_golden_examples():
+    cases = json.load(open(os.path.join(GOLDEN, "convert_examples.json")))["cases"]
+    for c in cases:
+        say(f"convert golden {c['name']}")
+        g, v = _gpu_convert(torch.tensor(c["req_id"], dtype=torch.int32),
+                            torch.tensor(c["block_table"], dtype=torch.int32),
+                            torch.tensor(c["topk_local"], dtype=torch.int32), c["block_size"])
+        assert g.tolist() == c["expect_global"], c["name"]
+        assert v.tolist() == c["expect_valid"], c["name"]
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_late", "decode_bf16", "nope_fp8", "prefill_bf16", "longctx_fp8"])
+def test_convert_workloads_bitexact(name):
+    w = I.generate(I.SPECS[name], with_values=False)
+    say(f"convert workload {name}")
+    g, v = _gpu_convert(w.req_id, w.block_table, w.topk_local)
+    go, vo = O.convert_indices(w.req_id.numpy(), w.block_table.numpy(), w.topk_local.numpy(), 64)
+    assert (g == go).all() and (v == vo).all()
+    assert (v == w.valid.numpy()).all()
+
+
+def test_convert_invalid_corners_bitexact():
+    rng = np.random.default_rng(17)
+    R, MB, B, T, K = 5, 7, 16, 37, 300
+    bt = rng.permutation(R * MB).reshape(R, MB).astype(np.int32)
+    bt[2, 3] = -1
+    bt[4, 0] = -5
+    req = rng.integers(0, R, T).astype(np.int32)
+    loc = rng.integers(-3, MB * B + 10, (T, K)).astype(np.int32)
+    for stride in (0, 3 * B):
+        say(f"convert corners stride={stride}")
+        g, v = _gpu_convert(torch.from_numpy(req), torch.from_numpy(bt), torch.from_numpy(loc), B, stride)
+        go, vo = O.convert_indices(req, bt, loc, B, B if stride == 0 else stride)
+        assert (g == go).all() and (v == vo).all()
+
+
+# ---------------------------------------------------------------------------
+# attention on the workload specs
+# ---------------------------------------------------------------------------
+
+def _run_workload(w, entry, tokens=None, num_splits=0, scale=None):
+    spec = w.spec
+    scale = spec.softmax_scale if scale is None else scale
+    q = w.q.to(DEV)
+    kv = w.kv_src.to(DEV).view(spec.num_blocks, I.BLOCK_SIZE, spec.d)
+    gidx, vcnt = smla.convert_indices(w.req_id.to(DEV), w.block_table.to(DEV), w.topk_local.to(DEV))
+    qn, qr = q[..., :512], (q[..., 512:] if spec.d_rope else None)
+    if entry == "decode":
+        out, lse = smla.decode_fwd(qn, qr, kv, gidx, scale, topk_length=vcnt, num_splits=num_splits)
+    else:
+        out, lse = smla.prefill_fwd(qn, qr, kv, gidx, scale, topk_length=vcnt, return_lse=True)
+    torch.cuda.synchronize()
+    go, vo = O.convert_indices(w.req_id.cpu().numpy(), w.block_table.cpu().numpy(), w.topk_local.cpu().numpy(), 64)
+    sel = np.arange(spec.num_tokens) if tokens is None else np.asarray(tokens)
+    # the oracle gathers only the rows it needs
+    ref_o, ref_l = oracle_for(w.q.cpu(), bits(w.kv_src), go, scale, vo, tokens=sel)
+    return compare(out[torch.as_tensor(sel, device=DEV)], lse[torch.as_tensor(sel, device=DEV)], ref_o, ref_l,
+                   f"{spec.name}/{entry}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_late"])
+@pytest.mark.parametrize("entry", ["decode", "prefill"])
+def test_tiny_workload(name, entry):
+    say(f"attention {name} {entry}")
+    w = I.generate(I.SPECS[name])
+    _run_workload(w, entry)
+
+
+def test_decode_bf16_full_size():
+    """The bf16 decode workload (32 requests x 8192 context, h=128, top-k 2048)
+    at full size, every output element, in the launch configuration the
+    benchmark times (automatic splits)."""
+    spec = I.SPECS["decode_bf16"]
+    say("attention decode_bf16 full")
+    w = I.generate(spec)
+    err, lerr = _run_workload(w, "decode")
+    print(f"decode_bf16 full: out err {err:.2e} lse err {lerr:.2e}")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 8])
+def test_decode_splits(splits):
+    spec = I.SPECS["decode_bf16"].scaled(num_requests=6, seed=212)
+    say(f"attention decode splits={splits}")
+    w = I.generate(spec)
+    _run_workload(w, "decode", num_splits=splits)
+
+
+def test_prefill_bf16_full_size_sampled():
+    """The bf16 prefill workload (4096 tokens, h=128, top-k 2048, causal
+    indices) at full size; the oracle checks a sample of tokens covering
+    short rows, the 2048 boundary and the longest rows."""
+    spec = I.SPECS["prefill_bf16"]
+    say("attention prefill_bf16 full (sampled)")
+    w = I.generate(spec, kv_device=DEV)
+    toks = [0, 1, 2, 31, 32, 33, 100, 1023, 2046, 2047, 2048, 2049, 3000, 4094, 4095]
+    err, lerr = _run_workload(w, "prefill", tokens=toks)
+    print(f"prefill_bf16 full sampled: out err {err:.2e} lse err {lerr:.2e}")
+
+
+# ---------------------------------------------------------------------------
+# edge shapes with global indices
+# ---------------------------------------------------------------------------
+
+def _run_case(c, scale, entry="prefill", topk_length="lengths", num_splits=0, slots_view=None):
+    q = c.q.to(DEV)
+    d_rope = q.shape[2] - 512
+    kv = c.kv_src.to(DEV)
+    idx = c.indices.to(DEV)
+    ln = c.lengths.to(DEV) if topk_length == "lengths" else None
+    qn, qr = q[..., :512], (q[..., 512:] if d_rope else None)
+    if entry == "decode":
+        out, lse = smla.decode_fwd(qn, qr, kv, idx, scale, topk_length=ln, num_splits=num_splits)
+    else:
+        out, lse = smla.prefill_fwd(qn, qr, kv, idx, scale, topk_length=ln, return_lse=True)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_for(c.q, bits(c.kv_src), c.indices.numpy(), scale,
+                              None if ln is None else c.lengths.numpy())
+    return out, lse, compare(out, lse, ref_o, ref_l, "edge")
+
+
+@pytest.mark.parametrize("h", [1, 16, 33, 64, 100, 128])
+@pytest.mark.parametrize("d_rope", [64, 0])
+def test_heads_and_nope(h, d_rope):
+    say(f"edge heads h={h} d_rope={d_rope}")
+    c = I.random_case(T=3, h=h, d_rope=d_rope, topk=100, num_slots=500, seed=h * 10 + d_rope,
+                      lengths=[100, 37, 64])
+    for entry in ("prefill", "decode"):
+        _run_case(c, 0.07, entry)
+
+
+@pytest.mark.parametrize("topk,lengths", [(1, [1, 0, 1]), (31, [31, 5, 30]), (33, [33, 32, 1]),
+                                          (257, [257, 200, 129]), (2048, [2048, 1500, 33])])
+def test_topk_widths_and_ragged_tails(topk, lengths):
+    say(f"edge topk={topk} lengths={lengths}")
+    c = I.random_case(T=3, h=128, d_rope=64, topk=topk, num_slots=4096, seed=topk, lengths=lengths)
+    for entry in ("prefill", "decode"):
+        _run_case(c, 192 ** -0.5, entry)
+
+
+def test_scattered_invalid_without_lengths():
+    """-1, other negatives and slots >= num_slots anywhere in the row are
+    skipped when no length array is passed."""
+    say("edge scattered invalid")
+    c = I.random_case(T=4, h=64, d_rope=64, topk=200, num_slots=300, seed=5)
+    g = torch.Generator().manual_seed(6)
+    mask = torch.rand(c.indices.shape, generator=g) < 0.3
+    c.indices[mask] = -1
+    c.indices[0, 7] = -9
+    c.indices[1, 3] = 300
+    c.indices[2, 150] = 2 ** 31 - 1
+    for entry in ("prefill", "decode"):
+        _run_case(c, 0.1, entry, topk_length=None)
+
+
+def test_empty_rows_give_merge_identity():
+    say("edge empty rows")
+    c = I.random_case(T=3, h=64, d_rope=64, topk=64, num_slots=100, seed=8, lengths=[64, 0, 10])
+    c.indices[2, :] = -1
+    for entry in ("prefill", "decode"):
+        out, lse, _ = _run_case(c, 0.1, entry)
+        assert (out[1:].float() == 0).all() and torch.isneginf(lse[1:]).all()
+
+
+def test_large_logit_jump_takes_the_exact_path():
+    """A slot whose score exceeds the first tile's maximum by far more than the
+    reference headroom: the result must still match the oracle."""
+    say("edge large logit jump")
+    c = I.random_case(T=2, h=32, d_rope=64, topk=128, num_slots=256, seed=9)
+    # make slot used at position 100 of each row strongly aligned with head 0's query
+    for t in range(2):
+        s = int(c.indices[t, 100])
+        c.kv_src[s] = (c.q[t, 0].float() * 4.0).to(torch.bfloat16)
+    for entry in ("prefill", "decode"):
+        _run_case(c, 0.1, entry)
+
+
+def test_deterministic_bitwise():
+    say("determinism")
+    c = I.random_case(T=8, h=128, d_rope=64, topk=512, num_slots=2048, seed=12)
+    q, kv, idx = c.q.to(DEV), c.kv_src.to(DEV), c.indices.to(DEV)
+    a, la = smla.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, num_splits=4)
+    b, lb = smla.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, num_splits=4)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
+
+
+def test_strided_query_and_output_views():
+    """q_nope / q_rope as views of one [T, h, 576] tensor and an output with a
+    padded head stride."""
+    say("strided views")
+    c = I.random_case(T=5, h=20, d_rope=64, topk=96, num_slots=640, seed=13)
+    q = c.q.to(DEV)
+    big = torch.zeros((5, 20, 640), dtype=torch.bfloat16, device=DEV)
+    out = big[:, :, :512]
+    o, l = smla.prefill_fwd(q[..., :512], q[..., 512:], c.kv_src.to(DEV), c.indices.to(DEV), 0.05,
+                            out=out, return_lse=True)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_for(c.q, bits(c.kv_src), c.indices.numpy(), 0.05)
+    compare(out, l, ref_o, ref_l, "strided")
+    assert (big[:, :, 512:] == 0).all()
+
+
+def test_decode_matches_prefill():
+    say("decode vs prefill")
+    c = I.random_case(T=6, h=128, d_rope=64, topk=1024, num_slots=3000, seed=14, lengths=[1024, 900, 513, 64, 33, 1])
+    q, kv, idx, ln = c.q.to(DEV), c.kv_src.to(DEV), c.indices.to(DEV), c.lengths.to(DEV)
+    a, la = smla.prefill_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, topk_length=ln, return_lse=True)
+    b, lb = smla.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, topk_length=ln, num_splits=4)
+    torch.cuda.synchronize()
+    assert (a.float() - b.float()).abs().max().item() <= 2 * OUT_TOL
+    assert (la - lb).abs().max().item() <= 2 * LSE_TOL
