@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse MLA hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+request-local -> global index conversion, then the sparse attention (decode:
+split top-k + LSE combine; prefill: one workgroup per token). Prints one JSON
+line with the throughput, the roofline position of the attention kernel and
+the fp64 CPU oracle timed on the host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode_bf16]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+WORKLOAD_TEXT = {
+    "decode_bf16": "sparse MLA decode, bf16 paged cache [4096,64,576]: 32 requests x 8192 context, "
+                   "1 query token each, h=128, top-k=2048 all valid, scale 0.0723, out + LSE",
+    "prefill_bf16": "sparse MLA prefill, bf16 cache [64,64,576]: 1 request of 4096 new tokens, h=128, "
+                    "top-k=2048, causal indices (valid = min(2048, pos+1)), scale 192^-0.5",
+    "tiny": "tiny sparse MLA: 4 tokens, h=16, top-k=64, cache 256 x 576 bf16",
+}
+ENTRY = {"decode_bf16": "decode", "prefill_bf16": "prefill", "tiny": "decode"}
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("attn_fwd.hip", "smla_device.h", "smla_internal.h"):
+        h.update(open(os.path.join(ROOT, "sparse_mla_attention_top_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(config: str):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"attn_traffic_{config}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def algorithmic_bytes(spec, gidx_np, valid_np, row_bytes: int) -> int:
+    """Unique cache rows gathered x row bytes + Q + out + LSE + indices."""
+    import numpy as np
+    rows = []
+    for t in range(gidx_np.shape[0]):
+        rows.append(gidx_np[t, :valid_np[t]])
+    uniq = np.unique(np.concatenate(rows)).size
+    T, h, D = spec.num_tokens, spec.heads, spec.d
+    q = T * h * D * 2
+    out = T * h * 512 * 2
+    lse = T * h * 4
+    idx = int(valid_np.sum()) * 4 + T * 4
+    return int(uniq * row_bytes + q + out + lse + idx)
+
+
+def hip_elapsed_ms(a, b) -> float:
+    """hipEventElapsedTime on the raw handles of two torch events recorded by
+    the library (torch's own bookkeeping does not see those records)."""
+    import ctypes
+    global _HIP
+    if "_HIP" not in globals():
+        _HIP = ctypes.CDLL("libamdhip64.so")
+        _HIP.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        _HIP.hipEventElapsedTime.restype = ctypes.c_int
+    ms = ctypes.c_float()
+    rc = _HIP.hipEventElapsedTime(ctypes.byref(ms), a.cuda_event, b.cuda_event)
+    if rc != 0:
+        raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+    return ms.value
+
+
+def cpu_baseline(w, gidx_np, valid_np, min_seconds: float):
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle import sparse_mla as O
+    spec = w.spec
+    qf = O.bf16_bits_to_f64(w.q.cpu().view(torch.int16).numpy().view(np.uint16))
+    cache = w.kv_src.cpu().view(torch.int16).numpy().view(np.uint16)
+    n_tok, reps = 0, 0
+    t0 = time.perf_counter()
+    tokens = np.arange(spec.num_tokens)
+    if spec.num_tokens > 64:           # prefill: a strided sample of tokens, long rows included
+        tokens = np.linspace(spec.num_tokens - 1, 0, 64).astype(int)
+    while True:
+        O.attention(qf, cache, O.KV_BF16, gidx_np, spec.softmax_scale, topk_length=valid_np, tokens=tokens)
+        n_tok += len(tokens)
+        reps += 1
+        if time.perf_counter() - t0 >= min_seconds:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    sample = (f"{len(tokens)} tokens of the same workload (all h={spec.heads} heads, their full top-k rows) "
+              f"x {reps} repetitions, numpy fp64")
+    return {"value": n_tok / dt, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="decode_bf16", choices=sorted(ENTRY))
+    ap.add_argument("--rotate", type=int, default=6, help="independent cache copies cycled through (cold L2/MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the design notes describe how it would shard); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from sparse_mla_attention_top_amd import inputs as I
+    from sparse_mla_attention_top_amd import smla
+
+    dev = "cuda"
+    spec = I.SPECS[args.config]
+    entry = ENTRY[args.config]
+    w = I.generate(spec, kv_device=dev)
+    R = max(1, args.rotate)
+    caches = [w.kv_src] + [I.draw_cache_copy(spec, k, dev) for k in range(1, R)]
+    caches = [c.view(spec.num_blocks, I.BLOCK_SIZE, spec.d) for c in caches]
+    q = w.q.to(dev)
+    qn, qr = q[..., :512], (q[..., 512:] if spec.d_rope else None)
+    req, bt, loc = w.req_id.to(dev), w.block_table.to(dev), w.topk_local.to(dev)
+    T, H, K = spec.num_tokens, spec.heads, spec.topk
+    gidx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    vcnt = torch.empty((T,), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws_bytes = smla.decode_workspace_size(T, H, K) if entry == "decode" else 0
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    splits = smla.decode_num_splits(T, H, K) if entry == "decode" else 1
+
+    def step(k: int):
+        smla.convert_indices(req, bt, loc, out=gidx, valid_counts=vcnt)
+        if entry == "decode":
+            smla.decode_fwd(qn, qr, caches[k % R], gidx, spec.softmax_scale, topk_length=vcnt,
+                            out=out, lse=lse, workspace=ws)
+        else:
+            smla.prefill_fwd(qn, qr, caches[k % R], gidx, spec.softmax_scale, topk_length=vcnt,
+                             out=out, lse=lse)
+
+    # eager warmup and the eager reference of step 0
+    for k in range(args.warmup):
+        step(k)
+    step(0)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+
+    # one graph = R consecutive steps (one per cache copy)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        step(0)
+        torch.cuda.current_stream().synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for k in range(R):
+                step(k)
+    torch.cuda.synchronize()
+    replays = max(1, (args.steps + R - 1) // R)
+    steps = replays * R
+    # every replay must reproduce the eager result (replays interleaved with eager work)
+    for _ in range(2):
+        g.replay()
+        torch.cuda.synchronize()
+        step(0)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)) and torch.equal(lse, ref_lse)
+    g.replay()
+    torch.cuda.synchronize()
+
+    t0 = time.perf_counter()
+    for _ in range(replays):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    dt = t1 - t0
+    ms_per_step = dt / steps * 1e3
+    tokens_per_s = T * steps / dt
+
+    # attention kernel duration: HIP events around the kernel, queue backed up first
+    n_ev = min(steps, 120)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for a, b in evs:          # torch creates the HIP events on first record
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    for k in range(n_ev):
+        smla.set_timing_events(*evs[k])
+        step(k)
+    smla.set_timing_events(None, None)
+    torch.cuda.synchronize()
+    kern_ms = sum(hip_elapsed_ms(a, b) for a, b in evs) / n_ev
+
+    gidx_np, vcnt_np = gidx.cpu().numpy(), vcnt.cpu().numpy()
+    row_bytes = I.kv_row_bytes(spec)
+    alg_bytes = algorithmic_bytes(spec, gidx_np, vcnt_np, row_bytes)
+    flops = I.algorithmic_flops(spec, vcnt)
+    tflops = flops * steps / dt / 1e12
+    ai = flops / alg_bytes
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai < ridge:
+        achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = flops / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roof["traffic"] = traffic_from_profiles(args.config)
+    roofline_time = max(alg_bytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, gidx_np, vcnt_np, args.cpu_seconds)
+
+    line = {
+        "metric": "sparse-MLA query tokens/s and TFLOP/s (h=128, top-k=2048) + % of roofline",
+        "value": round(tokens_per_s, 1),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config, "num_tokens": T, "heads": H,
+                   "topk": K, "entry": f"smla_{entry}_fwd", "splits": splits, "cache_copies_rotated": R,
+                   "timing": "HIP graph of R steps replayed; cold L2/MALL by cache rotation"},
+        "tflops": round(tflops, 2),
+        "pct_of_path_roofline": round(100 * roofline_time / (dt / steps), 2),
+        "attn_kernel_us": round(kern_ms * 1e3, 3),
+        "alg_bytes_per_step": alg_bytes,
+        "alg_flops_per_step": flops,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

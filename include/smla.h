@@ -177,6 +177,16 @@ int smla_cache_write(const void* kv_c, int64_t kv_c_stride, const void* k_pe, in
                      int32_t kv_format, float k_scale, void* kv_cache, int64_t num_slots,
                      int64_t kv_row_stride_bytes, float* group_scales, void* stream);
 
+/*
+ * Profiling hook (not part of the computation). When set for the calling
+ * thread, every following smla_decode_fwd / smla_prefill_fwd call records
+ * `start` (a hipEvent_t) on its stream immediately before the main attention
+ * kernel and `end` immediately after it, so the kernel's own duration can be
+ * read with hipEventElapsedTime while the split combine is excluded. Pass
+ * NULL, NULL to clear. The events are owned by the caller.
+ */
+int smla_set_timing_events(void* start, void* end);
+
 /* Thread-local description of the last non-OK return ("" if none). */
 const char* smla_last_error(void);
 

@@ -505,8 +505,13 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
   }
   const int grid = kp.head_blocks == 2 ? ((kp.num_items + 7) / 8) * 16 : kp.num_items;
   if (a.kv_format != 0) return hipErrorInvalidValue;
+  if (a.ev_start) {
+    hipError_t er = hipEventRecord(a.ev_start, stream);
+    if (er != hipSuccess) return er;
+  }
   if (a.d_rope == 64) launch_kernel<576>(kp, grid, stream); else launch_kernel<512>(kp, grid, stream);
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && a.ev_end) e = hipEventRecord(a.ev_end, stream);
   if (e != hipSuccess || splits == 1) return e;
   const int64_t total = (int64_t)a.num_tokens * a.num_heads * (kDLatent / 4);
   smla_combine_kernel<<<(int)((total + 255) / 256), 256, 0, stream>>>(

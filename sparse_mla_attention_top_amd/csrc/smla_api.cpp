@@ -13,6 +13,7 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_end = nullptr;
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -104,6 +105,8 @@ smla::AttnArgs to_internal(const smla_attn_args* a) {
   r.out_sh = a->out_stride_head;
   r.lse = a->lse;
   r.lse_st = a->lse_stride_tok;
+  r.ev_start = g_ev_start;
+  r.ev_end = g_ev_end;
   return r;
 }
 
@@ -114,6 +117,13 @@ extern "C" {
 const char* smla_last_error(void) { return g_err; }
 
 const char* smla_version(void) { return "smla 0.1 gfx950"; }
+
+int smla_set_timing_events(void* start, void* end) {
+  if ((start == nullptr) != (end == nullptr)) return fail(SMLA_ERR_INVALID_ARG, "set both events or neither");
+  g_ev_start = (hipEvent_t)start;
+  g_ev_end = (hipEvent_t)end;
+  return ok();
+}
 
 int smla_convert_indices(const int32_t* req_id, const int32_t* block_table, int32_t num_reqs,
                          int32_t max_blocks, int64_t bt_row_stride, const int32_t* topk_local,

@@ -53,6 +53,7 @@ struct AttnArgs {
   int64_t out_st, out_sh;
   float* lse;
   int64_t lse_st;
+  hipEvent_t ev_start, ev_end;   // optional, recorded around the main kernel
 };
 
 constexpr int kTileRows = 32;

@@ -227,3 +227,11 @@ def random_case(T: int, h: int, d_rope: int, topk: int, num_slots: int, seed: in
         idx[t, :v] = torch.randperm(num_slots, generator=g)[:v].to(torch.int32)
     return RandomCase(q.to(device), kv.to(device), idx.to(device),
                       torch.tensor(lengths, dtype=torch.int32).to(device))
+
+
+def draw_cache_copy(spec: WorkloadSpec, copy: int, device) -> torch.Tensor:
+    """Another independent draw of the cache rows ([S, D] bf16) of ``spec``
+    (copy 0 is the one ``generate`` returns); used to rotate inputs so that
+    repeated steps do not find their rows in the last-level cache."""
+    stream = 4 if copy == 0 else 100 + copy
+    return _bf16_normal((spec.num_slots, spec.d), spec.seed, stream, device)

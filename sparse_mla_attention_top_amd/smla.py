@@ -29,6 +29,7 @@ EXPORTED = (
     "smla_decode_fwd",
     "smla_prefill_fwd",
     "smla_cache_write",
+    "smla_set_timing_events",
     "smla_last_error",
     "smla_version",
 )
@@ -96,6 +97,8 @@ def load() -> ctypes.CDLL:
     lib.smla_prefill_fwd.restype = ctypes.c_int
     lib.smla_cache_write.argtypes = [vp, i64, vp, i64, vp, i32, i32, i32, f32, vp, i64, i64, vp, vp]
     lib.smla_cache_write.restype = ctypes.c_int
+    lib.smla_set_timing_events.argtypes = [vp, vp]
+    lib.smla_set_timing_events.restype = ctypes.c_int
     lib.smla_last_error.argtypes = []
     lib.smla_last_error.restype = ctypes.c_char_p
     lib.smla_version.argtypes = []
@@ -266,6 +269,14 @@ def cache_write(kv_c: torch.Tensor, k_pe: Optional[torch.Tensor], slot_mapping: 
                                  _ptr(slot_mapping), kv_c.shape[0], d_rope, kv_format, float(k_scale),
                                  _ptr(kv_cache), S, row_stride, _ptr(group_scales), _stream(stream))
     _check("smla_cache_write", rc)
+
+
+def set_timing_events(start=None, end=None) -> None:
+    """Record torch.cuda.Event pair around the main attention kernel of the
+    following calls on this thread (None, None clears)."""
+    rc = load().smla_set_timing_events(None if start is None else start.cuda_event,
+                                       None if end is None else end.cuda_event)
+    _check("smla_set_timing_events", rc)
 
 
 def version() -> str:
