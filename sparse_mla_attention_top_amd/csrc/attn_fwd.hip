@@ -59,6 +59,9 @@ __device__ __forceinline__ bf16x8 lds_ld128(const lds_char* p) {
 __device__ __forceinline__ void lds_st64(lds_char* p, uint64_t v) {
   *(__attribute__((address_space(3))) uint64_t*)p = v;
 }
+__device__ __forceinline__ void lds_st128(lds_char* p, bf16x8 v) {
+  *(__attribute__((address_space(3))) bf16x8*)p = v;
+}
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -73,6 +76,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // a later score exceeds m + 64 the workgroup restarts: a max-only pass finds
 // the exact per-head maximum, then the full pass runs with it.
 constexpr float kRefHeadroom = 64.0f;
+constexpr int kLatKS = kDLatent / 32;   // k-steps over the 512 latent channels
 
 template <int D>
 struct TileShape {
@@ -99,6 +103,9 @@ smla_attn_bf16_kernel(KParams p) {
   __shared__ float s_l[4 * 32];
   __shared__ float s_inv[64];
   __shared__ int s_flag;
+  __shared__ int s_nrows;
+  __shared__ __attribute__((aligned(16))) char s_qrope[(QKS > kLatKS ? 4 * 2 * (QKS - kLatKS) : 1) * 64 * 16];
+  lds_char* qrope = (lds_char*)s_qrope;
 
   lds_char* tiles = (lds_char*)s_tiles;
   lds_char* pbuf = (lds_char*)s_p;
@@ -135,110 +142,131 @@ smla_attn_bf16_kernel(KParams p) {
   if (p.topk_length) len = min(max(p.topk_length[t], 0), p.topk);
   const int row0 = split * p.split_rows;
   const int nrows = max(0, min(len, row0 + p.split_rows) - row0);
-  const int ntiles = (nrows + kTileRows - 1) / kTileRows;
 
   // ---- Q^T as the B operand of 16x16x32: lane holds head hb + 32hg + 16nbq + li,
   //      channels 32ks + 8lg .. +8 (ks < 16 latent, ks >= 16 rope)
-  bf16x8 q[2][QKS];
+  //      The 16 latent k-steps stay in registers; the rope k-steps (D = 576) are
+  //      staged in LDS in the same lane layout and read once per tile.
+  bf16x8 q[2][kLatKS];
 #pragma unroll
   for (int nbq = 0; nbq < 2; nbq++) {
     const int head = hb + 32 * hg + 16 * nbq + li;
     const bool valid = head < H;
     const int hq = valid ? head : 0;
     const uint16_t* qn = p.q_nope + t * p.qn_st + hq * p.qn_sh + 8 * lg;
-    const uint16_t* qr = p.q_rope + t * p.qr_st + hq * p.qr_sh + 8 * lg;
 #pragma unroll
-    for (int ks = 0; ks < QKS; ks++)
-      q[nbq][ks] = ks < 16 ? *(const bf16x8*)(qn + 32 * ks) : *(const bf16x8*)(qr + 32 * (ks - 16));
+    for (int ks = 0; ks < kLatKS; ks++) q[nbq][ks] = *(const bf16x8*)(qn + 32 * ks);
     if (!valid) {
 #pragma unroll
-      for (int ks = 0; ks < QKS; ks++) q[nbq][ks] = (bf16x8){};
+      for (int ks = 0; ks < kLatKS; ks++) q[nbq][ks] = (bf16x8){};
+    }
+    if (QKS > kLatKS) {
+      const uint16_t* qr = p.q_rope + t * p.qr_st + hq * p.qr_sh + 8 * lg;
+#pragma unroll
+      for (int ks = kLatKS; ks < QKS; ks++) {
+        bf16x8 v = *(const bf16x8*)(qr + 32 * (ks - kLatKS));
+        if (!valid) v = (bf16x8){};
+        lds_st128(qrope + (((w * 2 + nbq) * (QKS - kLatKS) + (ks - kLatKS)) * 64 + l) * 16, v);
+      }
     }
   }
 
-  // ---- the workgroup's index range -> LDS (-1 marks an entry that does not take part)
+  // ---- the workgroup's index range -> LDS (-1 marks an entry that does not take
+  //      part); tiles past the last valid entry (an invalid tail) are not visited
+  if (threadIdx.x == 0) {
+    s_flag = 0;
+    s_nrows = 0;
+  }
+  __syncthreads();
   const int32_t* irow = p.indices + (int64_t)t * p.idx_stride + row0;
-  for (int j = threadIdx.x; j < ntiles * kTileRows; j += 256) {
+  const int span = (nrows + kTileRows - 1) / kTileRows * kTileRows;
+  int last = 0;
+  for (int j = threadIdx.x; j < span; j += 256) {
     int g = -1;
     if (j < nrows) {
       g = irow[j];
       if (g < 0 || (int64_t)g >= p.num_slots) g = -1;
     }
     s_idx[j] = g;
+    if (g >= 0) last = j + 1;
   }
-  if (threadIdx.x == 0) s_flag = 0;
+  for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+  if (l == 0) atomicMax(&s_nrows, last);
   // Q and the indices must be in registers/LDS before the tile DMAs start:
   // later waits only count the DMAs.
   wait_vmcnt<0>();
   __syncthreads();
+  const int ntiles = (s_nrows + kTileRows - 1) / kTileRows;
 
-  // Instruction u of wave w fills the 16-byte LDS slots (4u + w)*64 + lane of
-  // the tile: slot s is row s / NC, physical chunk s % NC.
+  // DMA instruction u of wave w fills block 4u + w of the tile (chunks
+  // 2(4u + w) and 2(4u + w) + 1 of all rows); lane l loads row l (l < 32) or
+  // row (l - 40) mod 32 (l >= 32, the odd chunk), the same row for every u, so
+  // one address per tile serves all PER instructions through the immediate
+  // offset 128u.
   const uint32_t tiles_addr = (uint32_t)(uintptr_t)tiles;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int drow = l < 32 ? l : ((l - 40) & 31);
+  const uint32_t dcol = (uint32_t)(32 * wu + 16 * (l >> 5));
+  const uint32_t kv_stride = (uint32_t)p.kv_row_stride;
+  auto dma_src = [&](int tt) -> const uint8_t* {
+    const int g = max(s_idx[tt * kTileRows + drow], 0);
+    return p.kv + ((uint64_t)(uint32_t)g * kv_stride + dcol);
+  };
+  auto issue_one = [&](const uint8_t* src, int b, auto u_c) {
+    constexpr int u = decltype(u_c)::value;
+    dma_16b<128 * u>(src, __builtin_amdgcn_readfirstlane(tiles_addr + b * TILE_BYTES + (4 * u + wu) * 1024));
+  };
   auto issue_tile = [&](int tt, int b) {
-    int lo;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(lo) : "v"(l));   // keep the address math in the loop
-    const int wu = __builtin_amdgcn_readfirstlane(w);
-    int rr[PER], gg[PER];
-#pragma unroll
-    for (int u = 0; u < PER; u++) {
-      const int s = (4 * u + wu) * 64 + lo;
-      rr[u] = s / NC;
-      gg[u] = s_idx[tt * kTileRows + rr[u]];
-    }
-    const uint32_t tb = __builtin_amdgcn_readfirstlane(tiles_addr + b * TILE_BYTES);
-#pragma unroll
-    for (int u = 0; u < PER; u++) {
-      const int s = (4 * u + wu) * 64 + lo;
-      const int pc = s - rr[u] * NC;
-      const uint8_t* src = p.kv + (int64_t)max(gg[u], 0) * p.kv_row_stride + ((pc ^ swz(rr[u])) << 4);
-      dma_16b(src, tb + (4 * u + wu) * 1024);
-    }
+    const uint8_t* src = dma_src(tt);
+    static_for<PER>([&](auto u_c) { issue_one(src, b, u_c); });
   };
 
-  // K reads (A operand of 16x16x32): row 16rh + li, logical chunk 4ks + lg. With
-  // ks = 2a + j the physical chunk is 8a + ((4j + lg) ^ swz(row)).
-  int kbase[2];
-  {
-    const int krow = 16 * rh + li, ksw = swz(krow);
-#pragma unroll
-    for (int j = 0; j < 2; j++) kbase[j] = krow * RB + (((4 * j + lg) ^ ksw) << 4);
-  }
+  // K reads (A operand of 16x16x32): row 16rh + li, chunk 4ks + lg, at
+  // kbase + 2048 ks.
+  const int kbase = tile_pos(16 * rh + li, lg);
   // V transposing reads (B operand of P.V): in 16-lane group lg, lane li = 4e + q
-  // reads row 4lg + e (then 16 + 4lg + e), channels 128w + 16nb + 4q .. +3.
-  // Both rows have swizzle sw = swz(4lg + e); the physical chunk of
-  // 16w + 2nb + (q >> 1) is 16w + 8(nb >> 2) + 2((nb & 3) ^ (sw >> 1)) + ((q >> 1) ^ (sw & 1)).
-  int vbase[2][4];
+  // reads row 4lg + e (then 16 + 4lg + e), channels 128w + 16nb + 4q .. +3,
+  // at vbase[half] + 1024 nb.
+  int vbase[2];
   {
     const int e = li >> 2, q4 = li & 3;
-    const int sw = swz(4 * lg + e);
 #pragma unroll
     for (int half = 0; half < 2; half++)
-#pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const int row = 16 * half + 4 * lg + e;
-        const int chunk = 16 * w + 2 * (j ^ (sw >> 1)) + ((q4 >> 1) ^ (sw & 1));
-        vbase[half][j] = row * RB + chunk * 16 + 8 * (q4 & 1);
-      }
+      vbase[half] = tile_pos(16 * half + 4 * lg + e, 16 * w + (q4 >> 1)) + 8 * (q4 & 1);
   }
 
   // S^T[16 rows x 32 heads] of the wave for tile buffer tb, base-2 units, masked.
-  // Lane holds rows 16rh + 4lg + r (r = 0..3) of heads 32hg + 16nbq + li.
-  auto scores = [&](const lds_char* tb, uint32_t vmask, float (&tv)[2][4]) {
+  // Lane holds rows 16rh + 4lg + r (r = 0..3) of heads 32hg + 16nbq + li. The
+  // DMAs of tile dma_tt (if >= 0) are issued between the k-steps.
+  auto scores = [&](const lds_char* tb, uint32_t vmask, float (&tv)[2][4], int dma_tt) {
     f32x4 s0 = {}, s1 = {};
     constexpr int PF = 4;                      // K operand reads kept in flight
     bf16x8 a[PF];
 #pragma unroll
-    for (int ks = 0; ks < PF; ks++) a[ks] = lds_ld128(tb + kbase[ks & 1] + 128 * (ks >> 1));
-#pragma unroll
-    for (int ks = 0; ks < QKS; ks++) {
+    for (int ks = 0; ks < PF; ks++) a[ks] = lds_ld128(tb + kbase + 2048 * ks);
+    const uint8_t* dsrc = dma_tt >= 0 ? dma_src(dma_tt) : p.kv;
+    const int db = dma_tt >= 0 ? dma_tt % NBUF : 0;
+    static_for<QKS>([&](auto ks_c) {
+      constexpr int ks = decltype(ks_c)::value;
       const bf16x8 cur = a[ks % PF];
-      if (ks + PF < QKS) a[ks % PF] = lds_ld128(tb + kbase[(ks + PF) & 1] + 128 * ((ks + PF) >> 1));
+      if constexpr (ks + PF < QKS) a[ks % PF] = lds_ld128(tb + kbase + 2048 * (ks + PF));
+      if constexpr ((ks & 1) == 0 && (ks >> 1) < PER) {
+        if (dma_tt >= 0) issue_one(dsrc, db, std::integral_constant<int, (ks >> 1)>{});
+      }
       __builtin_amdgcn_sched_barrier(0);       // keep the read-ahead ahead of the MFMAs
-      s0 = mfma16x16x32(cur, q[0][ks], s0);
-      s1 = mfma16x16x32(cur, q[1][ks], s1);
+      bf16x8 b0, b1;
+      if constexpr (ks < kLatKS) {
+        b0 = q[0][ks];
+        b1 = q[1][ks];
+      } else {
+        b0 = lds_ld128(qrope + (((w * 2 + 0) * (QKS - kLatKS) + (ks - kLatKS)) * 64 + l) * 16);
+        b1 = lds_ld128(qrope + (((w * 2 + 1) * (QKS - kLatKS) + (ks - kLatKS)) * 64 + l) * 16);
+      }
+      s0 = mfma16x16x32(cur, b0, s0);
+      s1 = mfma16x16x32(cur, b1, s1);
       __builtin_amdgcn_sched_barrier(0);
-    }
+    });
+    static_assert(2 * PER <= QKS + 1, "DMA issue slots");
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const bool ok = (vmask >> (16 * rh + 4 * lg + r)) & 1;
@@ -246,15 +274,28 @@ smla_attn_bf16_kernel(KParams p) {
       tv[1][r] = ok ? s1[r] * p.scale_log2 : -INFINITY;
     }
   };
-  // maximum over the wave's 16 rows, per head
-  auto half_max = [&](const float (&tv)[2][4], float (&mx)[2]) {
+  // lane-local maximum of the 4 rows it holds, per head block
+  auto lane_max = [&](const float (&tv)[2][4], float (&mx)[2]) {
+#pragma unroll
+    for (int nbq = 0; nbq < 2; nbq++)
+      mx[nbq] = fmaxf(fmaxf(tv[nbq][0], tv[nbq][1]), fmaxf(tv[nbq][2], tv[nbq][3]));
+  };
+  // maximum over the workgroup's 32 rows of a tile (or of a whole pass), per head
+  auto wg_max = [&](float (&mx)[2]) {
 #pragma unroll
     for (int nbq = 0; nbq < 2; nbq++) {
-      float m = fmaxf(fmaxf(tv[nbq][0], tv[nbq][1]), fmaxf(tv[nbq][2], tv[nbq][3]));
+      float m = mx[nbq];
       m = fmaxf(m, __shfl_xor(m, 16, 64));
       m = fmaxf(m, __shfl_xor(m, 32, 64));
       mx[nbq] = m;
     }
+    if (lg == 0) {
+      s_m[w * 32 + li] = mx[0];
+      s_m[w * 32 + 16 + li] = mx[1];
+    }
+    lds_barrier();
+    mx[0] = fmaxf(mx[0], s_m[(w ^ 2) * 32 + li]);
+    mx[1] = fmaxf(mx[1], s_m[(w ^ 2) * 32 + 16 + li]);
   };
 
   float m_ref[2] = {-INFINITY, -INFINITY};
@@ -273,22 +314,18 @@ smla_attn_bf16_kernel(KParams p) {
     for (int tt = 0; tt < ntiles; tt++) {
       if (tt + 1 < ntiles) wait_vmcnt<PER>(); else wait_vmcnt<0>();
       lds_barrier();
-      if (tt + 2 < ntiles) issue_tile(tt + 2, (tt + 2) % NBUF);
+      const int dma_tt = (tt + 2 < ntiles) ? tt + 2 : -1;
       const lds_char* tb = tiles + (tt % NBUF) * TILE_BYTES;
       const uint32_t vmask = (uint32_t)__ballot((l < 32) ? (s_idx[tt * kTileRows + l] >= 0) : 0);
 
       float tv[2][4];
-      scores(tb, vmask, tv);
+      scores(tb, vmask, tv, dma_tt);
       float mx[2];
-      half_max(tv, mx);
-      if (!have_ref && vmask != 0) {                       // uniform: first tile with a valid row
-        if (lg == 0) {
-          s_m[w * 32 + li] = mx[0];
-          s_m[w * 32 + 16 + li] = mx[1];
-        }
-        lds_barrier();
-        m_ref[0] = fmaxf(mx[0], s_m[(w ^ 2) * 32 + li]);
-        m_ref[1] = fmaxf(mx[1], s_m[(w ^ 2) * 32 + 16 + li]);
+      lane_max(tv, mx);
+      if (!have_ref) {                                     // uniform: first tile with a valid row
+        wg_max(mx);
+        m_ref[0] = mx[0];
+        m_ref[1] = mx[1];
         have_ref = true;
       }
       if (fmaxf(mx[0] - m_ref[0], mx[1] - m_ref[1]) > kRefHeadroom) s_flag = 1;
@@ -310,17 +347,22 @@ smla_attn_bf16_kernel(KParams p) {
 #pragma unroll
       for (int mb = 0; mb < 4; mb++) pa[mb] = lds_ld128(pbuf + (mb * 64 + l) * 16);
 
-      // O[64 heads x 128 ch] += P[64 x 32] . V[32 x 128]
-      s16x4 vr[2][2];
-      vr[0][0] = lds_read_tr16(tb + vbase[0][0]);
-      vr[0][1] = lds_read_tr16(tb + vbase[1][0]);
+      // O[64 heads x 128 ch] += P[64 x 32] . V[32 x 128]; V reads run two n-blocks ahead
+      constexpr int VPF = 2;
+      s16x4 vr[VPF + 1][2];
+#pragma unroll
+      for (int nb = 0; nb < VPF; nb++) {
+        vr[nb][0] = lds_read_tr16(tb + vbase[0] + 1024 * nb);
+        vr[nb][1] = lds_read_tr16(tb + vbase[1] + 1024 * nb);
+      }
 #pragma unroll
       for (int nb = 0; nb < 8; nb++) {
-        const s16x4 v0 = vr[nb & 1][0];
-        const s16x4 v1 = vr[nb & 1][1];
-        if (nb + 1 < 8) {
-          vr[(nb + 1) & 1][0] = lds_read_tr16(tb + vbase[0][(nb + 1) & 3] + 128 * ((nb + 1) >> 2));
-          vr[(nb + 1) & 1][1] = lds_read_tr16(tb + vbase[1][(nb + 1) & 3] + 128 * ((nb + 1) >> 2));
+        const s16x4 v0 = vr[nb % (VPF + 1)][0];
+        const s16x4 v1 = vr[nb % (VPF + 1)][1];
+        if (nb + VPF < 8) {
+          const int n2 = nb + VPF;
+          vr[n2 % (VPF + 1)][0] = lds_read_tr16(tb + vbase[0] + 1024 * n2);
+          vr[n2 % (VPF + 1)][1] = lds_read_tr16(tb + vbase[1] + 1024 * n2);
         }
         __builtin_amdgcn_sched_barrier(0);
         const bf16x8 bv = concat_bf16x4(v0, v1);
@@ -338,23 +380,19 @@ smla_attn_bf16_kernel(KParams p) {
     for (int tt = 0; tt < ntiles; tt++) {
       if (tt + 1 < ntiles) wait_vmcnt<PER>(); else wait_vmcnt<0>();
       lds_barrier();
-      if (tt + 2 < ntiles) issue_tile(tt + 2, (tt + 2) % NBUF);
+      const int dma_tt = (tt + 2 < ntiles) ? tt + 2 : -1;
       const lds_char* tb = tiles + (tt % NBUF) * TILE_BYTES;
       const uint32_t vmask = (uint32_t)__ballot((l < 32) ? (s_idx[tt * kTileRows + l] >= 0) : 0);
       float tv[2][4];
-      scores(tb, vmask, tv);
+      scores(tb, vmask, tv, dma_tt);
       float mx[2];
-      half_max(tv, mx);
+      lane_max(tv, mx);
       mx_all[0] = fmaxf(mx_all[0], mx[0]);
       mx_all[1] = fmaxf(mx_all[1], mx[1]);
     }
-    if (lg == 0) {
-      s_m[w * 32 + li] = mx_all[0];
-      s_m[w * 32 + 16 + li] = mx_all[1];
-    }
-    lds_barrier();
-    m_ref[0] = fmaxf(mx_all[0], s_m[(w ^ 2) * 32 + li]);
-    m_ref[1] = fmaxf(mx_all[1], s_m[(w ^ 2) * 32 + 16 + li]);
+    wg_max(mx_all);
+    m_ref[0] = mx_all[0];
+    m_ref[1] = mx_all[1];
     if (threadIdx.x == 0) s_flag = 0;
     lds_barrier();
   }

@@ -58,6 +58,8 @@ int check_attn(const smla_attn_args* a, bool decode) {
   if (a->kv_row_stride_bytes < row_bytes || a->kv_row_stride_bytes % 16 != 0)
     return fail(SMLA_ERR_INVALID_ARG, "kv_row_stride_bytes=%lld must be >= %lld and a multiple of 16",
                 (long long)a->kv_row_stride_bytes, (long long)row_bytes);
+  if (a->kv_row_stride_bytes > (int64_t)UINT32_MAX)
+    return fail(SMLA_ERR_UNSUPPORTED, "kv_row_stride_bytes must be below 2^32");
   if (!aligned16(a->kv_cache)) return fail(SMLA_ERR_INVALID_ARG, "kv_cache must be 16-byte aligned");
   if (!aligned16(a->q_nope) || (a->d_rope && !aligned16(a->q_rope)))
     return fail(SMLA_ERR_INVALID_ARG, "q_nope/q_rope must be 16-byte aligned");

@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace smla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -15,6 +18,16 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef __attribute__((address_space(3))) void lds_void;
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 constexpr int kWave = 64;
 constexpr int kDLatent = 512;
@@ -47,15 +60,16 @@ __device__ __forceinline__ float wave_xor32_max(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 16-byte chunk swizzle of a staged cache tile: row r's chunk c lives at
-// physical chunk c ^ swz(r). swz is the 3-bit reversal of (r >> 1) & 7, so
-// that (a) 16 consecutive rows read at one logical chunk hit 16 distinct
-// 16-byte bank groups and (b) 4 consecutive rows x 4 consecutive chunks
-// (the transposing reads) do too. It only permutes within an aligned group
-// of 8 chunks, so any row of a multiple of 8 chunks stays in place.
-__device__ __forceinline__ int swz(int r) {
-  int a = (r >> 1) & 7;
-  return ((a & 1) << 2) | (a & 2) | ((a >> 2) & 1);
+// Staged cache tile layout (32 rows x NC 16-byte chunks): chunks 2k and 2k+1
+// of all 32 rows form the 1 KB block k; chunk 2k of row r sits at
+// k*1024 + 16r, chunk 2k+1 at k*1024 + 512 + 16((r + 8) mod 32). One
+// 64-lane DMA instruction fills one block with each lane on a fixed row, a
+// read of one chunk by 16 consecutive rows covers 16 distinct 16-byte bank
+// groups, and the transposing V reads (4 rows x 2 chunks per 16 lanes) are
+// conflict-free per 32 lanes.
+__device__ __forceinline__ int tile_pos(int r, int c) {
+  const int odd = c & 1;
+  return (c >> 1) * 1024 + odd * 512 + ((r + 8 * odd) & 31) * 16;
 }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
@@ -65,15 +79,19 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// 16-byte global -> LDS copy (global_load_lds_dwordx4): lane i's 16 bytes land
-// at LDS byte address lds_base + 16*i. Issued from asm so the compiler does
-// not order later LDS reads behind it; completion is tracked by the caller
-// with wait_vmcnt (it counts like any vector load). lds_base must be
-// wave-uniform. The s_nop covers the M0-write -> LDS-DMA hazard.
+// 16-byte global -> LDS copy (global_load_lds_dwordx4): lane i reads 16 bytes
+// at gptr + OFF and they land at LDS byte address lds_base + 16*i. The
+// instruction's immediate offset is applied to the LDS address too, so M0 is
+// set to lds_base - OFF. Issued from asm so the compiler does not order later
+// LDS reads behind it; completion is tracked by the caller with wait_vmcnt
+// (it counts like any vector load). lds_base must be wave-uniform and >= OFF.
+// The s_nop covers the M0-write -> LDS-DMA hazard.
+template <int OFF>
 __device__ __forceinline__ void dma_16b(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  static_assert(OFF >= 0 && OFF < 4096, "immediate offset range");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off offset:%2"
                :
-               : "v"(gptr), "s"(lds_base)
+               : "v"(gptr), "s"(lds_base - (uint32_t)OFF), "i"(OFF)
                : "m0", "memory");
 }
 
