@@ -102,8 +102,9 @@ typedef struct {
 
   float softmax_scale;
 
-  /* Output bf16 [T][h][512]; LSE fp32 [T][h] natural log (NULL = not
-   * wanted). Only the h true heads are written. */
+  /* Output bf16 [T][h][512], 16-byte aligned, strides multiples of 8
+   * elements; LSE fp32 [T][h] natural log (NULL = not wanted). Only the h
+   * true heads are written. */
   void* out;
   int64_t out_stride_tok, out_stride_head;
   float* lse;

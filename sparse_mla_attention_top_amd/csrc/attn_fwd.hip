@@ -49,7 +49,7 @@ struct KParams {
   int64_t out_st, out_sh;
   float* lse;
   int64_t lse_st;
-  float* part_o;
+  uint16_t* part_o;     // bf16 [splits][T][H][512]
   float* part_lse;
 };
 
@@ -198,15 +198,15 @@ smla_attn_bf16_kernel(KParams p) {
   __syncthreads();
   const int ntiles = (s_nrows + kTileRows - 1) / kTileRows;
 
-  // DMA instruction u of wave w fills block 4u + w of the tile (chunks
-  // 2(4u + w) and 2(4u + w) + 1 of all rows); lane l loads row l (l < 32) or
-  // row (l - 40) mod 32 (l >= 32, the odd chunk), the same row for every u, so
-  // one address per tile serves all PER instructions through the immediate
-  // offset 128u.
+  // DMA instruction u of wave w fills block 4u + w of the tile: segment u
+  // (bytes 128u .. 128u+127) of rows 8w .. 8w+7. Lane l loads row 8w + l/8,
+  // logical chunk (l & 7) ^ swz(row) of the segment: the same row and column
+  // for every u, so one address per tile serves all PER copies through the
+  // immediate offset 128u.
   const uint32_t tiles_addr = (uint32_t)(uintptr_t)tiles;
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int drow = l < 32 ? l : ((l - 40) & 31);
-  const uint32_t dcol = (uint32_t)(32 * wu + 16 * (l >> 5));
+  const int drow = 8 * wu + (l >> 3);
+  const uint32_t dcol = (uint32_t)(16 * ((l & 7) ^ swz(drow)));
   const uint32_t kv_stride = (uint32_t)p.kv_row_stride;
   auto dma_src = [&](int tt) -> const uint8_t* {
     const int g = max(s_idx[tt * kTileRows + drow], 0);
@@ -222,34 +222,38 @@ smla_attn_bf16_kernel(KParams p) {
   };
 
   // K reads (A operand of 16x16x32): row 16rh + li, chunk 4ks + lg, at
-  // kbase + 2048 ks.
-  const int kbase = tile_pos(16 * rh + li, lg);
+  // kbase[ks & 1] + 4096 (ks >> 1).
+  int kbase[2];
+#pragma unroll
+  for (int j = 0; j < 2; j++) kbase[j] = tile_pos(16 * rh + li, 4 * j + lg);
   // V transposing reads (B operand of P.V): in 16-lane group lg, lane li = 4e + q
   // reads row 4lg + e (then 16 + 4lg + e), channels 128w + 16nb + 4q .. +3,
-  // at vbase[half] + 1024 nb.
-  int vbase[2];
+  // at vbase[half][nb & 3] + 4096 (nb >> 2).
+  int vbase[2][4];
   {
     const int e = li >> 2, q4 = li & 3;
 #pragma unroll
     for (int half = 0; half < 2; half++)
-      vbase[half] = tile_pos(16 * half + 4 * lg + e, 16 * w + (q4 >> 1)) + 8 * (q4 & 1);
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+        vbase[half][j] = tile_pos(16 * half + 4 * lg + e, 16 * w + 2 * j + (q4 >> 1)) + 8 * (q4 & 1);
   }
 
   // S^T[16 rows x 32 heads] of the wave for tile buffer tb, base-2 units, masked.
   // Lane holds rows 16rh + 4lg + r (r = 0..3) of heads 32hg + 16nbq + li. The
   // DMAs of tile dma_tt (if >= 0) are issued between the k-steps.
   auto scores = [&](const lds_char* tb, uint32_t vmask, float (&tv)[2][4], int dma_tt) {
-    f32x4 s0 = {}, s1 = {};
+    f32x4 s0 = {}, s1 = {}, s2 = {}, s3 = {};  // even / odd k-steps: 4 independent chains
     constexpr int PF = 4;                      // K operand reads kept in flight
     bf16x8 a[PF];
 #pragma unroll
-    for (int ks = 0; ks < PF; ks++) a[ks] = lds_ld128(tb + kbase + 2048 * ks);
+    for (int ks = 0; ks < PF; ks++) a[ks] = lds_ld128(tb + kbase[ks & 1] + 4096 * (ks >> 1));
     const uint8_t* dsrc = dma_tt >= 0 ? dma_src(dma_tt) : p.kv;
     const int db = dma_tt >= 0 ? dma_tt % NBUF : 0;
     static_for<QKS>([&](auto ks_c) {
       constexpr int ks = decltype(ks_c)::value;
       const bf16x8 cur = a[ks % PF];
-      if constexpr (ks + PF < QKS) a[ks % PF] = lds_ld128(tb + kbase + 2048 * (ks + PF));
+      if constexpr (ks + PF < QKS) a[ks % PF] = lds_ld128(tb + kbase[(ks + PF) & 1] + 4096 * ((ks + PF) >> 1));
       if constexpr ((ks & 1) == 0 && (ks >> 1) < PER) {
         if (dma_tt >= 0) issue_one(dsrc, db, std::integral_constant<int, (ks >> 1)>{});
       }
@@ -262,10 +266,17 @@ smla_attn_bf16_kernel(KParams p) {
         b0 = lds_ld128(qrope + (((w * 2 + 0) * (QKS - kLatKS) + (ks - kLatKS)) * 64 + l) * 16);
         b1 = lds_ld128(qrope + (((w * 2 + 1) * (QKS - kLatKS) + (ks - kLatKS)) * 64 + l) * 16);
       }
-      s0 = mfma16x16x32(cur, b0, s0);
-      s1 = mfma16x16x32(cur, b1, s1);
+      if constexpr ((ks & 1) == 0) {
+        s0 = mfma16x16x32(cur, b0, s0);
+        s1 = mfma16x16x32(cur, b1, s1);
+      } else {
+        s2 = mfma16x16x32(cur, b0, s2);
+        s3 = mfma16x16x32(cur, b1, s3);
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
+    s0 += s2;
+    s1 += s3;
     static_assert(2 * PER <= QKS + 1, "DMA issue slots");
 #pragma unroll
     for (int r = 0; r < 4; r++) {
@@ -352,8 +363,8 @@ smla_attn_bf16_kernel(KParams p) {
       s16x4 vr[VPF + 1][2];
 #pragma unroll
       for (int nb = 0; nb < VPF; nb++) {
-        vr[nb][0] = lds_read_tr16(tb + vbase[0] + 1024 * nb);
-        vr[nb][1] = lds_read_tr16(tb + vbase[1] + 1024 * nb);
+        vr[nb][0] = lds_read_tr16(tb + vbase[0][nb & 3] + 4096 * (nb >> 2));
+        vr[nb][1] = lds_read_tr16(tb + vbase[1][nb & 3] + 4096 * (nb >> 2));
       }
 #pragma unroll
       for (int nb = 0; nb < 8; nb++) {
@@ -361,8 +372,8 @@ smla_attn_bf16_kernel(KParams p) {
         const s16x4 v1 = vr[nb % (VPF + 1)][1];
         if (nb + VPF < 8) {
           const int n2 = nb + VPF;
-          vr[n2 % (VPF + 1)][0] = lds_read_tr16(tb + vbase[0] + 1024 * n2);
-          vr[n2 % (VPF + 1)][1] = lds_read_tr16(tb + vbase[1] + 1024 * n2);
+          vr[n2 % (VPF + 1)][0] = lds_read_tr16(tb + vbase[0][n2 & 3] + 4096 * (n2 >> 2));
+          vr[n2 % (VPF + 1)][1] = lds_read_tr16(tb + vbase[1][n2 & 3] + 4096 * (n2 >> 2));
         }
         __builtin_amdgcn_sched_barrier(0);
         const bf16x8 bv = concat_bf16x4(v0, v1);
@@ -428,63 +439,87 @@ smla_attn_bf16_kernel(KParams p) {
     }
   }
   __syncthreads();
-  // O lane layout: m-block mb, n-block nb: heads 16mb + 4lg + r, channel 128w + 16nb + li
+  // Stage the normalised O block [64 heads][512 ch] as bf16 in the (now idle)
+  // tile buffers, then write whole 16-byte chunks. O lane layout: m-block mb,
+  // n-block nb: head 16mb + 4lg + r, channel 128w + 16nb + li. Staged row h,
+  // byte b sits at h*1024 + (b ^ (((h >> 2) & 3) << 5)): the 4 head groups of
+  // one store instruction fall in different banks.
+  lds_char* stage = tiles;
 #pragma unroll
   for (int mb = 0; mb < 4; mb++) {
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const int hl = 16 * mb + 4 * lg + r;
-      const int head = hb + hl;
-      if (head < H) {
-        const float sc = s_inv[hl];
+      const float sc = s_inv[hl];
 #pragma unroll
-        for (int nb = 0; nb < 8; nb++) {
-          const int col = 128 * w + 16 * nb + li;
-          const float o = O[mb][nb][r] * sc;
-          if (p.splits == 1) {
-            p.out[(int64_t)t * p.out_st + (int64_t)head * p.out_sh + col] = f32_to_bf16_rne(o);
-          } else {
-            p.part_o[(((int64_t)split * T + t) * H + head) * kDLatent + col] = o;
-          }
-        }
+      for (int nb = 0; nb < 8; nb++) {
+        const int col = 128 * w + 16 * nb + li;
+        *(__attribute__((address_space(3))) uint16_t*)(stage + hl * 1024 + ((2 * col) ^ (lg << 5))) =
+            f32_to_bf16_rne(O[mb][nb][r] * sc);
       }
+    }
+  }
+  __syncthreads();
+  uint16_t* dst_base;
+  int64_t dst_sh;
+  if (p.splits == 1) {
+    dst_base = p.out + (int64_t)t * p.out_st + (int64_t)hb * p.out_sh;
+    dst_sh = p.out_sh;
+  } else {
+    dst_base = p.part_o + (((int64_t)split * T + t) * H + hb) * kDLatent;
+    dst_sh = kDLatent;
+  }
+  const int hmax = min(64, H - hb);
+#pragma unroll
+  for (int k = 0; k < 16; k++) {
+    const int id = k * 256 + threadIdx.x;
+    const int hl = id >> 6, c16 = id & 63;
+    if (hl < hmax) {
+      const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(stage + hl * 1024 + ((16 * c16) ^ (((hl >> 2) & 3) << 5)));
+      *(u32x4*)(dst_base + (int64_t)hl * dst_sh + 8 * c16) = v;
     }
   }
 }
 
 // Merge split partials by their LSE: lse = ln sum_s exp(lse_s),
-// out = sum_s exp(lse_s - lse) * O_s; (0, -inf) is the identity.
+// out = sum_s exp(lse_s - lse) * O_s; (0, -inf) is the identity. Partials are
+// the normalised O_s in bf16.
 __global__ void __launch_bounds__(256)
-smla_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse, int splits,
+smla_combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse, int splits,
                     int T, int H, uint16_t* __restrict__ out, int64_t out_st, int64_t out_sh,
                     float* __restrict__ lse, int64_t lse_st) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one thread = 4 channels
-  const int64_t total = (int64_t)T * H * (kDLatent / 4);
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one thread = 8 channels
+  const int64_t total = (int64_t)T * H * (kDLatent / 8);
   if (gid >= total) return;
-  const int c4 = (int)(gid % (kDLatent / 4));
-  const int64_t th = gid / (kDLatent / 4);
+  const int c8 = (int)(gid % (kDLatent / 8));
+  const int64_t th = gid / (kDLatent / 8);
   const int head = (int)(th % H);
   const int t = (int)(th / H);
   float m = -INFINITY;
   for (int s = 0; s < splits; s++) m = fmaxf(m, part_lse[((int64_t)s * T + t) * H + head]);
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float tot = 0.0f;
   if (m != -INFINITY) {
     for (int s = 0; s < splits; s++) {
       const float ls = part_lse[((int64_t)s * T + t) * H + head];
       const float wgt = (ls == -INFINITY) ? 0.0f : expf(ls - m);
       tot += wgt;
-      const f32x4 o = *(const f32x4*)(part_o + (((int64_t)s * T + t) * H + head) * kDLatent + 4 * c4);
-      acc += wgt * o;
+      const u32x4 o = *(const u32x4*)(part_o + (((int64_t)s * T + t) * H + head) * kDLatent + 8 * c8);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        acc[2 * i] += wgt * __builtin_bit_cast(float, o[i] << 16);
+        acc[2 * i + 1] += wgt * __builtin_bit_cast(float, o[i] & 0xffff0000u);
+      }
     }
-    acc *= 1.0f / tot;
+    const float inv = 1.0f / tot;
+#pragma unroll
+    for (int i = 0; i < 8; i++) acc[i] *= inv;
   }
-  uint16_t* dst = out + (int64_t)t * out_st + (int64_t)head * out_sh + 4 * c4;
-  const uint32_t lo = f32_to_bf16_rne(acc[0]) | ((uint32_t)f32_to_bf16_rne(acc[1]) << 16);
-  const uint32_t hi = f32_to_bf16_rne(acc[2]) | ((uint32_t)f32_to_bf16_rne(acc[3]) << 16);
-  dst[0] = (uint16_t)lo; dst[1] = (uint16_t)(lo >> 16);
-  dst[2] = (uint16_t)hi; dst[3] = (uint16_t)(hi >> 16);
-  if (c4 == 0 && lse) lse[(int64_t)t * lse_st + head] = (m == -INFINITY) ? -INFINITY : m + logf(tot);
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; i++) r[i] = f32_to_bf16_rne(acc[2 * i]) | ((uint32_t)f32_to_bf16_rne(acc[2 * i + 1]) << 16);
+  *(u32x4*)(out + (int64_t)t * out_st + (int64_t)head * out_sh + 8 * c8) = r;
+  if (c8 == 0 && lse) lse[(int64_t)t * lse_st + head] = (m == -INFINITY) ? -INFINITY : m + logf(tot);
 }
 
 int32_t plan_splits(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t requested) {
@@ -508,7 +543,7 @@ size_t workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t topk, int3
   (void)topk;
   if (splits <= 1) return 0;
   const size_t n = (size_t)splits * num_tokens * num_heads;
-  return n * kDLatent * sizeof(float) + n * sizeof(float);
+  return n * kDLatent * sizeof(uint16_t) + n * sizeof(float);
 }
 
 template <int D>
@@ -538,8 +573,8 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
   kp.part_o = nullptr; kp.part_lse = nullptr;
   if (splits > 1) {
     const size_t n = (size_t)splits * a.num_tokens * a.num_heads;
-    kp.part_o = (float*)workspace;
-    kp.part_lse = (float*)((char*)workspace + n * kDLatent * sizeof(float));
+    kp.part_o = (uint16_t*)workspace;
+    kp.part_lse = (float*)((char*)workspace + n * kDLatent * sizeof(uint16_t));
   }
   const int grid = kp.head_blocks == 2 ? ((kp.num_items + 7) / 8) * 16 : kp.num_items;
   if (a.kv_format != 0) return hipErrorInvalidValue;
@@ -551,7 +586,7 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && a.ev_end) e = hipEventRecord(a.ev_end, stream);
   if (e != hipSuccess || splits == 1) return e;
-  const int64_t total = (int64_t)a.num_tokens * a.num_heads * (kDLatent / 4);
+  const int64_t total = (int64_t)a.num_tokens * a.num_heads * (kDLatent / 8);
   smla_combine_kernel<<<(int)((total + 255) / 256), 256, 0, stream>>>(
       kp.part_o, kp.part_lse, splits, a.num_tokens, a.num_heads, a.out, a.out_st, a.out_sh, a.lse, a.lse_st);
   return hipGetLastError();

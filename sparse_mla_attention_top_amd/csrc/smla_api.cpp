@@ -69,6 +69,8 @@ int check_attn(const smla_attn_args* a, bool decode) {
   if (a->indices_stride < a->topk) return fail(SMLA_ERR_INVALID_ARG, "indices_stride < topk");
   if (a->out_stride_head < 512 && a->num_heads > 1)
     return fail(SMLA_ERR_INVALID_ARG, "out_stride_head < 512");
+  if (!aligned16(a->out) || a->out_stride_tok % 8 || a->out_stride_head % 8)
+    return fail(SMLA_ERR_INVALID_ARG, "out must be 16-byte aligned with strides that are multiples of 8 elements");
   if (a->lse && a->lse_stride_tok < a->num_heads) return fail(SMLA_ERR_INVALID_ARG, "lse_stride_tok < num_heads");
   if (a->kv_format == SMLA_KV_FP8_E4M3_GROUP128 && !a->group_scales)
     return fail(SMLA_ERR_INVALID_ARG, "group_scales is NULL for the group-scaled FP8 format");

@@ -60,16 +60,21 @@ __device__ __forceinline__ float wave_xor32_max(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Staged cache tile layout (32 rows x NC 16-byte chunks): chunks 2k and 2k+1
-// of all 32 rows form the 1 KB block k; chunk 2k of row r sits at
-// k*1024 + 16r, chunk 2k+1 at k*1024 + 512 + 16((r + 8) mod 32). One
-// 64-lane DMA instruction fills one block with each lane on a fixed row, a
-// read of one chunk by 16 consecutive rows covers 16 distinct 16-byte bank
-// groups, and the transposing V reads (4 rows x 2 chunks per 16 lanes) are
-// conflict-free per 32 lanes.
+// 3-bit swizzle of a tile row: reversal of the bits of (r >> 1) & 7.
+__device__ __forceinline__ int swz(int r) {
+  const int a = (r >> 1) & 7;
+  return ((a & 1) << 2) | (a & 2) | ((a >> 2) & 1);
+}
+
+// Staged cache tile layout (32 rows x NC 16-byte chunks, NC = 8 x segments of
+// 128 bytes). Block 4s + g (1 KB) holds segment s of rows 8g..8g+7; inside
+// it row r's chunk 8s + cc sits at ((r & 7) * 8 + (cc ^ swz(r))) * 16. So a
+// 64-lane global->LDS copy fills one block from 8 whole 128-byte lines (lane
+// l: row 8g + l/8), a read of one chunk by 16 consecutive rows hits 16
+// distinct 16-byte bank groups, and the transposing V reads (4 rows x 2
+// chunks per 16 lanes) are conflict-free per 32 lanes.
 __device__ __forceinline__ int tile_pos(int r, int c) {
-  const int odd = c & 1;
-  return (c >> 1) * 1024 + odd * 512 + ((r + 8 * odd) & 31) * 16;
+  return (4 * (c >> 3) + (r >> 3)) * 1024 + ((r & 7) * 8 + ((c & 7) ^ swz(r))) * 16;
 }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS

@@ -88,5 +88,5 @@ def test_split_plan_is_shape_only():
     assert smla.decode_num_splits(4096, 128, 2048) == 1
     assert smla.decode_num_splits(1, 128, 64) == 1
     assert smla.decode_num_splits(32, 128, 2048, 3) == 3
-    assert smla.decode_workspace_size(32, 128, 2048) == 8 * 32 * 128 * (512 + 1) * 4
+    assert smla.decode_workspace_size(32, 128, 2048) == 8 * 32 * 128 * (512 * 2 + 4)
     assert smla.decode_workspace_size(4096, 128, 2048) == 0
