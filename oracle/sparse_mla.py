@@ -137,18 +137,24 @@ def valid_entries(idx_row: np.ndarray, length: Optional[int], num_slots: int) ->
     return row[(row >= 0) & (row < num_slots)]
 
 
-def attention_rows(q_t: np.ndarray, rows: np.ndarray, scale: float, d_v: int = D_V):
+def attention_rows(q_t: np.ndarray, rows: np.ndarray, scale: float, d_v: int = D_V,
+                   magnitude: bool = False):
     """One query token: q_t [h, D] and its gathered rows [v, D] (fp64).
-    Returns out [h, d_v], lse [h]."""
+    Returns out [h, d_v], lse [h]; with ``magnitude`` also
+    mag [h, d_v] = sum_j p_j |v_j|, the size against which rounding of the
+    terms p_j v_j of the output is measured (0 for an empty row)."""
     h = q_t.shape[0]
     if rows.shape[0] == 0:
-        return np.zeros((h, d_v)), np.full(h, -np.inf)
+        empty = (np.zeros((h, d_v)), np.full(h, -np.inf))
+        return empty + (np.zeros((h, d_v)),) if magnitude else empty
     s = scale * (q_t @ rows.T)                      # [h, v]
     m = s.max(axis=1, keepdims=True)
     p = np.exp(s - m)
     l = p.sum(axis=1, keepdims=True)
     out = (p @ rows[:, :d_v]) / l
     lse = (m + np.log(l))[:, 0]
+    if magnitude:
+        return out, lse, (p @ np.abs(rows[:, :d_v])) / l
     return out, lse
 
 
@@ -161,20 +167,39 @@ def attention(q: np.ndarray, cache: np.ndarray, kv_format: int, indices: np.ndar
     q: [T, h, D] float64 (already the bf16 values); cache: flat [S, D] in the
     storage format; indices: [T, K] global slots. Only the listed ``tokens``
     (default all) are computed. Returns out [n, h, d_v], lse [n, h] fp64."""
+    res = _attention(q, cache, kv_format, indices, softmax_scale, topk_length, k_scale, group_scales,
+                     tokens, d_v, False)
+    return res[0], res[1]
+
+
+def attention_with_magnitude(q: np.ndarray, cache: np.ndarray, kv_format: int, indices: np.ndarray,
+                             softmax_scale: float, topk_length: Optional[np.ndarray] = None,
+                             k_scale: float = 1.0, group_scales: Optional[np.ndarray] = None,
+                             tokens: Optional[np.ndarray] = None, d_v: int = D_V):
+    """``attention`` plus mag [n, h, d_v] = sum_j p_j |v_j| per output element
+    (the softmax-weighted sum of the magnitudes of the value rows)."""
+    return _attention(q, cache, kv_format, indices, softmax_scale, topk_length, k_scale, group_scales,
+                      tokens, d_v, True)
+
+
+def _attention(q, cache, kv_format, indices, softmax_scale, topk_length, k_scale, group_scales,
+               tokens, d_v, magnitude):
     tokens = np.arange(q.shape[0]) if tokens is None else np.asarray(tokens)
     S = cache.shape[0]
-    outs, lses = [], []
+    outs, lses, mags = [], [], []
     for t in tokens:
         length = None if topk_length is None else int(topk_length[t])
         sel = valid_entries(indices[t], length, S)
         rows = dequantize_rows(cache, kv_format, sel, k_scale, group_scales)
-        o, l = attention_rows(q[t], rows, softmax_scale, d_v)
-        outs.append(o)
-        lses.append(l)
+        r = attention_rows(q[t], rows, softmax_scale, d_v, magnitude)
+        outs.append(r[0])
+        lses.append(r[1])
+        if magnitude:
+            mags.append(r[2])
     h = q.shape[1]
     if not outs:
-        return np.zeros((0, h, d_v)), np.zeros((0, h))
-    return np.stack(outs), np.stack(lses)
+        return np.zeros((0, h, d_v)), np.zeros((0, h)), np.zeros((0, h, d_v))
+    return np.stack(outs), np.stack(lses), (np.stack(mags) if magnitude else None)
 
 
 def merge_partials(outs: np.ndarray, lses: np.ndarray):

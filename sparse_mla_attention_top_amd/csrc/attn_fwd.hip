@@ -35,6 +35,7 @@ struct KParams {
   int64_t qr_st, qr_sh;
   const uint8_t* kv;
   int64_t kv_row_stride, num_slots;
+  const float* group_scales;   // [num_slots][ceil(D/128)] (group-scaled FP8 only)
   const int32_t* indices;
   int64_t idx_stride;
   int32_t topk;
@@ -80,23 +81,52 @@ constexpr int kLatKS = kDLatent / 32;   // k-steps over the 512 latent channels
 
 template <int D>
 struct TileShape {
-  static constexpr int RB = 2 * D;                    // bytes of one staged row
-  static constexpr int NC = D / 8;                    // 16-byte chunks per row
+  static constexpr int RB = 2 * D;                    // bytes of one staged bf16 row
+  static constexpr int NC = D / 8;                    // 16-byte bf16 chunks per row
   static constexpr int QKS = D / 32;                  // k-steps of the QK contraction
   static constexpr int TILE_BYTES = kTileRows * RB;
-  static constexpr int NBUF = 3;
-  static constexpr int PER = NC * kTileRows / 256;    // DMA instructions per wave per tile
+  static constexpr int PER = NC * kTileRows / 256;    // bf16 cache: DMA instructions per wave per tile
   static_assert(PER * 256 == NC * kTileRows, "tile must split evenly over 4 waves");
 };
 
-template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-smla_attn_bf16_kernel(KParams p) {
-  using TS = TileShape<D>;
-  constexpr int RB = TS::RB, NC = TS::NC, QKS = TS::QKS, TILE_BYTES = TS::TILE_BYTES;
-  constexpr int NBUF = TS::NBUF, PER = TS::PER;
+// FP8 staging of one 32-row tile, as copied from HBM (E4M3 bytes). Wave w
+// copies and later converts its own rows 8w .. 8w+7:
+//   latent : segment u (bytes 128u .. 128u+127 of the row, u < 4) of the 8
+//            rows in block 4u + w (1 KB, lane l = 8 (row & 7) + chunk);
+//   rope   : (D = 576) bytes 512 .. 575 of the 8 rows, 512 B per wave
+//            (lane l < 32 = 4 (row & 7) + chunk);
+//   scales : (group format) the G = ceil(D/128) fp32 group scales of the 8
+//            rows, 8G dwords per wave (lane l < 8G = G (row & 7) + group).
+template <int D, int FMT>
+struct Stage8 {
+  static constexpr bool ROPE = D > kDLatent;
+  static constexpr bool GROUP = FMT == 2;
+  static constexpr int G = (D + 127) / 128;
+  static constexpr int ROPE_OFF = 16 * 1024;
+  static constexpr int SC_OFF = ROPE_OFF + (ROPE ? 4 * 512 : 0);
+  static constexpr int BYTES = SC_OFF + (GROUP ? 4 * 256 : 0);
+  static constexpr int PERW = 4 + (ROPE ? 1 : 0) + (GROUP ? 1 : 0);  // DMA instructions per wave per tile
+  static constexpr int NBUF = 3;
+  static_assert(D == kDLatent || D == kDLatent + 64, "rope part must be 64 channels");
+  static_assert(8 * G <= 64, "scales of 8 rows fit one instruction");
+};
 
-  __shared__ __attribute__((aligned(16))) char s_tiles[NBUF * TILE_BYTES];
+// FMT: 0 = bf16 cache, 1 = E4M3 with one per-tensor scale, 2 = E4M3 with
+// per-row x 128-channel-group scales.
+template <int D, int FMT>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+smla_attn_kernel(KParams p) {
+  using TS = TileShape<D>;
+  using S8 = Stage8<D, FMT>;
+  constexpr bool F8 = FMT != 0;
+  constexpr int NC = TS::NC, QKS = TS::QKS, TILE_BYTES = TS::TILE_BYTES, PER = TS::PER;
+  constexpr int NBT = F8 ? 2 : 3;                      // bf16 tile buffers
+  constexpr int NDMA = F8 ? S8::PERW : PER;            // DMA instructions per wave per tile
+  static_assert(NBT * TILE_BYTES >= 64 * 1024, "the epilogue stages a 64 x 512 bf16 block in the tiles");
+  (void)NC;
+
+  __shared__ __attribute__((aligned(16))) char s_tiles[NBT * TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char s_stage[F8 ? S8::NBUF * S8::BYTES : 16];
   __shared__ __attribute__((aligned(16))) char s_p[4 * 64 * 16];    // P as A operands [mblock][lane]
   __shared__ int s_idx[kMaxTopk];
   __shared__ float s_m[4 * 32];
@@ -105,9 +135,13 @@ smla_attn_bf16_kernel(KParams p) {
   __shared__ int s_flag;
   __shared__ int s_nrows;
   __shared__ __attribute__((aligned(16))) char s_qrope[(QKS > kLatKS ? 4 * 2 * (QKS - kLatKS) : 1) * 64 * 16];
+  // group format: row scales of the two bf16 tile buffers, [buffer][group][row]
+  __shared__ __attribute__((aligned(16))) float s_rsc[S8::GROUP ? 2 * S8::G * kTileRows : 4];
   lds_char* qrope = (lds_char*)s_qrope;
 
   lds_char* tiles = (lds_char*)s_tiles;
+  lds_char* stage = (lds_char*)s_stage;
+  lds_char* rsc = (lds_char*)s_rsc;
   lds_char* pbuf = (lds_char*)s_p;
 
   const int w = threadIdx.x >> 6;
@@ -198,27 +232,106 @@ smla_attn_bf16_kernel(KParams p) {
   __syncthreads();
   const int ntiles = (s_nrows + kTileRows - 1) / kTileRows;
 
-  // DMA instruction u of wave w fills block 4u + w of the tile: segment u
-  // (bytes 128u .. 128u+127) of rows 8w .. 8w+7. Lane l loads row 8w + l/8,
-  // logical chunk (l & 7) ^ swz(row) of the segment: the same row and column
-  // for every u, so one address per tile serves all PER copies through the
-  // immediate offset 128u.
-  const uint32_t tiles_addr = (uint32_t)(uintptr_t)tiles;
   const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t kv_stride = (uint32_t)p.kv_row_stride;
+
+  // bf16 cache. DMA instruction u of wave w fills block 4u + w of the tile:
+  // segment u (bytes 128u .. 128u+127) of rows 8w .. 8w+7. Lane l loads row
+  // 8w + l/8, logical chunk (l & 7) ^ swz(row) of the segment: the same row
+  // and column for every u, so one address per tile serves all PER copies
+  // through the immediate offset 128u.
+  const uint32_t tiles_addr = (uint32_t)(uintptr_t)tiles;
   const int drow = 8 * wu + (l >> 3);
   const uint32_t dcol = (uint32_t)(16 * ((l & 7) ^ swz(drow)));
-  const uint32_t kv_stride = (uint32_t)p.kv_row_stride;
-  auto dma_src = [&](int tt) -> const uint8_t* {
-    const int g = max(s_idx[tt * kTileRows + drow], 0);
-    return p.kv + ((uint64_t)(uint32_t)g * kv_stride + dcol);
+
+  // FP8 cache: per-tile sources of this lane (latent chunk l & 7 of row
+  // 8w + l/8; rope chunk l & 3 of row 8w + l/4; scale l % G of row 8w + l/G).
+  const uint32_t stage_addr = (uint32_t)(uintptr_t)stage;
+  const int srow = min(l / S8::G, 7), sgrp = l % S8::G;
+  struct Src {
+    const uint8_t* lat;
+    const uint8_t* rope;
+    const float* sc;
   };
-  auto issue_one = [&](const uint8_t* src, int b, auto u_c) {
+  auto sources = [&](int tt) -> Src {
+    Src s;
+    const int base = tt * kTileRows + 8 * wu;
+    if constexpr (!F8) {
+      s.lat = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + (l >> 3)], 0) * kv_stride + dcol);
+    } else {
+      s.lat = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + (l >> 3)], 0) * kv_stride + 16 * (l & 7));
+      if constexpr (S8::ROPE)
+        s.rope = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + ((l >> 2) & 7)], 0) * kv_stride + kDLatent + 16 * (l & 3));
+      if constexpr (S8::GROUP)
+        s.sc = p.group_scales + ((uint64_t)(uint32_t)max(s_idx[base + srow], 0) * S8::G + sgrp);
+    }
+    return s;
+  };
+  // DMA instruction u (0 .. NDMA-1) of tile buffer b
+  auto issue_one = [&](const Src& s, int b, auto u_c) {
     constexpr int u = decltype(u_c)::value;
-    dma_16b<128 * u>(src, __builtin_amdgcn_readfirstlane(tiles_addr + b * TILE_BYTES + (4 * u + wu) * 1024));
+    if constexpr (!F8) {
+      dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(tiles_addr + b * TILE_BYTES + (4 * u + wu) * 1024));
+    } else {
+      const uint32_t sb = stage_addr + b * S8::BYTES;
+      if constexpr (u < 4) {
+        dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(sb + (4 * u + wu) * 1024));
+      } else if constexpr (u == 4 && S8::ROPE) {
+        if (l < 32) dma_16b<0>(s.rope, __builtin_amdgcn_readfirstlane(sb + S8::ROPE_OFF + wu * 512));
+      } else {
+        if (l < 8 * S8::G) dma_4b(s.sc, __builtin_amdgcn_readfirstlane(sb + S8::SC_OFF + wu * 256));
+      }
+    }
   };
-  auto issue_tile = [&](int tt, int b) {
-    const uint8_t* src = dma_src(tt);
-    static_for<PER>([&](auto u_c) { issue_one(src, b, u_c); });
+  constexpr int NBUF_DMA = 3;                // buffers the DMAs rotate over (bf16 tiles or FP8 stages)
+  auto issue_tile = [&](int tt) {
+    const Src s = sources(tt);
+    static_for<NDMA>([&](auto u_c) { issue_one(s, tt % NBUF_DMA, u_c); });
+  };
+  // wait until at most n (0..2) tiles' DMAs of this wave are outstanding
+  auto wait_tiles = [&](int n) {
+    if (n >= 2) wait_vmcnt<2 * NDMA>();
+    else if (n == 1) wait_vmcnt<NDMA>();
+    else wait_vmcnt<0>();
+  };
+  // FP8: this wave's rows of staged tile tt -> bf16 tile buffer tt & 1. The
+  // tile holds the E4M3 values themselves (exact in bf16); in the group
+  // format the row scales go to s_rsc[tt & 1] and are applied to the QK
+  // partial sums and to P (see scores and P.V).
+  auto convert_tile = [&](int tt) {
+    if constexpr (F8) {
+      const lds_char* st = stage + (tt % S8::NBUF) * S8::BYTES;
+      lds_char* tb = tiles + (tt & 1) * TILE_BYTES;
+      const int r = 8 * w + (l >> 3);
+      static_for<4>([&](auto u_c) {
+        constexpr int u = decltype(u_c)::value;
+        const u32x4 raw = *(const __attribute__((address_space(3))) u32x4*)(st + (4 * u + w) * 1024 + 16 * l);
+        if constexpr (S8::GROUP) {
+          const float sc = *(const __attribute__((address_space(3))) float*)(st + S8::SC_OFF + w * 256 + 4 * ((l >> 3) * S8::G + u));
+          *(__attribute__((address_space(3))) float*)(rsc + 4 * (((tt & 1) * S8::G + u) * kTileRows + r)) = sc;
+        }
+        u32x4 lo, hi;
+        e4m3x16_to_bf16<false>(raw, 1.0f, lo, hi);
+        const int k = 8 * u + (l & 7);
+        *(__attribute__((address_space(3))) u32x4*)(tb + tile_pos(r, 2 * k)) = lo;
+        *(__attribute__((address_space(3))) u32x4*)(tb + tile_pos(r, 2 * k + 1)) = hi;
+      });
+      if constexpr (S8::ROPE) {
+        if (l < 32) {
+          const int r2 = 8 * w + (l >> 2);
+          const u32x4 raw = *(const __attribute__((address_space(3))) u32x4*)(st + S8::ROPE_OFF + w * 512 + 16 * l);
+          if constexpr (S8::GROUP) {
+            const float sc = *(const __attribute__((address_space(3))) float*)(st + S8::SC_OFF + w * 256 + 4 * ((l >> 2) * S8::G + 4));
+            *(__attribute__((address_space(3))) float*)(rsc + 4 * (((tt & 1) * S8::G + 4) * kTileRows + r2)) = sc;
+          }
+          u32x4 lo, hi;
+          e4m3x16_to_bf16<false>(raw, 1.0f, lo, hi);
+          const int k = 32 + (l & 3);
+          *(__attribute__((address_space(3))) u32x4*)(tb + tile_pos(r2, 2 * k)) = lo;
+          *(__attribute__((address_space(3))) u32x4*)(tb + tile_pos(r2, 2 * k + 1)) = hi;
+        }
+      }
+    }
   };
 
   // K reads (A operand of 16x16x32): row 16rh + li, chunk 4ks + lg, at
@@ -242,20 +355,33 @@ smla_attn_bf16_kernel(KParams p) {
   // S^T[16 rows x 32 heads] of the wave for tile buffer tb, base-2 units, masked.
   // Lane holds rows 16rh + 4lg + r (r = 0..3) of heads 32hg + 16nbq + li. The
   // DMAs of tile dma_tt (if >= 0) are issued between the k-steps.
-  auto scores = [&](const lds_char* tb, uint32_t vmask, float (&tv)[2][4], int dma_tt) {
+  // Group format: the k-steps of channel group g = ks / 4 accumulate apart;
+  // each group's partial sums are scaled by the rows' group scales and added
+  // into t0 / t1 two k-steps into the next group (when its MFMAs are done).
+  auto scores = [&](const lds_char* tb, uint32_t vmask, float (&tv)[2][4], int dma_tt, int rbuf) {
     f32x4 s0 = {}, s1 = {}, s2 = {}, s3 = {};  // even / odd k-steps: 4 independent chains
+    f32x4 t0 = {}, t1 = {}, o0 = {}, o1 = {}, o2 = {}, o3 = {}, osc = {};
+    const lds_char* rs = rsc + 4 * (rbuf * S8::G * kTileRows + 16 * rh + 4 * lg);
+    (void)rs;
     constexpr int PF = 4;                      // K operand reads kept in flight
     bf16x8 a[PF];
 #pragma unroll
     for (int ks = 0; ks < PF; ks++) a[ks] = lds_ld128(tb + kbase[ks & 1] + 4096 * (ks >> 1));
-    const uint8_t* dsrc = dma_tt >= 0 ? dma_src(dma_tt) : p.kv;
-    const int db = dma_tt >= 0 ? dma_tt % NBUF : 0;
+    Src dsrc;
+    if (dma_tt >= 0) dsrc = sources(dma_tt);
+    const int db = dma_tt >= 0 ? dma_tt % NBUF_DMA : 0;
     static_for<QKS>([&](auto ks_c) {
       constexpr int ks = decltype(ks_c)::value;
       const bf16x8 cur = a[ks % PF];
       if constexpr (ks + PF < QKS) a[ks % PF] = lds_ld128(tb + kbase[(ks + PF) & 1] + 4096 * ((ks + PF) >> 1));
-      if constexpr ((ks & 1) == 0 && (ks >> 1) < PER) {
+      if constexpr ((ks & 1) == 0 && (ks >> 1) < NDMA) {
         if (dma_tt >= 0) issue_one(dsrc, db, std::integral_constant<int, (ks >> 1)>{});
+      }
+      if constexpr (S8::GROUP && F8 && (ks & 3) == 0 && ks > 0) {
+        // group ks/4 - 1 is complete: keep its chains and their scales, start afresh
+        o0 = s0; o1 = s1; o2 = s2; o3 = s3;
+        s0 = (f32x4){}; s1 = (f32x4){}; s2 = (f32x4){}; s3 = (f32x4){};
+        osc = *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * (ks / 4 - 1));
       }
       __builtin_amdgcn_sched_barrier(0);       // keep the read-ahead ahead of the MFMAs
       bf16x8 b0, b1;
@@ -273,11 +399,26 @@ smla_attn_bf16_kernel(KParams p) {
         s2 = mfma16x16x32(cur, b0, s2);
         s3 = mfma16x16x32(cur, b1, s3);
       }
+      if constexpr (S8::GROUP && F8 && (ks & 3) == 2 && ks > 4) {
+        t0 += osc * (o0 + o2);
+        t1 += osc * (o1 + o3);
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
-    s0 += s2;
-    s1 += s3;
-    static_assert(2 * PER <= QKS + 1, "DMA issue slots");
+    if constexpr (S8::GROUP && F8) {
+      constexpr int gl = (QKS - 1) / 4;                // last group
+      if constexpr ((QKS - 1) % 4 < 2 && gl > 0) {     // the group before it was not folded yet
+        t0 += osc * (o0 + o2);
+        t1 += osc * (o1 + o3);
+      }
+      const f32x4 lsc = *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * gl);
+      s0 = t0 + lsc * (s0 + s2);
+      s1 = t1 + lsc * (s1 + s3);
+    } else {
+      s0 += s2;
+      s1 += s3;
+    }
+    static_assert(2 * NDMA <= QKS + 1, "DMA issue slots");
 #pragma unroll
     for (int r = 0; r < 4; r++) {
       const bool ok = (vmask >> (16 * rh + 4 * lg + r)) & 1;
@@ -314,25 +455,48 @@ smla_attn_bf16_kernel(KParams p) {
   f32x4 O[4][8];
   bool have_ref = false;      // workgroup-uniform: a reference has been fixed
 
-  for (int attempt = 0; attempt < 2; attempt++) {
-#pragma unroll
-    for (int mb = 0; mb < 4; mb++)
-#pragma unroll
-      for (int nb = 0; nb < 8; nb++) O[mb][nb] = (f32x4){};
-    l_lane[0] = l_lane[1] = 0.0f;
-    if (ntiles > 0) issue_tile(0, 0);
-    if (ntiles > 1) issue_tile(1, 1);
+  // Tile pipeline. bf16 cache: tiles are copied straight into the bf16 tile
+  // buffers, two ahead. FP8 cache: tiles are copied into the FP8 stages three
+  // ahead; tile tt+1 is converted into the free bf16 buffer while tile tt is
+  // being consumed, by the wave that copied it (so only that wave's copy
+  // needs to have landed). full = softmax and P.V; otherwise only the
+  // per-head maximum of the pass is taken (into mx_all).
+  auto run_pass = [&](const bool full, float (&mx_all)[2]) {
+    if constexpr (!F8) {
+      if (ntiles > 0) issue_tile(0);
+      if (ntiles > 1) issue_tile(1);
+    } else {
+      if (ntiles > 0) issue_tile(0);
+      if (ntiles > 1) issue_tile(1);
+      if (ntiles > 2) issue_tile(2);
+      if (ntiles > 0) {
+        wait_tiles(min(ntiles - 1, 2));
+        convert_tile(0);
+      }
+    }
     for (int tt = 0; tt < ntiles; tt++) {
-      if (tt + 1 < ntiles) wait_vmcnt<PER>(); else wait_vmcnt<0>();
+      if constexpr (!F8) {
+        if (tt + 1 < ntiles) wait_vmcnt<PER>(); else wait_vmcnt<0>();
+      }
       lds_barrier();
-      const int dma_tt = (tt + 2 < ntiles) ? tt + 2 : -1;
-      const lds_char* tb = tiles + (tt % NBUF) * TILE_BYTES;
+      const int ahead = F8 ? 3 : 2;
+      const int dma_tt = (tt + ahead < ntiles) ? tt + ahead : -1;
+      const lds_char* tb = tiles + (F8 ? (tt & 1) : (tt % NBT)) * TILE_BYTES;
       const uint32_t vmask = (uint32_t)__ballot((l < 32) ? (s_idx[tt * kTileRows + l] >= 0) : 0);
 
       float tv[2][4];
-      scores(tb, vmask, tv, dma_tt);
+      scores(tb, vmask, tv, dma_tt, tt & 1);
       float mx[2];
       lane_max(tv, mx);
+      if (!full) {
+        mx_all[0] = fmaxf(mx_all[0], mx[0]);
+        mx_all[1] = fmaxf(mx_all[1], mx[1]);
+        if (F8 && tt + 1 < ntiles) {
+          wait_tiles(min(ntiles - tt - 2, 2));
+          convert_tile(tt + 1);
+        }
+        continue;
+      }
       if (!have_ref) {                                     // uniform: first tile with a valid row
         wg_max(mx);
         m_ref[0] = mx[0];
@@ -353,10 +517,23 @@ smla_attn_bf16_kernel(KParams p) {
         lds_st64(pbuf + ((2 * hg + nbq) * 64 + l) * 16 + 8 * rh, pk[nbq]);
       }
       lds_barrier();
+      if (F8 && tt + 1 < ntiles) {
+        wait_tiles(min(ntiles - tt - 2, 2));
+        convert_tile(tt + 1);
+      }
 
       bf16x8 pa[4];
 #pragma unroll
       for (int mb = 0; mb < 4; mb++) pa[mb] = lds_ld128(pbuf + (mb * 64 + l) * 16);
+      if constexpr (S8::GROUP && F8) {
+        // wave w's channels are group w: P[h][j] * scale[j][w] (elements 0..3 of
+        // the operand are rows 4lg .. 4lg+3, elements 4..7 rows 16+4lg .. 16+4lg+3)
+        const lds_char* rw = rsc + 4 * (((tt & 1) * S8::G + w) * kTileRows + 4 * lg);
+        const f32x4 sa = *(const __attribute__((address_space(3))) f32x4*)rw;
+        const f32x4 sb = *(const __attribute__((address_space(3))) f32x4*)(rw + 64);
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) pa[mb] = scale_bf16x8(pa[mb], sa, sb);
+      }
 
       // O[64 heads x 128 ch] += P[64 x 32] . V[32 x 128]; V reads run two n-blocks ahead
       constexpr int VPF = 2;
@@ -382,25 +559,21 @@ smla_attn_bf16_kernel(KParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+
+  for (int attempt = 0; attempt < 2; attempt++) {
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++)
+#pragma unroll
+      for (int nb = 0; nb < 8; nb++) O[mb][nb] = (f32x4){};
+    l_lane[0] = l_lane[1] = 0.0f;
+    float unused[2] = {-INFINITY, -INFINITY};
+    run_pass(true, unused);
     lds_barrier();
     if (!s_flag) break;                                    // uniform
     // exact per-head maximum, then the full pass again
     float mx_all[2] = {-INFINITY, -INFINITY};
-    if (ntiles > 0) issue_tile(0, 0);
-    if (ntiles > 1) issue_tile(1, 1);
-    for (int tt = 0; tt < ntiles; tt++) {
-      if (tt + 1 < ntiles) wait_vmcnt<PER>(); else wait_vmcnt<0>();
-      lds_barrier();
-      const int dma_tt = (tt + 2 < ntiles) ? tt + 2 : -1;
-      const lds_char* tb = tiles + (tt % NBUF) * TILE_BYTES;
-      const uint32_t vmask = (uint32_t)__ballot((l < 32) ? (s_idx[tt * kTileRows + l] >= 0) : 0);
-      float tv[2][4];
-      scores(tb, vmask, tv, dma_tt);
-      float mx[2];
-      lane_max(tv, mx);
-      mx_all[0] = fmaxf(mx_all[0], mx[0]);
-      mx_all[1] = fmaxf(mx_all[1], mx[1]);
-    }
+    run_pass(false, mx_all);
     wg_max(mx_all);
     m_ref[0] = mx_all[0];
     m_ref[1] = mx_all[1];
@@ -444,7 +617,7 @@ smla_attn_bf16_kernel(KParams p) {
   // n-block nb: head 16mb + 4lg + r, channel 128w + 16nb + li. Staged row h,
   // byte b sits at h*1024 + (b ^ (((h >> 2) & 3) << 5)): the 4 head groups of
   // one store instruction fall in different banks.
-  lds_char* stage = tiles;
+  lds_char* ostage = tiles;
 #pragma unroll
   for (int mb = 0; mb < 4; mb++) {
 #pragma unroll
@@ -454,7 +627,7 @@ smla_attn_bf16_kernel(KParams p) {
 #pragma unroll
       for (int nb = 0; nb < 8; nb++) {
         const int col = 128 * w + 16 * nb + li;
-        *(__attribute__((address_space(3))) uint16_t*)(stage + hl * 1024 + ((2 * col) ^ (lg << 5))) =
+        *(__attribute__((address_space(3))) uint16_t*)(ostage + hl * 1024 + ((2 * col) ^ (lg << 5))) =
             f32_to_bf16_rne(O[mb][nb][r] * sc);
       }
     }
@@ -475,7 +648,7 @@ smla_attn_bf16_kernel(KParams p) {
     const int id = k * 256 + threadIdx.x;
     const int hl = id >> 6, c16 = id & 63;
     if (hl < hmax) {
-      const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(stage + hl * 1024 + ((16 * c16) ^ (((hl >> 2) & 3) << 5)));
+      const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(ostage + hl * 1024 + ((16 * c16) ^ (((hl >> 2) & 3) << 5)));
       *(u32x4*)(dst_base + (int64_t)hl * dst_sh + 8 * c16) = v;
     }
   }
@@ -546,9 +719,9 @@ size_t workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t topk, int3
   return n * kDLatent * sizeof(uint16_t) + n * sizeof(float);
 }
 
-template <int D>
+template <int D, int FMT>
 static void launch_kernel(const KParams& kp, int grid, hipStream_t stream) {
-  smla_attn_bf16_kernel<D><<<grid, 256, 0, stream>>>(kp);
+  smla_attn_kernel<D, FMT><<<grid, 256, 0, stream>>>(kp);
 }
 
 hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, bool longest_first,
@@ -558,11 +731,17 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
   kp.q_nope = a.q_nope; kp.qn_st = a.qn_st; kp.qn_sh = a.qn_sh;
   kp.q_rope = a.d_rope ? a.q_rope : a.q_nope; kp.qr_st = a.qr_st; kp.qr_sh = a.qr_sh;
   kp.kv = a.kv; kp.kv_row_stride = a.kv_row_stride; kp.num_slots = a.num_slots;
+  kp.group_scales = a.group_scales;
   kp.indices = a.indices; kp.idx_stride = a.idx_stride; kp.topk = a.topk;
   kp.topk_length = a.topk_length;
   kp.num_tokens = a.num_tokens; kp.num_heads = a.num_heads;
   kp.scale_log2 = a.softmax_scale * 1.4426950408889634f;
   kp.out_mult = 1.0f;
+  if (a.kv_format == 1) {
+    // value = e4m3 * k_scale: the scale moves out of both contractions
+    kp.scale_log2 *= a.k_scale;
+    kp.out_mult = a.k_scale;
+  }
   kp.splits = splits;
   kp.split_rows = split_rows_for(a.topk, splits);
   kp.longest_first = longest_first ? 1 : 0;
@@ -577,12 +756,17 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
     kp.part_lse = (float*)((char*)workspace + n * kDLatent * sizeof(uint16_t));
   }
   const int grid = kp.head_blocks == 2 ? ((kp.num_items + 7) / 8) * 16 : kp.num_items;
-  if (a.kv_format != 0) return hipErrorInvalidValue;
   if (a.ev_start) {
     hipError_t er = hipEventRecord(a.ev_start, stream);
     if (er != hipSuccess) return er;
   }
-  if (a.d_rope == 64) launch_kernel<576>(kp, grid, stream); else launch_kernel<512>(kp, grid, stream);
+  const bool rope = a.d_rope == 64;
+  switch (a.kv_format) {
+    case 0: rope ? launch_kernel<576, 0>(kp, grid, stream) : launch_kernel<512, 0>(kp, grid, stream); break;
+    case 1: rope ? launch_kernel<576, 1>(kp, grid, stream) : launch_kernel<512, 1>(kp, grid, stream); break;
+    case 2: rope ? launch_kernel<576, 2>(kp, grid, stream) : launch_kernel<512, 2>(kp, grid, stream); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && a.ev_end) e = hipEventRecord(a.ev_end, stream);
   if (e != hipSuccess || splits == 1) return e;

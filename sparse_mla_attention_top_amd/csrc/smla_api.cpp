@@ -76,8 +76,8 @@ int check_attn(const smla_attn_args* a, bool decode) {
     return fail(SMLA_ERR_INVALID_ARG, "group_scales is NULL for the group-scaled FP8 format");
   if (a->kv_format == SMLA_KV_FP8_E4M3_PER_TENSOR && !(std::isfinite(a->k_scale) && a->k_scale > 0))
     return fail(SMLA_ERR_INVALID_ARG, "k_scale must be finite and > 0");
-  if (a->kv_format != SMLA_KV_BF16)
-    return fail(SMLA_ERR_UNSUPPORTED, "FP8 cache formats are not built yet");
+  if (a->kv_format == SMLA_KV_FP8_E4M3_GROUP128 && ((uintptr_t)a->group_scales & 3))
+    return fail(SMLA_ERR_INVALID_ARG, "group_scales must be 4-byte aligned");
   if (decode && a->num_splits < 0) return fail(SMLA_ERR_INVALID_ARG, "num_splits < 0");
   return SMLA_OK;
 }

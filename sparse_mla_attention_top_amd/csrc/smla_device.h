@@ -100,6 +100,52 @@ __device__ __forceinline__ void dma_16b(const void* gptr, uint32_t lds_base) {
                : "m0", "memory");
 }
 
+// 4-byte global -> LDS copy (global_load_lds_dword): lane i reads 4 bytes at
+// gptr and they land at LDS byte address lds_base + 4*i. Same rules as dma_16b.
+__device__ __forceinline__ void dma_4b(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gptr), "s"(lds_base)
+               : "m0", "memory");
+}
+
+// 16 OCP E4M3FN bytes (little-endian in 4 dwords, channel c = byte c) -> 16
+// bf16 values: channels 0..7 in lo, 8..15 in hi, two per dword (low half =
+// lower channel). v_cvt_pk_f32_fp8 decodes E4M3FN exactly on gfx950 (all 256
+// codes, NaN included) and every E4M3FN value is exact in bf16, so without a
+// scale the result is exact; SCALED = true multiplies by `scale` in fp32 and
+// rounds to bf16 to nearest-even. The pairs go through a vector float->bf16
+// conversion: reinterpreting the two decoded floats as integers to take their
+// high halves was compiled with element 0 read in place of element 1.
+template <bool SCALED>
+__device__ __forceinline__ void e4m3x16_to_bf16(u32x4 raw, float scale, u32x4& lo, u32x4& hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  uint32_t outw[8];
+#pragma unroll
+  for (int d = 0; d < 4; d++) {
+    f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[d], false);
+    f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[d], true);
+    if constexpr (SCALED) {
+      a = a * scale;
+      b = b * scale;
+    }
+    outw[2 * d] = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2));
+    outw[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2));
+  }
+  lo = (u32x4){outw[0], outw[1], outw[2], outw[3]};
+  hi = (u32x4){outw[4], outw[5], outw[6], outw[7]};
+}
+
+// x[i] * sa[i] (i < 4) and x[i] * sb[i - 4] (i >= 4), in fp32, rounded to
+// nearest-even bf16.
+__device__ __forceinline__ bf16x8 scale_bf16x8(bf16x8 x, f32x4 sa, f32x4 sb) {
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  const f32x8 f = __builtin_convertvector(x, f32x8);
+  const f32x8 sc = __builtin_shufflevector(sa, sb, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_convertvector(f * sc, bf16x8);
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

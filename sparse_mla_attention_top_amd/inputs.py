@@ -134,6 +134,11 @@ def _bf16_normal(shape, seed: int, stream: int, device, chunk_rows: int = 1 << 2
     return out
 
 
+def normal_bf16_rows(n: int, d: int, seed: int, stream: int = 0, device="cpu") -> torch.Tensor:
+    """[n, d] N(0,1) values rounded to bf16 from generator (seed, stream)."""
+    return _bf16_normal((n, d), seed, 1000 + stream, device)
+
+
 def per_tensor_scale_from_absmax(kv_src: torch.Tensor) -> float:
     """Calibrated per-tensor scale of the input recipe: fl32(absmax / 448)."""
     amax = np.float32(kv_src.abs().max().float().item())

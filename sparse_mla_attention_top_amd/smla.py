@@ -168,6 +168,19 @@ def _kv_geometry(kv_cache: torch.Tensor):
     return kv_cache.shape[0], kv_cache.stride(0) * kv_cache.element_size(), kv_cache.shape[1]
 
 
+def _check_kv(kv_cache: torch.Tensor, kv_format: int, width: int, S: int,
+              group_scales: Optional[torch.Tensor]) -> None:
+    """Storage type of the cache and the group-scale array for kv_format."""
+    if kv_format == KV_BF16:
+        _need(kv_cache.dtype == torch.bfloat16, "a bf16-format cache must be a bf16 tensor")
+    else:
+        _need(kv_cache.dtype == torch.uint8, "an FP8-format cache must be a uint8 tensor of E4M3FN codes")
+    if kv_format == KV_FP8_GROUP128:
+        G = (width + 127) // 128
+        _need(group_scales is not None and group_scales.dtype == torch.float32 and group_scales.is_contiguous()
+              and group_scales.numel() >= S * G, f"group_scales must be contiguous fp32 [num_slots, {G}]")
+
+
 def _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk_length, k_scale,
                group_scales, out, lse, num_splits) -> Tuple[AttnArgs, torch.Tensor, Optional[torch.Tensor]]:
     _need(q_nope.dtype == torch.bfloat16 and q_nope.dim() == 3 and q_nope.shape[2] == 512 and q_nope.stride(2) == 1,
@@ -181,7 +194,8 @@ def _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk
           "indices must be int32 [T, topk]")
     if topk_length is not None:
         _need(topk_length.dtype == torch.int32 and topk_length.numel() == T, "topk_length must be int32 [T]")
-    S, row_stride, _ = _kv_geometry(kv_cache)
+    S, row_stride, width = _kv_geometry(kv_cache)
+    _check_kv(kv_cache, kv_format, width, S, group_scales)
     if out is None:
         out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=q_nope.device)
     _need(out.dtype == torch.bfloat16 and out.shape == (T, H, 512) and out.stride(2) == 1, "out must be bf16 [T, h, 512]")
@@ -264,7 +278,8 @@ def cache_write(kv_c: torch.Tensor, k_pe: Optional[torch.Tensor], slot_mapping: 
     d_rope = 0 if k_pe is None else k_pe.shape[1]
     if k_pe is not None:
         _need(k_pe.dtype == torch.bfloat16 and k_pe.stride(1) == 1, "k_pe must be bf16 [T, d_rope]")
-    S, row_stride, _ = _kv_geometry(kv_cache)
+    S, row_stride, width = _kv_geometry(kv_cache)
+    _check_kv(kv_cache, kv_format, width, S, group_scales)
     rc = load().smla_cache_write(_ptr(kv_c), kv_c.stride(0), _ptr(k_pe), k_pe.stride(0) if k_pe is not None else 0,
                                  _ptr(slot_mapping), kv_c.shape[0], d_rope, kv_format, float(k_scale),
                                  _ptr(kv_cache), S, row_stride, _ptr(group_scales), _stream(stream))

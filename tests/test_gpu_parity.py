@@ -1,7 +1,8 @@
 """GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
 
-Bit-exact for index conversion; max-abs 1e-2 on the bf16 output and 1e-3 on
-the LSE for attention (the tolerances the build targets state)."""
+Bit-exact for index conversion; for attention max-abs 1e-2 on the bf16 output
+(plus the bf16 rounding allowance of parity_util, which only matters for
+outputs far larger than the N(0,1) workloads give) and 1e-3 on the LSE."""
 import json
 import os
 
@@ -85,8 +86,8 @@ def _run_workload(w, entry, tokens=None, num_splits=0, scale=None):
     go, vo = O.convert_indices(w.req_id.cpu().numpy(), w.block_table.cpu().numpy(), w.topk_local.cpu().numpy(), 64)
     sel = np.arange(spec.num_tokens) if tokens is None else np.asarray(tokens)
     # the oracle gathers only the rows it needs
-    ref_o, ref_l = oracle_for(w.q.cpu(), bits(w.kv_src), go, scale, vo, tokens=sel)
-    return compare(out[torch.as_tensor(sel, device=DEV)], lse[torch.as_tensor(sel, device=DEV)], ref_o, ref_l,
+    ref = oracle_for(w.q.cpu(), bits(w.kv_src), go, scale, vo, tokens=sel)
+    return compare(out[torch.as_tensor(sel, device=DEV)], lse[torch.as_tensor(sel, device=DEV)], ref,
                    f"{spec.name}/{entry}")
 
 
@@ -145,9 +146,8 @@ def _run_case(c, scale, entry="prefill", topk_length="lengths", num_splits=0, sl
     else:
         out, lse = smla.prefill_fwd(qn, qr, kv, idx, scale, topk_length=ln, return_lse=True)
     torch.cuda.synchronize()
-    ref_o, ref_l = oracle_for(c.q, bits(c.kv_src), c.indices.numpy(), scale,
-                              None if ln is None else c.lengths.numpy())
-    return out, lse, compare(out, lse, ref_o, ref_l, "edge")
+    ref = oracle_for(c.q, bits(c.kv_src), c.indices.numpy(), scale, None if ln is None else c.lengths.numpy())
+    return out, lse, compare(out, lse, ref, "edge")
 
 
 @pytest.mark.parametrize("h", [1, 16, 33, 64, 100, 128])
@@ -227,8 +227,8 @@ def test_strided_query_and_output_views():
     o, l = smla.prefill_fwd(q[..., :512], q[..., 512:], c.kv_src.to(DEV), c.indices.to(DEV), 0.05,
                             out=out, return_lse=True)
     torch.cuda.synchronize()
-    ref_o, ref_l = oracle_for(c.q, bits(c.kv_src), c.indices.numpy(), 0.05)
-    compare(out, l, ref_o, ref_l, "strided")
+    ref = oracle_for(c.q, bits(c.kv_src), c.indices.numpy(), 0.05)
+    compare(out, l, ref, "strided")
     assert (big[:, :, 512:] == 0).all()
 
 

@@ -189,6 +189,34 @@ def test_dense_special_case_matches_sdpa():
         assert np.abs(lse[t] - ref_lse.numpy()).max() < 1e-12
 
 
+def test_magnitude_is_sdpa_over_absolute_values():
+    """sum_j p_j |v_j|: dense attention (SDPA) with the value rows replaced by
+    their absolute values and the same weights; equals the output where every
+    value is >= 0 and bounds |out| everywhere."""
+    rng = np.random.default_rng(21)
+    T, h, D, S = 2, 8, 576, 80
+    q = O.bf16_bits_to_f64(_rand_bf16(rng, (T, h, D)))
+    cache = _rand_bf16(rng, (S, D))
+    idx = np.stack([rng.permutation(S) for _ in range(T)]).astype(np.int32)
+    out, lse, mag = O.attention_with_magnitude(q, cache, O.KV_BF16, idx, 0.07)
+    out2, lse2 = O.attention(q, cache, O.KV_BF16, idx, 0.07)
+    assert (out == out2).all() and (lse == lse2).all()
+    kv = torch.from_numpy(O.bf16_bits_to_f64(cache))
+    for t in range(T):
+        qt = torch.from_numpy(q[t])[None, :, None, :]
+        k = kv[None, None].expand(1, h, S, D)
+        v = kv[None, None, :, :512].abs().expand(1, h, S, 512)
+        ref = F.scaled_dot_product_attention(qt, k, v, scale=0.07)[0, :, 0]
+        assert np.abs(mag[t] - ref.numpy()).max() < 1e-12
+    assert (mag >= np.abs(out) - 1e-12).all()
+    pos = O.bf16_bits_to_f64(cache)
+    pos_bits = _bits(torch.from_numpy(np.abs(pos).astype(np.float32)))
+    o3, _, m3 = O.attention_with_magnitude(q, pos_bits, O.KV_BF16, idx, 0.07)
+    assert np.abs(o3 - m3).max() < 1e-12
+    e_o, e_l, e_m = O.attention_with_magnitude(q, cache, O.KV_BF16, np.full((T, 4), -1, np.int32), 0.07)
+    assert (e_m == 0).all() and (e_o == 0).all() and np.isneginf(e_l).all()
+
+
 def test_permutation_invariance():
     rng = np.random.default_rng(2)
     q, cache, idx = _setup(rng)
@@ -357,12 +385,12 @@ def test_planted_mistakes_are_caught(monkeypatch):
 
     real = O.attention_rows
 
-    def no_max_in_lse(q_t, rows, scale, d_v=512):       # dropped term
+    def no_max_in_lse(q_t, rows, scale, d_v=512, magnitude=False):   # dropped term
         o, l = real(q_t, rows, scale, d_v)
         s = scale * (q_t @ rows.T)
         return o, l - s.max(axis=1)
 
-    def rope_dropped(q_t, rows, scale, d_v=512):         # wrong channel range
+    def rope_dropped(q_t, rows, scale, d_v=512, magnitude=False):     # wrong channel range
         return real(q_t[:, :512], rows[:, :512], scale, d_v)
 
     for bad in (no_max_in_lse, rope_dropped):
