@@ -28,9 +28,16 @@ WORKLOAD_TEXT = {
                    "1 query token each, h=128, top-k=2048 all valid, scale 0.0723, out + LSE",
     "prefill_bf16": "sparse MLA prefill, bf16 cache [64,64,576]: 1 request of 4096 new tokens, h=128, "
                     "top-k=2048, causal indices (valid = min(2048, pos+1)), scale 192^-0.5",
+    "nope_fp8": "sparse MLA NoPE decode, FP8 E4M3 cache [32768,64,512] with per-tensor scale absmax/448: "
+                "128 requests x 16384 context, 1 query token each, h=64, top-k=2048, valid U[512,2048] "
+                "with a -1 tail, scale 192^-0.5, out + LSE",
+    "longctx_fp8": "sparse MLA long-context decode, FP8 E4M3 cache [65536,64,576] with per-row x 128-channel "
+                   "group scales: 64 requests x 65536 context, 4 query tokens each (256), h=128, top-k=2048 "
+                   "all valid, random block table, scale 192^-0.5, out + LSE",
     "tiny": "tiny sparse MLA: 4 tokens, h=16, top-k=64, cache 256 x 576 bf16",
 }
-ENTRY = {"decode_bf16": "decode", "prefill_bf16": "prefill", "tiny": "decode"}
+ENTRY = {"decode_bf16": "decode", "prefill_bf16": "prefill", "nope_fp8": "decode", "longctx_fp8": "decode",
+         "tiny": "decode"}
 
 
 def source_hash() -> str:
@@ -83,7 +90,10 @@ def hip_elapsed_ms(a, b) -> float:
     return ms.value
 
 
-def cpu_baseline(w, gidx_np, valid_np, min_seconds: float):
+def cpu_baseline(w, gidx_np, valid_np, min_seconds: float, k_scale: float):
+    """The fp64 oracle on the host over a sample of the workload's tokens. FP8
+    workloads: the rows the sample reads are quantised by the oracle's own
+    quantiser (untimed set-up, as the cache write is untimed on the GPU)."""
     import numpy as np
     import torch
     from threadpoolctl import threadpool_info
@@ -91,14 +101,27 @@ def cpu_baseline(w, gidx_np, valid_np, min_seconds: float):
     from oracle import sparse_mla as O
     spec = w.spec
     qf = O.bf16_bits_to_f64(w.q.cpu().view(torch.int16).numpy().view(np.uint16))
-    cache = w.kv_src.cpu().view(torch.int16).numpy().view(np.uint16)
+    tokens = np.arange(spec.num_tokens)
+    if spec.num_tokens > 64:           # a strided sample of tokens, long rows included
+        tokens = np.linspace(spec.num_tokens - 1, 0, 64).astype(int)
+    # the rows the sampled tokens read, as a compact cache, and the indices remapped to it
+    used = np.unique(np.concatenate([gidx_np[t, :valid_np[t]] for t in tokens]))
+    used = used[used >= 0]
+    rows_bits = w.kv_src[torch.as_tensor(used, device=w.kv_src.device)].cpu().view(torch.int16).numpy().view(np.uint16)
+    remap = np.where(gidx_np >= 0, np.searchsorted(used, np.maximum(gidx_np, 0)), -1).astype(np.int32)
+    remap[(gidx_np >= 0) & ~np.isin(gidx_np, used)] = -1
+    scales = None
+    if spec.kv_format == O.KV_BF16:
+        cache = rows_bits
+    elif spec.kv_format == O.KV_FP8_PER_TENSOR:
+        cache = O.quantize_per_tensor(rows_bits, k_scale)
+    else:
+        cache, scales = O.quantize_group128(rows_bits)
     n_tok, reps = 0, 0
     t0 = time.perf_counter()
-    tokens = np.arange(spec.num_tokens)
-    if spec.num_tokens > 64:           # prefill: a strided sample of tokens, long rows included
-        tokens = np.linspace(spec.num_tokens - 1, 0, 64).astype(int)
     while True:
-        O.attention(qf, cache, O.KV_BF16, gidx_np, spec.softmax_scale, topk_length=valid_np, tokens=tokens)
+        O.attention(qf, cache, spec.kv_format, remap, spec.softmax_scale, topk_length=valid_np, tokens=tokens,
+                    k_scale=k_scale, group_scales=scales)
         n_tok += len(tokens)
         reps += 1
         if time.perf_counter() - t0 >= min_seconds:
@@ -109,6 +132,38 @@ def cpu_baseline(w, gidx_np, valid_np, min_seconds: float):
               f"x {reps} repetitions, numpy fp64")
     return {"value": n_tok / dt, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
             "sample": sample, "seconds": round(dt, 2)}
+
+
+def build_caches(spec, w, R: int, dev):
+    """R independent caches in the workload's storage format ([blocks, 64, D]),
+    with their group-scale arrays and per-tensor scales. FP8 caches are written
+    by the library's cache write (untimed set-up) from N(0,1) rows."""
+    import torch
+
+    from sparse_mla_attention_top_amd import inputs as I
+    from sparse_mla_attention_top_amd import smla
+    caches, gscales, kscales = [], [], []
+    S, D = spec.num_slots, spec.d
+    slots = torch.arange(S, dtype=torch.int64, device=dev) if spec.kv_format != I.KV_BF16 else None
+    for k in range(R):
+        vals = w.kv_src if k == 0 else I.draw_cache_copy(spec, k, dev)
+        if spec.kv_format == I.KV_BF16:
+            caches.append(vals.view(spec.num_blocks, I.BLOCK_SIZE, D))
+            gscales.append(None)
+            kscales.append(1.0)
+            continue
+        ks = I.per_tensor_scale_from_absmax(vals) if spec.kv_format == I.KV_FP8_PER_TENSOR else 1.0
+        cache = torch.empty((S, D), dtype=torch.uint8, device=dev)
+        gs = None
+        if spec.kv_format == I.KV_FP8_GROUP128:
+            gs = torch.empty((S, (D + 127) // 128), dtype=torch.float32, device=dev)
+        smla.cache_write(vals[:, :512], vals[:, 512:] if spec.d_rope else None, slots, cache, spec.kv_format, ks, gs)
+        torch.cuda.synchronize()
+        caches.append(cache.view(spec.num_blocks, I.BLOCK_SIZE, D))
+        gscales.append(gs)
+        kscales.append(ks)
+        del vals
+    return caches, gscales, kscales
 
 
 def main() -> int:
@@ -138,8 +193,7 @@ def main() -> int:
     entry = ENTRY[args.config]
     w = I.generate(spec, kv_device=dev)
     R = max(1, args.rotate)
-    caches = [w.kv_src] + [I.draw_cache_copy(spec, k, dev) for k in range(1, R)]
-    caches = [c.view(spec.num_blocks, I.BLOCK_SIZE, spec.d) for c in caches]
+    caches, gscales, kscales = build_caches(spec, w, R, dev)
     q = w.q.to(dev)
     qn, qr = q[..., :512], (q[..., 512:] if spec.d_rope else None)
     req, bt, loc = w.req_id.to(dev), w.block_table.to(dev), w.topk_local.to(dev)
@@ -154,11 +208,14 @@ def main() -> int:
 
     def step(k: int):
         smla.convert_indices(req, bt, loc, out=gidx, valid_counts=vcnt)
+        c = k % R
         if entry == "decode":
-            smla.decode_fwd(qn, qr, caches[k % R], gidx, spec.softmax_scale, topk_length=vcnt,
+            smla.decode_fwd(qn, qr, caches[c], gidx, spec.softmax_scale, kv_format=spec.kv_format,
+                            topk_length=vcnt, k_scale=kscales[c], group_scales=gscales[c],
                             out=out, lse=lse, workspace=ws)
         else:
-            smla.prefill_fwd(qn, qr, caches[k % R], gidx, spec.softmax_scale, topk_length=vcnt,
+            smla.prefill_fwd(qn, qr, caches[c], gidx, spec.softmax_scale, kv_format=spec.kv_format,
+                             topk_length=vcnt, k_scale=kscales[c], group_scales=gscales[c],
                              out=out, lse=lse)
 
     # eager warmup and the eager reference of step 0
@@ -235,7 +292,7 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, gidx_np, vcnt_np, args.cpu_seconds)
+        cpu = cpu_baseline(w, gidx_np, vcnt_np, args.cpu_seconds, kscales[0])
 
     line = {
         "metric": "sparse-MLA query tokens/s and TFLOP/s (h=128, top-k=2048) + % of roofline",
@@ -252,6 +309,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config, "num_tokens": T, "heads": H,
                    "topk": K, "entry": f"smla_{entry}_fwd", "splits": splits, "cache_copies_rotated": R,
+                   "kv_storage": ["bf16", "e4m3 per-tensor scale", "e4m3 per-row x 128-group scales"][spec.kv_format],
                    "timing": "HIP graph of R steps replayed; cold L2/MALL by cache rotation"},
         "tflops": round(tflops, 2),
         "pct_of_path_roofline": round(100 * roofline_time / (dt / steps), 2),
