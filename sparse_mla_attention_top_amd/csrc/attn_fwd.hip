@@ -133,7 +133,7 @@ smla_attn_kernel(KParams p) {
   __shared__ float s_l[4 * 32];
   __shared__ float s_inv[64];
   __shared__ int s_flag;
-  __shared__ int s_nrows;
+  __shared__ int s_last[4];
   __shared__ __attribute__((aligned(16))) char s_qrope[(QKS > kLatKS ? 4 * 2 * (QKS - kLatKS) : 1) * 64 * 16];
   // group format: row scales of the two bf16 tile buffers, [buffer][group][row]
   __shared__ __attribute__((aligned(16))) float s_rsc[S8::GROUP ? 2 * S8::G * kTileRows : 4];
@@ -172,66 +172,43 @@ smla_attn_kernel(KParams p) {
     split = item - t * p.splits;
   }
   const int hb = 64 * hblk;
+  const int row0 = split * p.split_rows;
+  const int cap = max(0, min(p.topk, row0 + p.split_rows) - row0);   // entries of this split
+
+  // ---- the split's index entries -> LDS (-1 marks an entry that does not take
+  //      part). They gate the first tile copies, so they are loaded first and
+  //      without waiting for the row length; tiles past the last valid entry
+  //      (an invalid tail) are not visited.
+  const int32_t* irow = p.indices + (int64_t)t * p.idx_stride + row0;
+  constexpr int kIdxPerThread = kMaxTopk / 256;
+  int gi[kIdxPerThread];
+#pragma unroll
+  for (int k = 0; k < kIdxPerThread; k++) {
+    const int j = threadIdx.x + 256 * k;
+    gi[k] = (j < cap) ? irow[j] : -1;
+  }
   int len = p.topk;
   if (p.topk_length) len = min(max(p.topk_length[t], 0), p.topk);
-  const int row0 = split * p.split_rows;
   const int nrows = max(0, min(len, row0 + p.split_rows) - row0);
-
-  // ---- Q^T as the B operand of 16x16x32: lane holds head hb + 32hg + 16nbq + li,
-  //      channels 32ks + 8lg .. +8 (ks < 16 latent, ks >= 16 rope)
-  //      The 16 latent k-steps stay in registers; the rope k-steps (D = 576) are
-  //      staged in LDS in the same lane layout and read once per tile.
-  bf16x8 q[2][kLatKS];
-#pragma unroll
-  for (int nbq = 0; nbq < 2; nbq++) {
-    const int head = hb + 32 * hg + 16 * nbq + li;
-    const bool valid = head < H;
-    const int hq = valid ? head : 0;
-    const uint16_t* qn = p.q_nope + t * p.qn_st + hq * p.qn_sh + 8 * lg;
-#pragma unroll
-    for (int ks = 0; ks < kLatKS; ks++) q[nbq][ks] = *(const bf16x8*)(qn + 32 * ks);
-    if (!valid) {
-#pragma unroll
-      for (int ks = 0; ks < kLatKS; ks++) q[nbq][ks] = (bf16x8){};
-    }
-    if (QKS > kLatKS) {
-      const uint16_t* qr = p.q_rope + t * p.qr_st + hq * p.qr_sh + 8 * lg;
-#pragma unroll
-      for (int ks = kLatKS; ks < QKS; ks++) {
-        bf16x8 v = *(const bf16x8*)(qr + 32 * (ks - kLatKS));
-        if (!valid) v = (bf16x8){};
-        lds_st128(qrope + (((w * 2 + nbq) * (QKS - kLatKS) + (ks - kLatKS)) * 64 + l) * 16, v);
-      }
-    }
-  }
-
-  // ---- the workgroup's index range -> LDS (-1 marks an entry that does not take
-  //      part); tiles past the last valid entry (an invalid tail) are not visited
-  if (threadIdx.x == 0) {
-    s_flag = 0;
-    s_nrows = 0;
-  }
-  __syncthreads();
-  const int32_t* irow = p.indices + (int64_t)t * p.idx_stride + row0;
   const int span = (nrows + kTileRows - 1) / kTileRows * kTileRows;
   int last = 0;
-  for (int j = threadIdx.x; j < span; j += 256) {
-    int g = -1;
-    if (j < nrows) {
-      g = irow[j];
+#pragma unroll
+  for (int k = 0; k < kIdxPerThread; k++) {
+    const int j = threadIdx.x + 256 * k;
+    if (j < span) {
+      int g = (j < nrows) ? gi[k] : -1;
       if (g < 0 || (int64_t)g >= p.num_slots) g = -1;
+      s_idx[j] = g;
+      if (g >= 0) last = j + 1;
     }
-    s_idx[j] = g;
-    if (g >= 0) last = j + 1;
   }
   for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
-  if (l == 0) atomicMax(&s_nrows, last);
-  // Q and the indices must be in registers/LDS before the tile DMAs start:
-  // later waits only count the DMAs.
-  wait_vmcnt<0>();
-  __syncthreads();
-  const int ntiles = (s_nrows + kTileRows - 1) / kTileRows;
+  if (l == 0) s_last[w] = last;
+  if (threadIdx.x == 0) s_flag = 0;
+  lds_barrier();
+  const int ntiles = (max(max(s_last[0], s_last[1]), max(s_last[2], s_last[3])) + kTileRows - 1) / kTileRows;
 
+  bf16x8 q[2][kLatKS];     // Q^T operands, loaded after the first tile copies are issued
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const uint32_t kv_stride = (uint32_t)p.kv_row_stride;
 
@@ -461,14 +438,14 @@ smla_attn_kernel(KParams p) {
   // being consumed, by the wave that copied it (so only that wave's copy
   // needs to have landed). full = softmax and P.V; otherwise only the
   // per-head maximum of the pass is taken (into mx_all).
-  auto run_pass = [&](const bool full, float (&mx_all)[2]) {
-    if constexpr (!F8) {
-      if (ntiles > 0) issue_tile(0);
-      if (ntiles > 1) issue_tile(1);
-    } else {
-      if (ntiles > 0) issue_tile(0);
-      if (ntiles > 1) issue_tile(1);
-      if (ntiles > 2) issue_tile(2);
+  auto issue_first = [&]() {
+    if (ntiles > 0) issue_tile(0);
+    if (ntiles > 1) issue_tile(1);
+    if (F8 && ntiles > 2) issue_tile(2);
+  };
+  auto run_pass = [&](const bool full, float (&mx_all)[2], const bool issued) {
+    if (!issued) issue_first();
+    if constexpr (F8) {
       if (ntiles > 0) {
         wait_tiles(min(ntiles - 1, 2));
         convert_tile(0);
@@ -561,6 +538,37 @@ smla_attn_kernel(KParams p) {
     }
   };
 
+  // The first tile copies go out before Q is loaded, so the two latencies
+  // overlap (the first wait on Q also covers those copies).
+  issue_first();
+  // ---- Q^T as the B operand of 16x16x32: lane holds head hb + 32hg + 16nbq + li,
+  //      channels 32ks + 8lg .. +8 (ks < 16 latent, ks >= 16 rope)
+  //      The 16 latent k-steps stay in registers; the rope k-steps (D = 576) are
+  //      staged in LDS in the same lane layout and read once per tile.
+#pragma unroll
+  for (int nbq = 0; nbq < 2; nbq++) {
+    const int head = hb + 32 * hg + 16 * nbq + li;
+    const bool valid = head < H;
+    const int hq = valid ? head : 0;
+    const uint16_t* qn = p.q_nope + t * p.qn_st + hq * p.qn_sh + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < kLatKS; ks++) q[nbq][ks] = *(const bf16x8*)(qn + 32 * ks);
+    if (!valid) {
+#pragma unroll
+      for (int ks = 0; ks < kLatKS; ks++) q[nbq][ks] = (bf16x8){};
+    }
+    if (QKS > kLatKS) {
+      const uint16_t* qr = p.q_rope + t * p.qr_st + hq * p.qr_sh + 8 * lg;
+#pragma unroll
+      for (int ks = kLatKS; ks < QKS; ks++) {
+        bf16x8 v = *(const bf16x8*)(qr + 32 * (ks - kLatKS));
+        if (!valid) v = (bf16x8){};
+        lds_st128(qrope + (((w * 2 + nbq) * (QKS - kLatKS) + (ks - kLatKS)) * 64 + l) * 16, v);
+      }
+    }
+  }
+
+
   for (int attempt = 0; attempt < 2; attempt++) {
 #pragma unroll
     for (int mb = 0; mb < 4; mb++)
@@ -568,12 +576,12 @@ smla_attn_kernel(KParams p) {
       for (int nb = 0; nb < 8; nb++) O[mb][nb] = (f32x4){};
     l_lane[0] = l_lane[1] = 0.0f;
     float unused[2] = {-INFINITY, -INFINITY};
-    run_pass(true, unused);
+    run_pass(true, unused, attempt == 0);
     lds_barrier();
     if (!s_flag) break;                                    // uniform
     // exact per-head maximum, then the full pass again
     float mx_all[2] = {-INFINITY, -INFINITY};
-    run_pass(false, mx_all);
+    run_pass(false, mx_all, false);
     wg_max(mx_all);
     m_ref[0] = mx_all[0];
     m_ref[1] = mx_all[1];
@@ -696,12 +704,15 @@ smla_combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict
 }
 
 int32_t plan_splits(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t requested) {
-  (void)num_heads;
   const int32_t max_splits = max(1, (topk + kTileRows - 1) / kTileRows);
   if (requested > 0) return min(requested, max_splits);
   if (num_tokens <= 0) return 1;
-  const int32_t target_wgs = 256;              // one workgroup per CU fills the chip
-  int32_t s = (target_wgs + num_tokens - 1) / num_tokens;
+  // One workgroup per CU (the LDS use allows one): the most splits that keep
+  // tokens x head blocks x splits within one round of 256 workgroups, since a
+  // second partial round costs a whole workgroup time.
+  const int32_t head_blocks = num_heads > 64 ? 2 : 1;
+  const int32_t target_wgs = 256;
+  int32_t s = target_wgs / (num_tokens * head_blocks);
   const int32_t min_rows = 256;                // keep >= 8 tiles per split
   s = min(s, max(1, topk / min_rows));
   return max(1, min(s, max_splits));

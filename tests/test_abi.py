@@ -84,9 +84,11 @@ def test_convert_and_cache_write_reject_bad_args():
 
 
 def test_split_plan_is_shape_only():
-    assert smla.decode_num_splits(32, 128, 2048) == 8
+    assert smla.decode_num_splits(32, 128, 2048) == 4      # 32 tokens x 2 head blocks x 4 = 256
+    assert smla.decode_num_splits(128, 64, 2048) == 2      # 128 tokens x 1 head block x 2 = 256
+    assert smla.decode_num_splits(48, 128, 2048) == 2      # never more than one round of 256
     assert smla.decode_num_splits(4096, 128, 2048) == 1
     assert smla.decode_num_splits(1, 128, 64) == 1
     assert smla.decode_num_splits(32, 128, 2048, 3) == 3
-    assert smla.decode_workspace_size(32, 128, 2048) == 8 * 32 * 128 * (512 * 2 + 4)
+    assert smla.decode_workspace_size(32, 128, 2048) == 4 * 32 * 128 * (512 * 2 + 4)
     assert smla.decode_workspace_size(4096, 128, 2048) == 0
