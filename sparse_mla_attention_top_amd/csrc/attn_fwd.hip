@@ -45,7 +45,7 @@ struct KParams {
   float out_mult;
   int32_t splits, split_rows, longest_first;
   int32_t head_blocks;  // 1 (<= 64 heads) or 2
-  int32_t num_items;    // num_tokens * splits
+  int32_t xcd_group;    // 1: all workgroups of token t run on XCD t % 8
   uint16_t* out;
   int64_t out_st, out_sh;
   float* lse;
@@ -150,26 +150,29 @@ smla_attn_kernel(KParams p) {
   const int hg = w & 1, rh = w >> 1;            // QK role: 32-head group, 16-row half
   const int T = p.num_tokens, H = p.num_heads;
 
-  // ---- work item; with two head blocks, blocks b and b+8 (same XCD) share a token
-  int item, hblk;
+  // ---- work item. The head blocks and splits of one token run on one XCD
+  //      (blocks are dispatched round-robin over the 8 XCDs, so block b runs on
+  //      XCD b % 8): its Q and its cache rows are fetched from HBM once and then
+  //      hit that XCD's L2. Token t goes to XCD t % 8 (with fewer than 8 tokens
+  //      the blocks are dealt in token order instead).
+  int t, split, hblk;
   {
     const int b = blockIdx.x;
-    if (p.head_blocks == 2) {
-      item = (b >> 4) * 8 + (b & 7);
-      hblk = (b >> 3) & 1;
+    const int per_tok = p.head_blocks * p.splits;
+    int rem;
+    if (p.xcd_group) {
+      const int k = b >> 3;
+      const int u = k / per_tok;
+      rem = k - u * per_tok;
+      t = 8 * u + (b & 7);
     } else {
-      item = b;
-      hblk = 0;
+      t = b / per_tok;
+      rem = b - t * per_tok;
     }
-  }
-  if (item >= p.num_items) return;
-  int t, split;
-  if (p.splits == 1) {
-    t = p.longest_first ? (T - 1 - item) : item;
-    split = 0;
-  } else {
-    t = item / p.splits;
-    split = item - t * p.splits;
+    if (t >= T) return;
+    hblk = rem / p.splits;
+    split = rem - hblk * p.splits;
+    if (p.longest_first) t = T - 1 - t;
   }
   const int hb = 64 * hblk;
   const int row0 = split * p.split_rows;
@@ -601,7 +604,7 @@ smla_attn_kernel(KParams p) {
     s_l[w * 32 + li] = l_lane[0];
     s_l[w * 32 + 16 + li] = l_lane[1];
   }
-  __syncthreads();
+  lds_barrier();             // LDS-only barriers from here on: stores are never waited for
   if (rh == 0 && lg == 0) {
 #pragma unroll
     for (int nbq = 0; nbq < 2; nbq++) {
@@ -619,28 +622,33 @@ smla_attn_kernel(KParams p) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   // Stage the normalised O block [64 heads][512 ch] as bf16 in the (now idle)
   // tile buffers, then write whole 16-byte chunks. O lane layout: m-block mb,
-  // n-block nb: head 16mb + 4lg + r, channel 128w + 16nb + li. Staged row h,
-  // byte b sits at h*1024 + (b ^ (((h >> 2) & 3) << 5)): the 4 head groups of
-  // one store instruction fall in different banks.
+  // n-block nb: head 16mb + 4lg + r, channel 128w + 16nb + li. Two heads of one
+  // channel are rounded together (v_cvt_pk_bf16_f32). Staged row h, byte b
+  // sits at h*1024 + (b ^ (((h >> 2) & 3) << 5)): the 4 head groups of one
+  // store instruction fall in different banks.
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   lds_char* ostage = tiles;
 #pragma unroll
   for (int mb = 0; mb < 4; mb++) {
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int hl = 16 * mb + 4 * lg + r;
-      const float sc = s_inv[hl];
+    for (int rp = 0; rp < 2; rp++) {
+      const int h0 = 16 * mb + 4 * lg + 2 * rp;
+      const float sc0 = s_inv[h0], sc1 = s_inv[h0 + 1];
 #pragma unroll
       for (int nb = 0; nb < 8; nb++) {
-        const int col = 128 * w + 16 * nb + li;
-        *(__attribute__((address_space(3))) uint16_t*)(ostage + hl * 1024 + ((2 * col) ^ (lg << 5))) =
-            f32_to_bf16_rne(O[mb][nb][r] * sc);
+        const int off = (2 * (128 * w + 16 * nb + li)) ^ (lg << 5);
+        const f32x2 v = {O[mb][nb][2 * rp] * sc0, O[mb][nb][2 * rp + 1] * sc1};
+        const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+        *(__attribute__((address_space(3))) uint16_t*)(ostage + h0 * 1024 + off) = (uint16_t)pk;
+        *(__attribute__((address_space(3))) uint16_t*)(ostage + (h0 + 1) * 1024 + off) = (uint16_t)(pk >> 16);
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   uint16_t* dst_base;
   int64_t dst_sh;
   if (p.splits == 1) {
@@ -757,7 +765,7 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
   kp.split_rows = split_rows_for(a.topk, splits);
   kp.longest_first = longest_first ? 1 : 0;
   kp.head_blocks = a.num_heads > 64 ? 2 : 1;
-  kp.num_items = a.num_tokens * splits;
+  kp.xcd_group = a.num_tokens >= 8 ? 1 : 0;
   kp.out = a.out; kp.out_st = a.out_st; kp.out_sh = a.out_sh;
   kp.lse = a.lse; kp.lse_st = a.lse_st;
   kp.part_o = nullptr; kp.part_lse = nullptr;
@@ -766,7 +774,8 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
     kp.part_o = (uint16_t*)workspace;
     kp.part_lse = (float*)((char*)workspace + n * kDLatent * sizeof(uint16_t));
   }
-  const int grid = kp.head_blocks == 2 ? ((kp.num_items + 7) / 8) * 16 : kp.num_items;
+  const int per_tok = kp.head_blocks * splits;
+  const int grid = kp.xcd_group ? 8 * ((a.num_tokens + 7) / 8) * per_tok : a.num_tokens * per_tok;
   if (a.ev_start) {
     hipError_t er = hipEventRecord(a.ev_start, stream);
     if (er != hipSuccess) return er;

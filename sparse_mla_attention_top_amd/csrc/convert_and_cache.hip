@@ -22,24 +22,36 @@ convert_indices_kernel(const int32_t* __restrict__ req_id, const int32_t* __rest
                        int32_t* __restrict__ global_out, int64_t out_stride,
                        int32_t* __restrict__ valid_counts) {
   const int t = blockIdx.x;
+  const int32_t* src = topk_local + (int64_t)t * loc_stride;
+  int32_t* dst = global_out + (int64_t)t * out_stride;
   const int r = req_id[t];
   const bool req_ok = (r >= 0) && (r < num_reqs);
   const int32_t* bt = block_table + (int64_t)(req_ok ? r : 0) * bt_row_stride;
-  const int32_t* src = topk_local + (int64_t)t * loc_stride;
-  int32_t* dst = global_out + (int64_t)t * out_stride;
   int cnt = 0;
-  for (int j = threadIdx.x; j < topk; j += 256) {
-    int l = src[j];
-    int g = -1;
-    if (req_ok && l >= 0) {
-      int blk = l / block_size;
-      if (blk < max_blocks) {
-        int e = bt[blk];
-        if (e >= 0) g = e * block_stride_rows + (l - blk * block_size);
-      }
+  // 2048 entries per pass, 8 per thread: all local-index loads of a pass are
+  // in flight together, then all block-table lookups, then the stores.
+  constexpr int PER = 8;
+  for (int base = 0; base < topk; base += 256 * PER) {
+    int l[PER];
+#pragma unroll
+    for (int k = 0; k < PER; k++) {
+      const int j = base + threadIdx.x + 256 * k;
+      l[k] = (j < topk) ? src[j] : -1;
     }
-    dst[j] = g;
-    cnt += (g >= 0);
+    int e[PER];
+#pragma unroll
+    for (int k = 0; k < PER; k++) {
+      const int blk = l[k] >= 0 ? l[k] / block_size : max_blocks;
+      e[k] = (req_ok && blk < max_blocks) ? bt[blk] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; k++) {
+      const int j = base + threadIdx.x + 256 * k;
+      int g = -1;
+      if (e[k] >= 0) g = e[k] * block_stride_rows + (l[k] - (l[k] / block_size) * block_size);
+      if (j < topk) dst[j] = g;
+      cnt += (g >= 0);
+    }
   }
   if (valid_counts) {
     // wave reduction then across the 4 waves
