@@ -6,21 +6,21 @@
 // scale) . c_kv; FlashMLA sparse API docs: heads padded to 64 or 128, LSE per
 // (token, head), empty rows give (0, -inf)).
 //
-// One workgroup = one (token, 64-head block, split), 4 waves. A token with
-// more than 64 heads takes two workgroups, dispatched to the same XCD so the
-// second gather of the same rows hits that XCD's L2. Per tile of 32 rows:
-//   gather : direct global->LDS 16-byte loads (global_load_lds_dwordx4) of the
-//            32 rows into a swizzled bf16 tile, two tiles in flight;
-//   S^T=K.Q^T: v_mfma_f32_16x16x32_bf16; wave (hg, rh) scores rows
-//            16rh..16rh+15 against heads 32hg..32hg+31, A = K from LDS,
-//            B = the wave's Q held in registers for the whole kernel;
-//   softmax: base 2 against a fixed per-head reference (see below), row
-//            reductions in-lane plus two lane shuffles;
-//   O += P.V : v_mfma_f32_16x16x32_bf16; wave w owns O for all 64 heads x
-//            latent channels 128w..128w+127 in accumulator registers, A = P
-//            (bf16) exchanged through LDS, B = V read with ds_read_b64_tr_b16
-//            from the same tile (V is the first 512 channels of the gathered
-//            row, no second gather).
+// One workgroup = one (token, 64-head block, split), 8 waves in two roles,
+// two waves per SIMD (waves w and w+4 share a SIMD):
+//   S-waves (0..3): Q^T in registers for the whole kernel. Per tile of 32
+//     rows, S^T = K.Q^T on v_mfma_f32_16x16x32_bf16 (wave (hg, rh) scores rows
+//     16rh..16rh+15 against heads 32hg..32hg+31, A = K from LDS), then the
+//     softmax (base 2, fixed per-head reference, see below) and P (bf16) into
+//     a double-buffered LDS block.
+//   O-waves (4..7): the tile copies (global_load_lds_dwordx4 straight into
+//     LDS; for FP8 caches into a stage, then converted to bf16 by the wave that
+//     copied it), and O += P.V one tile behind the S-waves: wave 4+w owns O for
+//     all 64 heads x latent channels 128w..128w+127 in accumulator registers,
+//     A = P from LDS, B = V read with ds_read_b64_tr_b16 from the same tile
+//     (V is the first 512 channels of the gathered row, no second gather).
+// So on every SIMD one wave's softmax / conversion work overlaps the other's
+// MFMAs, and one barrier per tile orders both roles.
 #include "smla_device.h"
 #include "smla_internal.h"
 
@@ -60,9 +60,6 @@ __device__ __forceinline__ bf16x8 lds_ld128(const lds_char* p) {
 __device__ __forceinline__ void lds_st64(lds_char* p, uint64_t v) {
   *(__attribute__((address_space(3))) uint64_t*)p = v;
 }
-__device__ __forceinline__ void lds_st128(lds_char* p, bf16x8 v) {
-  *(__attribute__((address_space(3))) bf16x8*)p = v;
-}
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -72,25 +69,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // Reference maximum policy. O and the running sum are accumulated against a
-// per-head reference m (base-2 units) fixed at the first tile that holds a
-// valid entry; p = 2^(t - m) stays finite in bf16/fp32 while t - m <= 64. If
-// a later score exceeds m + 64 the workgroup restarts: a max-only pass finds
-// the exact per-head maximum, then the full pass runs with it.
+// per-head reference m (base-2 units) fixed at the first tile; p = 2^(t - m)
+// stays finite in bf16/fp32 while t - m <= 64. If a later score exceeds m + 64
+// the workgroup restarts: a max-only pass finds the exact per-head maximum,
+// then the full pass runs with it.
 constexpr float kRefHeadroom = 64.0f;
-constexpr int kLatKS = kDLatent / 32;   // k-steps over the 512 latent channels
+constexpr int kLatKS = kDLatent / 32;                  // k-steps over the 512 latent channels
+constexpr int kLatBytes = kTileRows * kDLatent * 2;    // bf16 latent part of a tile (32 KB)
+constexpr int kRopeBytes = kTileRows * 64 * 2;         // bf16 rope part of a tile (4 KB)
 
-template <int D>
-struct TileShape {
-  static constexpr int RB = 2 * D;                    // bytes of one staged bf16 row
-  static constexpr int NC = D / 8;                    // 16-byte bf16 chunks per row
-  static constexpr int QKS = D / 32;                  // k-steps of the QK contraction
-  static constexpr int TILE_BYTES = kTileRows * RB;
-  static constexpr int PER = NC * kTileRows / 256;    // bf16 cache: DMA instructions per wave per tile
-  static_assert(PER * 256 == NC * kTileRows, "tile must split evenly over 4 waves");
-};
-
-// FP8 staging of one 32-row tile, as copied from HBM (E4M3 bytes). Wave w
-// copies and later converts its own rows 8w .. 8w+7:
+// Buffers of one workgroup. A bf16 tile is its latent part (chunks 0..63 of
+// every row, tile_pos layout, 32 KB) plus, for D = 576, its rope part (chunks
+// 64..71, 4 KB) in a separate ring: the latent part is read one tile longer
+// (by P.V).
+//   bf16 cache: 4 latent + 3 rope buffers; tile i+2 is copied during tile i.
+//   FP8 cache : 3 latent + 2 rope bf16 buffers and 2 FP8 stages; tile i+2 is
+//               copied and tile i+1 converted during tile i.
+// FP8 stage of one tile, as copied from HBM (E4M3 bytes). O-wave w copies and
+// later converts its own rows 8w .. 8w+7:
 //   latent : segment u (bytes 128u .. 128u+127 of the row, u < 4) of the 8
 //            rows in block 4u + w (1 KB, lane l = 8 (row & 7) + chunk);
 //   rope   : (D = 576) bytes 512 .. 575 of the 8 rows, 512 B per wave
@@ -98,15 +94,21 @@ struct TileShape {
 //   scales : (group format) the G = ceil(D/128) fp32 group scales of the 8
 //            rows, 8G dwords per wave (lane l < 8G = G (row & 7) + group).
 template <int D, int FMT>
-struct Stage8 {
+struct Shape {
+  static constexpr bool F8 = FMT != 0;
   static constexpr bool ROPE = D > kDLatent;
   static constexpr bool GROUP = FMT == 2;
+  static constexpr int QKS = D / 32;                   // k-steps of the QK contraction
+  static constexpr int NLAT = F8 ? 3 : 4;
+  static constexpr int NROPE = ROPE ? (F8 ? 2 : 3) : 0;
   static constexpr int G = (D + 127) / 128;
-  static constexpr int ROPE_OFF = 16 * 1024;
-  static constexpr int SC_OFF = ROPE_OFF + (ROPE ? 4 * 512 : 0);
-  static constexpr int BYTES = SC_OFF + (GROUP ? 4 * 256 : 0);
-  static constexpr int PERW = 4 + (ROPE ? 1 : 0) + (GROUP ? 1 : 0);  // DMA instructions per wave per tile
-  static constexpr int NBUF = 3;
+  static constexpr int ST_ROPE = 16 * 1024;
+  static constexpr int ST_SC = ST_ROPE + (ROPE ? 4 * 512 : 0);
+  static constexpr int ST_BYTES = ST_SC + (GROUP ? 4 * 256 : 0);
+  static constexpr int NSTAGE = F8 ? 2 : 0;
+  static constexpr int NRSC = GROUP ? 3 : 0;           // row-scale sets (tiles i-1, i, i+1)
+  // copy instructions per O-wave per tile
+  static constexpr int NDMA = F8 ? 4 + (ROPE ? 1 : 0) + (GROUP ? 1 : 0) : D / 64;
   static_assert(D == kDLatent || D == kDLatent + 64, "rope part must be 64 channels");
   static_assert(8 * G <= 64, "scales of 8 rows fit one instruction");
 };
@@ -114,40 +116,39 @@ struct Stage8 {
 // FMT: 0 = bf16 cache, 1 = E4M3 with one per-tensor scale, 2 = E4M3 with
 // per-row x 128-channel-group scales.
 template <int D, int FMT>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 smla_attn_kernel(KParams p) {
-  using TS = TileShape<D>;
-  using S8 = Stage8<D, FMT>;
-  constexpr bool F8 = FMT != 0;
-  constexpr int NC = TS::NC, QKS = TS::QKS, TILE_BYTES = TS::TILE_BYTES, PER = TS::PER;
-  constexpr int NBT = F8 ? 2 : 3;                      // bf16 tile buffers
-  constexpr int NDMA = F8 ? S8::PERW : PER;            // DMA instructions per wave per tile
-  static_assert(NBT * TILE_BYTES >= 64 * 1024, "the epilogue stages a 64 x 512 bf16 block in the tiles");
-  (void)NC;
+  using S = Shape<D, FMT>;
+  constexpr bool F8 = S::F8;
+  constexpr int QKS = S::QKS, NLAT = S::NLAT, NROPE = S::NROPE, NDMA = S::NDMA;
 
-  __shared__ __attribute__((aligned(16))) char s_tiles[NBT * TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) char s_stage[F8 ? S8::NBUF * S8::BYTES : 16];
-  __shared__ __attribute__((aligned(16))) char s_p[4 * 64 * 16];    // P as A operands [mblock][lane]
+  __shared__ __attribute__((aligned(16))) char s_lat[NLAT * kLatBytes];
+  __shared__ __attribute__((aligned(16))) char s_rope[(NROPE ? NROPE * kRopeBytes : 16)];
+  __shared__ __attribute__((aligned(16))) char s_stage[F8 ? S::NSTAGE * S::ST_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char s_p[2 * 4 * 64 * 16];   // P(i) in block i & 1, [mblock][lane]
   __shared__ int s_idx[kMaxTopk];
-  __shared__ float s_m[4 * 32];
-  __shared__ float s_l[4 * 32];
-  __shared__ float s_inv[64];
+  __shared__ __attribute__((aligned(16))) float s_rsc[S::GROUP ? S::NRSC * S::G * kTileRows : 4];
   __shared__ int s_flag;
-  __shared__ int s_last[4];
-  __shared__ __attribute__((aligned(16))) char s_qrope[(QKS > kLatKS ? 4 * 2 * (QKS - kLatKS) : 1) * 64 * 16];
-  // group format: row scales of the two bf16 tile buffers, [buffer][group][row]
-  __shared__ __attribute__((aligned(16))) float s_rsc[S8::GROUP ? 2 * S8::G * kTileRows : 4];
-  lds_char* qrope = (lds_char*)s_qrope;
+  __shared__ int s_last[8];
+  static_assert(NLAT >= 3, "the epilogue stages O in latent buffers 0-1 and row sums in buffer 2");
 
-  lds_char* tiles = (lds_char*)s_tiles;
+  lds_char* lat = (lds_char*)s_lat;
+  lds_char* rope = (lds_char*)s_rope;
   lds_char* stage = (lds_char*)s_stage;
-  lds_char* rsc = (lds_char*)s_rsc;
   lds_char* pbuf = (lds_char*)s_p;
+  lds_char* rsc = (lds_char*)s_rsc;
+  // per-head maxima exchanged by the S-waves (only while P block 1 is unused)
+  float* s_m = (float*)(s_p + 4 * 64 * 16);
+  // epilogue: row sums and inverse sums in latent buffer 2 (O is staged in 0-1)
+  float* s_l = (float*)(s_lat + 2 * kLatBytes);
+  float* s_inv = s_l + 4 * 32;
 
   const int w = threadIdx.x >> 6;
   const int l = threadIdx.x & 63;
   const int lg = l >> 4, li = l & 15;
-  const int hg = w & 1, rh = w >> 1;            // QK role: 32-head group, 16-row half
+  const bool is_s = w < 4;
+  const int wr = w & 3;                         // index within the role
+  const int hg = wr & 1, rh = wr >> 1;          // S role: 32-head group, 16-row half
   const int T = p.num_tokens, H = p.num_heads;
 
   // ---- work item. The head blocks and splits of one token run on one XCD
@@ -179,15 +180,14 @@ smla_attn_kernel(KParams p) {
   const int cap = max(0, min(p.topk, row0 + p.split_rows) - row0);   // entries of this split
 
   // ---- the split's index entries -> LDS (-1 marks an entry that does not take
-  //      part). They gate the first tile copies, so they are loaded first and
-  //      without waiting for the row length; tiles past the last valid entry
-  //      (an invalid tail) are not visited.
+  //      part). Loaded without waiting for the row length; tiles past the last
+  //      valid entry (an invalid tail) are not visited.
   const int32_t* irow = p.indices + (int64_t)t * p.idx_stride + row0;
-  constexpr int kIdxPerThread = kMaxTopk / 256;
+  constexpr int kIdxPerThread = kMaxTopk / 512;
   int gi[kIdxPerThread];
 #pragma unroll
   for (int k = 0; k < kIdxPerThread; k++) {
-    const int j = threadIdx.x + 256 * k;
+    const int j = threadIdx.x + 512 * k;
     gi[k] = (j < cap) ? irow[j] : -1;
   }
   int len = p.topk;
@@ -197,7 +197,7 @@ smla_attn_kernel(KParams p) {
   int last = 0;
 #pragma unroll
   for (int k = 0; k < kIdxPerThread; k++) {
-    const int j = threadIdx.x + 256 * k;
+    const int j = threadIdx.x + 512 * k;
     if (j < span) {
       int g = (j < nrows) ? gi[k] : -1;
       if (g < 0 || (int64_t)g >= p.num_slots) g = -1;
@@ -209,319 +209,376 @@ smla_attn_kernel(KParams p) {
   if (l == 0) s_last[w] = last;
   if (threadIdx.x == 0) s_flag = 0;
   lds_barrier();
-  const int ntiles = (max(max(s_last[0], s_last[1]), max(s_last[2], s_last[3])) + kTileRows - 1) / kTileRows;
+  int nlast = 0;
+#pragma unroll
+  for (int k = 0; k < 8; k++) nlast = max(nlast, s_last[k]);
+  const int ntiles = (nlast + kTileRows - 1) / kTileRows;
 
-  bf16x8 q[2][kLatKS];     // Q^T operands, loaded after the first tile copies are issued
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  const uint32_t kv_stride = (uint32_t)p.kv_row_stride;
+  // address of chunk c (16 bytes of a bf16 row) of tile row r in bf16 tile i
+  auto lat_buf = [&](int i) -> lds_char* { return lat + (i % NLAT) * kLatBytes; };
+  auto rope_buf = [&](int i) -> lds_char* { return rope + (NROPE ? (i % (NROPE ? NROPE : 1)) * kRopeBytes : 0); };
+  auto rsc_buf = [&](int i) -> lds_char* { return rsc + (S::GROUP ? (i % (S::NRSC ? S::NRSC : 1)) * S::G * kTileRows * 4 : 0); };
 
-  // bf16 cache. DMA instruction u of wave w fills block 4u + w of the tile:
-  // segment u (bytes 128u .. 128u+127) of rows 8w .. 8w+7. Lane l loads row
-  // 8w + l/8, logical chunk (l & 7) ^ swz(row) of the segment: the same row
-  // and column for every u, so one address per tile serves all PER copies
-  // through the immediate offset 128u.
-  const uint32_t tiles_addr = (uint32_t)(uintptr_t)tiles;
-  const int drow = 8 * wu + (l >> 3);
-  const uint32_t dcol = (uint32_t)(16 * ((l & 7) ^ swz(drow)));
-
-  // FP8 cache: per-tile sources of this lane (latent chunk l & 7 of row
-  // 8w + l/8; rope chunk l & 3 of row 8w + l/4; scale l % G of row 8w + l/G).
-  const uint32_t stage_addr = (uint32_t)(uintptr_t)stage;
-  const int srow = min(l / S8::G, 7), sgrp = l % S8::G;
-  struct Src {
-    const uint8_t* lat;
-    const uint8_t* rope;
-    const float* sc;
-  };
-  auto sources = [&](int tt) -> Src {
-    Src s;
-    const int base = tt * kTileRows + 8 * wu;
-    if constexpr (!F8) {
-      s.lat = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + (l >> 3)], 0) * kv_stride + dcol);
-    } else {
-      s.lat = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + (l >> 3)], 0) * kv_stride + 16 * (l & 7));
-      if constexpr (S8::ROPE)
-        s.rope = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + ((l >> 2) & 7)], 0) * kv_stride + kDLatent + 16 * (l & 3));
-      if constexpr (S8::GROUP)
-        s.sc = p.group_scales + ((uint64_t)(uint32_t)max(s_idx[base + srow], 0) * S8::G + sgrp);
-    }
-    return s;
-  };
-  // DMA instruction u (0 .. NDMA-1) of tile buffer b
-  auto issue_one = [&](const Src& s, int b, auto u_c) {
-    constexpr int u = decltype(u_c)::value;
-    if constexpr (!F8) {
-      dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(tiles_addr + b * TILE_BYTES + (4 * u + wu) * 1024));
-    } else {
-      const uint32_t sb = stage_addr + b * S8::BYTES;
-      if constexpr (u < 4) {
-        dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(sb + (4 * u + wu) * 1024));
-      } else if constexpr (u == 4 && S8::ROPE) {
-        if (l < 32) dma_16b<0>(s.rope, __builtin_amdgcn_readfirstlane(sb + S8::ROPE_OFF + wu * 512));
-      } else {
-        if (l < 8 * S8::G) dma_4b(s.sc, __builtin_amdgcn_readfirstlane(sb + S8::SC_OFF + wu * 256));
+  if (is_s) {
+    // ======================================================================
+    // S-waves: QK^T, softmax, P
+    // ======================================================================
+    // Q^T as the B operand of 16x16x32: lane holds head hb + 32hg + 16nbq + li,
+    // channels 32ks + 8lg .. +8 (ks < 16 latent, ks >= 16 rope). Heads past h are zero.
+    bf16x8 q[2][QKS];
+#pragma unroll
+    for (int nbq = 0; nbq < 2; nbq++) {
+      const int head = hb + 32 * hg + 16 * nbq + li;
+      const bool valid = head < H;
+      const int hq = valid ? head : 0;
+      const uint16_t* qn = p.q_nope + t * p.qn_st + hq * p.qn_sh + 8 * lg;
+#pragma unroll
+      for (int ks = 0; ks < kLatKS; ks++) q[nbq][ks] = *(const bf16x8*)(qn + 32 * ks);
+      if (QKS > kLatKS) {
+        const uint16_t* qr = p.q_rope + t * p.qr_st + hq * p.qr_sh + 8 * lg;
+#pragma unroll
+        for (int ks = kLatKS; ks < QKS; ks++) q[nbq][ks] = *(const bf16x8*)(qr + 32 * (ks - kLatKS));
+      }
+      if (!valid) {
+#pragma unroll
+        for (int ks = 0; ks < QKS; ks++) q[nbq][ks] = (bf16x8){};
       }
     }
-  };
-  constexpr int NBUF_DMA = 3;                // buffers the DMAs rotate over (bf16 tiles or FP8 stages)
-  auto issue_tile = [&](int tt) {
-    const Src s = sources(tt);
-    static_for<NDMA>([&](auto u_c) { issue_one(s, tt % NBUF_DMA, u_c); });
-  };
-  // wait until at most n (0..2) tiles' DMAs of this wave are outstanding
-  auto wait_tiles = [&](int n) {
-    if (n >= 2) wait_vmcnt<2 * NDMA>();
-    else if (n == 1) wait_vmcnt<NDMA>();
-    else wait_vmcnt<0>();
-  };
-  // FP8: this wave's rows of staged tile tt -> bf16 tile buffer tt & 1. The
-  // tile holds the E4M3 values themselves (exact in bf16); in the group
-  // format the row scales go to s_rsc[tt & 1] and are applied to the QK
-  // partial sums and to P (see scores and P.V).
-  auto convert_tile = [&](int tt) {
-    if constexpr (F8) {
-      const lds_char* st = stage + (tt % S8::NBUF) * S8::BYTES;
-      lds_char* tb = tiles + (tt & 1) * TILE_BYTES;
-      const int r = 8 * w + (l >> 3);
-      static_for<4>([&](auto u_c) {
-        constexpr int u = decltype(u_c)::value;
-        const u32x4 raw = *(const __attribute__((address_space(3))) u32x4*)(st + (4 * u + w) * 1024 + 16 * l);
-        if constexpr (S8::GROUP) {
-          const float sc = *(const __attribute__((address_space(3))) float*)(st + S8::SC_OFF + w * 256 + 4 * ((l >> 3) * S8::G + u));
-          *(__attribute__((address_space(3))) float*)(rsc + 4 * (((tt & 1) * S8::G + u) * kTileRows + r)) = sc;
+    // complete here, so that the compiler puts no wait on the Q registers inside the loop
+    wait_vmcnt<0>();
+
+    // K reads (A operand of 16x16x32): row 16rh + li, chunk 4ks + lg; k-steps
+    // 0..15 in the latent buffer at kbase[ks & 1] + 4096 (ks >> 1), 16..17 in
+    // the rope buffer at kbase[ks & 1] + 4096 (ks >> 1) - 32768.
+    int kbase[2];
+#pragma unroll
+    for (int j = 0; j < 2; j++) kbase[j] = tile_pos(16 * rh + li, 4 * j + lg);
+
+    // S^T[16 rows x 32 heads] of the wave for tile i, base-2 units, masked. Lane
+    // holds rows 16rh + 4lg + r (r = 0..3) of heads 32hg + 16nbq + li. Group
+    // format: the k-steps of channel group g = ks / 4 accumulate apart; each
+    // group's partial sums are scaled by the rows' group scales and added into
+    // t0 / t1 two k-steps into the next group (when its MFMAs are done).
+    auto scores = [&](int i, uint32_t vmask, float (&tv)[2][4]) {
+      const lds_char* lb = lat_buf(i);
+      const lds_char* rb = rope_buf(i);
+      auto kaddr = [&](auto ks_c) -> const lds_char* {
+        constexpr int ks = decltype(ks_c)::value;
+        if constexpr (ks < kLatKS) return lb + kbase[ks & 1] + 4096 * (ks >> 1);
+        else return rb + kbase[ks & 1] + 4096 * (ks >> 1) - kLatBytes;
+      };
+      f32x4 s0 = {}, s1 = {}, s2 = {}, s3 = {};   // even / odd k-steps: 4 independent chains
+      f32x4 t0 = {}, t1 = {}, o0 = {}, o1 = {}, o2 = {}, o3 = {}, osc = {};
+      const lds_char* rs = rsc_buf(i) + 4 * (16 * rh + 4 * lg);
+      (void)rs;
+      constexpr int PF = S::GROUP ? 4 : 6;        // K operand reads kept in flight
+      bf16x8 a[PF];
+      static_for<PF>([&](auto ks_c) { a[decltype(ks_c)::value] = lds_ld128(kaddr(ks_c)); });
+      static_for<QKS>([&](auto ks_c) {
+        constexpr int ks = decltype(ks_c)::value;
+        const bf16x8 cur = a[ks % PF];
+        if constexpr (ks + PF < QKS) a[ks % PF] = lds_ld128(kaddr(std::integral_constant<int, ks + PF>{}));
+        if constexpr (S::GROUP && (ks & 3) == 0 && ks > 0) {
+          // group ks/4 - 1 is complete: keep its chains and their scales, start afresh
+          o0 = s0; o1 = s1; o2 = s2; o3 = s3;
+          s0 = (f32x4){}; s1 = (f32x4){}; s2 = (f32x4){}; s3 = (f32x4){};
+          osc = *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * (ks / 4 - 1));
         }
-        u32x4 lo, hi;
-        e4m3x16_to_bf16<false>(raw, 1.0f, lo, hi);
-        const int k = 8 * u + (l & 7);
-        *(__attribute__((address_space(3))) u32x4*)(tb + tile_pos(r, 2 * k)) = lo;
-        *(__attribute__((address_space(3))) u32x4*)(tb + tile_pos(r, 2 * k + 1)) = hi;
+        __builtin_amdgcn_sched_barrier(0);          // keep the read-ahead ahead of the MFMAs
+        const bf16x8 b0 = q[0][ks], b1 = q[1][ks];
+        if constexpr ((ks & 1) == 0) {
+          s0 = mfma16x16x32(cur, b0, s0);
+          s1 = mfma16x16x32(cur, b1, s1);
+        } else {
+          s2 = mfma16x16x32(cur, b0, s2);
+          s3 = mfma16x16x32(cur, b1, s3);
+        }
+        if constexpr (S::GROUP && (ks & 3) == 2 && ks > 4) {
+          t0 += osc * (o0 + o2);
+          t1 += osc * (o1 + o3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       });
-      if constexpr (S8::ROPE) {
-        if (l < 32) {
-          const int r2 = 8 * w + (l >> 2);
-          const u32x4 raw = *(const __attribute__((address_space(3))) u32x4*)(st + S8::ROPE_OFF + w * 512 + 16 * l);
-          if constexpr (S8::GROUP) {
-            const float sc = *(const __attribute__((address_space(3))) float*)(st + S8::SC_OFF + w * 256 + 4 * ((l >> 2) * S8::G + 4));
-            *(__attribute__((address_space(3))) float*)(rsc + 4 * (((tt & 1) * S8::G + 4) * kTileRows + r2)) = sc;
+      if constexpr (S::GROUP) {
+        constexpr int gl = (QKS - 1) / 4;               // last group
+        if constexpr ((QKS - 1) % 4 < 2 && gl > 0) {    // the group before it was not folded yet
+          t0 += osc * (o0 + o2);
+          t1 += osc * (o1 + o3);
+        }
+        const f32x4 lsc = *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * gl);
+        s0 = t0 + lsc * (s0 + s2);
+        s1 = t1 + lsc * (s1 + s3);
+      } else {
+        s0 += s2;
+        s1 += s3;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const bool ok = (vmask >> (16 * rh + 4 * lg + r)) & 1;
+        tv[0][r] = ok ? s0[r] * p.scale_log2 : -INFINITY;
+        tv[1][r] = ok ? s1[r] * p.scale_log2 : -INFINITY;
+      }
+    };
+    // maximum over the workgroup's 32 rows (both row halves), per head; one
+    // barrier, which the O-waves match
+    auto wg_max = [&](float (&mx)[2]) {
+#pragma unroll
+      for (int nbq = 0; nbq < 2; nbq++) {
+        float m = mx[nbq];
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        mx[nbq] = m;
+      }
+      if (lg == 0) {
+        s_m[wr * 32 + li] = mx[0];
+        s_m[wr * 32 + 16 + li] = mx[1];
+      }
+      lds_barrier();
+      mx[0] = fmaxf(mx[0], s_m[(wr ^ 2) * 32 + li]);
+      mx[1] = fmaxf(mx[1], s_m[(wr ^ 2) * 32 + 16 + li]);
+    };
+
+    float m_ref[2] = {-INFINITY, -INFINITY};
+    float l_lane[2] = {0.0f, 0.0f};
+    bool have_ref = false;                                 // workgroup-uniform
+
+    // one pass over the tiles; full = softmax and P, otherwise only the
+    // per-head maximum (into mx_all). Barriers: one per tile, plus the
+    // reference exchange in tile 0 of a full pass.
+    auto s_pass = [&](const bool full, float (&mx_all)[2]) {
+      l_lane[0] = l_lane[1] = 0.0f;
+      lds_barrier();                                       // pass start: tiles 0 (and 1) are in LDS
+      for (int i = 0; i <= ntiles; i++) {
+        const bool have = i < ntiles;
+        float tv[2][4];
+        float mx[2] = {-INFINITY, -INFINITY};
+        if (have) {
+          const uint32_t vmask = (uint32_t)__ballot((l < 32) ? (s_idx[i * kTileRows + l] >= 0) : 0);
+          scores(i, vmask, tv);
+#pragma unroll
+          for (int nbq = 0; nbq < 2; nbq++)
+            mx[nbq] = fmaxf(fmaxf(tv[nbq][0], tv[nbq][1]), fmaxf(tv[nbq][2], tv[nbq][3]));
+        }
+        if (!full) {
+          mx_all[0] = fmaxf(mx_all[0], mx[0]);
+          mx_all[1] = fmaxf(mx_all[1], mx[1]);
+          lds_barrier();
+          continue;
+        }
+        if (i == 0) {                                      // the reference: tile 0's maximum
+          float m0[2] = {mx[0], mx[1]};                    // (the exchange barrier always runs:
+          wg_max(m0);                                      //  the O-waves match it)
+          if (!have_ref) {                                 // a rerun keeps the exact maximum
+            m_ref[0] = m0[0];
+            m_ref[1] = m0[1];
+            have_ref = true;
+          }
+        }
+        if (have) {
+          if (fmaxf(mx[0] - m_ref[0], mx[1] - m_ref[1]) > kRefHeadroom) s_flag = 1;
+          lds_char* pb = pbuf + (i & 1) * (4 * 64 * 16);
+#pragma unroll
+          for (int nbq = 0; nbq < 2; nbq++) {
+            const float msub = (m_ref[nbq] == -INFINITY) ? 0.0f : m_ref[nbq];
+            float pr[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) pr[r] = fast_exp2(tv[nbq][r] - msub);
+            l_lane[nbq] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+            const uint64_t pk = (uint64_t)pack_bf16x2(pr[0], pr[1]) | ((uint64_t)pack_bf16x2(pr[2], pr[3]) << 32);
+            // A operand of m-block 2hg + nbq, elements 4rh .. 4rh+3
+            lds_st64(pb + ((2 * hg + nbq) * 64 + l) * 16 + 8 * rh, pk);
+          }
+        }
+        lds_barrier();
+      }
+    };
+
+    for (int attempt = 0; attempt < 2; attempt++) {
+      float unused[2] = {-INFINITY, -INFINITY};
+      s_pass(true, unused);
+      if (!s_flag) break;                                  // uniform (after the pass's last barrier)
+      // exact per-head maximum, then the full pass again
+      float mx_all[2] = {-INFINITY, -INFINITY};
+      s_pass(false, mx_all);
+      wg_max(mx_all);
+      m_ref[0] = mx_all[0];
+      m_ref[1] = mx_all[1];
+      if (threadIdx.x == 0) s_flag = 0;
+    }
+
+    // ---- epilogue (S side): row sums per head, LSE, inverse sums
+#pragma unroll
+    for (int nbq = 0; nbq < 2; nbq++) {
+      float v = l_lane[nbq];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      l_lane[nbq] = v;
+    }
+    if (lg == 0) {
+      s_l[wr * 32 + li] = l_lane[0];
+      s_l[wr * 32 + 16 + li] = l_lane[1];
+    }
+    lds_barrier();                                         // E1
+    if (rh == 0 && lg == 0) {
+#pragma unroll
+      for (int nbq = 0; nbq < 2; nbq++) {
+        const float lt = s_l[wr * 32 + 16 * nbq + li] + s_l[(wr ^ 2) * 32 + 16 * nbq + li];
+        const int hl = 32 * hg + 16 * nbq + li;          // head within the block
+        s_inv[hl] = (lt > 0.0f) ? p.out_mult / lt : 0.0f;
+        const float lse_v = (lt > 0.0f) ? (m_ref[nbq] + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+        const int head = hb + hl;
+        if (head < H) {
+          if (p.splits == 1) {
+            if (p.lse) p.lse[(int64_t)t * p.lse_st + head] = lse_v;
+          } else {
+            p.part_lse[((int64_t)split * T + t) * H + head] = lse_v;
+          }
+        }
+      }
+    }
+    lds_barrier();                                         // E2
+    lds_barrier();                                         // E3: O staged
+  } else {
+    // ======================================================================
+    // O-waves: tile copies (and FP8 conversion), P.V
+    // ======================================================================
+    const int wu = __builtin_amdgcn_readfirstlane(wr);
+    const uint32_t kv_stride = (uint32_t)p.kv_row_stride;
+    const uint32_t lat_addr = (uint32_t)(uintptr_t)lat;
+    const uint32_t rope_addr = (uint32_t)(uintptr_t)rope;
+    const uint32_t stage_addr = (uint32_t)(uintptr_t)stage;
+    // bf16 cache: copy u of wave w fills block 4u + w of the tile (segment u,
+    // bytes 128u .. 128u+127, of rows 8w .. 8w+7; segment 8 is the rope part).
+    // Lane l loads row 8w + l/8, logical chunk (l & 7) ^ swz(row): the same row
+    // and column for every u, so one address per tile serves all copies
+    // through the immediate offset 128u.
+    const int drow = 8 * wu + (l >> 3);
+    const uint32_t dcol = (uint32_t)(16 * ((l & 7) ^ swz(drow)));
+    // FP8 cache: latent chunk l & 7 of row 8w + l/8; rope chunk l & 3 of row
+    // 8w + l/4; scale l % G of row 8w + l/G.
+    const int srow = min(l / S::G, 7), sgrp = l % S::G;
+    struct Src {
+      const uint8_t* lat;
+      const uint8_t* rope;
+      const float* sc;
+    };
+    auto sources = [&](int i) -> Src {
+      Src s;
+      const int base = i * kTileRows + 8 * wu;
+      if constexpr (!F8) {
+        s.lat = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + (l >> 3)], 0) * kv_stride + dcol);
+      } else {
+        s.lat = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + (l >> 3)], 0) * kv_stride + 16 * (l & 7));
+        if constexpr (S::ROPE)
+          s.rope = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + ((l >> 2) & 7)], 0) * kv_stride + kDLatent + 16 * (l & 3));
+        if constexpr (S::GROUP)
+          s.sc = p.group_scales + ((uint64_t)(uint32_t)max(s_idx[base + srow], 0) * S::G + sgrp);
+      }
+      return s;
+    };
+    // copy instruction u (0 .. NDMA-1) of tile i
+    auto issue_one = [&](const Src& s, int i, auto u_c) {
+      constexpr int u = decltype(u_c)::value;
+      if constexpr (!F8) {
+        if constexpr (u < 8) {
+          dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(lat_addr + (i % NLAT) * kLatBytes + (4 * u + wu) * 1024));
+        } else {
+          dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(rope_addr + (i % (NROPE ? NROPE : 1)) * kRopeBytes + wu * 1024));
+        }
+      } else {
+        const uint32_t sb = stage_addr + (i % S::NSTAGE) * S::ST_BYTES;
+        if constexpr (u < 4) {
+          dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(sb + (4 * u + wu) * 1024));
+        } else if constexpr (u == 4 && S::ROPE) {
+          if (l < 32) dma_16b<0>(s.rope, __builtin_amdgcn_readfirstlane(sb + S::ST_ROPE + wu * 512));
+        } else {
+          if (l < 8 * S::G) dma_4b(s.sc, __builtin_amdgcn_readfirstlane(sb + S::ST_SC + wu * 256));
+        }
+      }
+    };
+    auto issue_tile = [&](int i) {
+      const Src s = sources(i);
+      static_for<NDMA>([&](auto u_c) { issue_one(s, i, u_c); });
+    };
+    // wait until at most n (0 or 1) tiles' copies of this wave are outstanding
+    auto wait_tiles = [&](int n) {
+      if (n >= 1) wait_vmcnt<NDMA>(); else wait_vmcnt<0>();
+    };
+    // FP8: this wave's rows of staged tile i -> bf16 tile i (exact E4M3 values);
+    // group format: the rows' scales -> row-scale set i ([group][row]).
+    auto convert_tile = [&](int i) {
+      if constexpr (F8) {
+        const lds_char* st = stage + (i % S::NSTAGE) * S::ST_BYTES;
+        lds_char* lb = lat_buf(i);
+        const int r = 8 * wr + (l >> 3);
+        static_for<4>([&](auto u_c) {
+          constexpr int u = decltype(u_c)::value;
+          const u32x4 raw = *(const __attribute__((address_space(3))) u32x4*)(st + (4 * u + wr) * 1024 + 16 * l);
+          if constexpr (S::GROUP) {
+            const float sc = *(const __attribute__((address_space(3))) float*)(st + S::ST_SC + wr * 256 + 4 * ((l >> 3) * S::G + u));
+            *(__attribute__((address_space(3))) float*)(rsc_buf(i) + 4 * (u * kTileRows + r)) = sc;
           }
           u32x4 lo, hi;
           e4m3x16_to_bf16<false>(raw, 1.0f, lo, hi);
-          const int k = 32 + (l & 3);
-          *(__attribute__((address_space(3))) u32x4*)(tb + tile_pos(r2, 2 * k)) = lo;
-          *(__attribute__((address_space(3))) u32x4*)(tb + tile_pos(r2, 2 * k + 1)) = hi;
+          const int k = 8 * u + (l & 7);
+          *(__attribute__((address_space(3))) u32x4*)(lb + tile_pos(r, 2 * k)) = lo;
+          *(__attribute__((address_space(3))) u32x4*)(lb + tile_pos(r, 2 * k + 1)) = hi;
+        });
+        if constexpr (S::ROPE) {
+          if (l < 32) {
+            const int r2 = 8 * wr + (l >> 2);
+            const u32x4 raw = *(const __attribute__((address_space(3))) u32x4*)(st + S::ST_ROPE + wr * 512 + 16 * l);
+            if constexpr (S::GROUP) {
+              const float sc = *(const __attribute__((address_space(3))) float*)(st + S::ST_SC + wr * 256 + 4 * ((l >> 2) * S::G + 4));
+              *(__attribute__((address_space(3))) float*)(rsc_buf(i) + 4 * (4 * kTileRows + r2)) = sc;
+            }
+            u32x4 lo, hi;
+            e4m3x16_to_bf16<false>(raw, 1.0f, lo, hi);
+            const int k = (l & 3);                          // chunks 64 + 2k, 65 + 2k: rope buffer
+            lds_char* rb = rope_buf(i);
+            *(__attribute__((address_space(3))) u32x4*)(rb + tile_pos(r2, 64 + 2 * k) - kLatBytes) = lo;
+            *(__attribute__((address_space(3))) u32x4*)(rb + tile_pos(r2, 65 + 2 * k) - kLatBytes) = hi;
+          }
         }
       }
-    }
-  };
+    };
 
-  // K reads (A operand of 16x16x32): row 16rh + li, chunk 4ks + lg, at
-  // kbase[ks & 1] + 4096 (ks >> 1).
-  int kbase[2];
+    // V transposing reads (B operand of P.V): in 16-lane group lg, lane li = 4e + q
+    // reads row 4lg + e (then 16 + 4lg + e), channels 128w + 16nb + 4q .. +3,
+    // at vbase[half][nb & 3] + 4096 (nb >> 2).
+    int vbase[2][4];
+    {
+      const int e = li >> 2, q4 = li & 3;
 #pragma unroll
-  for (int j = 0; j < 2; j++) kbase[j] = tile_pos(16 * rh + li, 4 * j + lg);
-  // V transposing reads (B operand of P.V): in 16-lane group lg, lane li = 4e + q
-  // reads row 4lg + e (then 16 + 4lg + e), channels 128w + 16nb + 4q .. +3,
-  // at vbase[half][nb & 3] + 4096 (nb >> 2).
-  int vbase[2][4];
-  {
-    const int e = li >> 2, q4 = li & 3;
+      for (int half = 0; half < 2; half++)
 #pragma unroll
-    for (int half = 0; half < 2; half++)
-#pragma unroll
-      for (int j = 0; j < 4; j++)
-        vbase[half][j] = tile_pos(16 * half + 4 * lg + e, 16 * w + 2 * j + (q4 >> 1)) + 8 * (q4 & 1);
-  }
-
-  // S^T[16 rows x 32 heads] of the wave for tile buffer tb, base-2 units, masked.
-  // Lane holds rows 16rh + 4lg + r (r = 0..3) of heads 32hg + 16nbq + li. The
-  // DMAs of tile dma_tt (if >= 0) are issued between the k-steps.
-  // Group format: the k-steps of channel group g = ks / 4 accumulate apart;
-  // each group's partial sums are scaled by the rows' group scales and added
-  // into t0 / t1 two k-steps into the next group (when its MFMAs are done).
-  auto scores = [&](const lds_char* tb, uint32_t vmask, float (&tv)[2][4], int dma_tt, int rbuf) {
-    f32x4 s0 = {}, s1 = {}, s2 = {}, s3 = {};  // even / odd k-steps: 4 independent chains
-    f32x4 t0 = {}, t1 = {}, o0 = {}, o1 = {}, o2 = {}, o3 = {}, osc = {};
-    const lds_char* rs = rsc + 4 * (rbuf * S8::G * kTileRows + 16 * rh + 4 * lg);
-    (void)rs;
-    constexpr int PF = 4;                      // K operand reads kept in flight
-    bf16x8 a[PF];
-#pragma unroll
-    for (int ks = 0; ks < PF; ks++) a[ks] = lds_ld128(tb + kbase[ks & 1] + 4096 * (ks >> 1));
-    Src dsrc;
-    if (dma_tt >= 0) dsrc = sources(dma_tt);
-    const int db = dma_tt >= 0 ? dma_tt % NBUF_DMA : 0;
-    static_for<QKS>([&](auto ks_c) {
-      constexpr int ks = decltype(ks_c)::value;
-      const bf16x8 cur = a[ks % PF];
-      if constexpr (ks + PF < QKS) a[ks % PF] = lds_ld128(tb + kbase[(ks + PF) & 1] + 4096 * ((ks + PF) >> 1));
-      if constexpr ((ks & 1) == 0 && (ks >> 1) < NDMA) {
-        if (dma_tt >= 0) issue_one(dsrc, db, std::integral_constant<int, (ks >> 1)>{});
-      }
-      if constexpr (S8::GROUP && F8 && (ks & 3) == 0 && ks > 0) {
-        // group ks/4 - 1 is complete: keep its chains and their scales, start afresh
-        o0 = s0; o1 = s1; o2 = s2; o3 = s3;
-        s0 = (f32x4){}; s1 = (f32x4){}; s2 = (f32x4){}; s3 = (f32x4){};
-        osc = *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * (ks / 4 - 1));
-      }
-      __builtin_amdgcn_sched_barrier(0);       // keep the read-ahead ahead of the MFMAs
-      bf16x8 b0, b1;
-      if constexpr (ks < kLatKS) {
-        b0 = q[0][ks];
-        b1 = q[1][ks];
-      } else {
-        b0 = lds_ld128(qrope + (((w * 2 + 0) * (QKS - kLatKS) + (ks - kLatKS)) * 64 + l) * 16);
-        b1 = lds_ld128(qrope + (((w * 2 + 1) * (QKS - kLatKS) + (ks - kLatKS)) * 64 + l) * 16);
-      }
-      if constexpr ((ks & 1) == 0) {
-        s0 = mfma16x16x32(cur, b0, s0);
-        s1 = mfma16x16x32(cur, b1, s1);
-      } else {
-        s2 = mfma16x16x32(cur, b0, s2);
-        s3 = mfma16x16x32(cur, b1, s3);
-      }
-      if constexpr (S8::GROUP && F8 && (ks & 3) == 2 && ks > 4) {
-        t0 += osc * (o0 + o2);
-        t1 += osc * (o1 + o3);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    if constexpr (S8::GROUP && F8) {
-      constexpr int gl = (QKS - 1) / 4;                // last group
-      if constexpr ((QKS - 1) % 4 < 2 && gl > 0) {     // the group before it was not folded yet
-        t0 += osc * (o0 + o2);
-        t1 += osc * (o1 + o3);
-      }
-      const f32x4 lsc = *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * gl);
-      s0 = t0 + lsc * (s0 + s2);
-      s1 = t1 + lsc * (s1 + s3);
-    } else {
-      s0 += s2;
-      s1 += s3;
+        for (int j = 0; j < 4; j++)
+          vbase[half][j] = tile_pos(16 * half + 4 * lg + e, 16 * wr + 2 * j + (q4 >> 1)) + 8 * (q4 & 1);
     }
-    static_assert(2 * NDMA <= QKS + 1, "DMA issue slots");
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const bool ok = (vmask >> (16 * rh + 4 * lg + r)) & 1;
-      tv[0][r] = ok ? s0[r] * p.scale_log2 : -INFINITY;
-      tv[1][r] = ok ? s1[r] * p.scale_log2 : -INFINITY;
-    }
-  };
-  // lane-local maximum of the 4 rows it holds, per head block
-  auto lane_max = [&](const float (&tv)[2][4], float (&mx)[2]) {
-#pragma unroll
-    for (int nbq = 0; nbq < 2; nbq++)
-      mx[nbq] = fmaxf(fmaxf(tv[nbq][0], tv[nbq][1]), fmaxf(tv[nbq][2], tv[nbq][3]));
-  };
-  // maximum over the workgroup's 32 rows of a tile (or of a whole pass), per head
-  auto wg_max = [&](float (&mx)[2]) {
-#pragma unroll
-    for (int nbq = 0; nbq < 2; nbq++) {
-      float m = mx[nbq];
-      m = fmaxf(m, __shfl_xor(m, 16, 64));
-      m = fmaxf(m, __shfl_xor(m, 32, 64));
-      mx[nbq] = m;
-    }
-    if (lg == 0) {
-      s_m[w * 32 + li] = mx[0];
-      s_m[w * 32 + 16 + li] = mx[1];
-    }
-    lds_barrier();
-    mx[0] = fmaxf(mx[0], s_m[(w ^ 2) * 32 + li]);
-    mx[1] = fmaxf(mx[1], s_m[(w ^ 2) * 32 + 16 + li]);
-  };
 
-  float m_ref[2] = {-INFINITY, -INFINITY};
-  float l_lane[2];
-  f32x4 O[4][8];
-  bool have_ref = false;      // workgroup-uniform: a reference has been fixed
-
-  // Tile pipeline. bf16 cache: tiles are copied straight into the bf16 tile
-  // buffers, two ahead. FP8 cache: tiles are copied into the FP8 stages three
-  // ahead; tile tt+1 is converted into the free bf16 buffer while tile tt is
-  // being consumed, by the wave that copied it (so only that wave's copy
-  // needs to have landed). full = softmax and P.V; otherwise only the
-  // per-head maximum of the pass is taken (into mx_all).
-  auto issue_first = [&]() {
-    if (ntiles > 0) issue_tile(0);
-    if (ntiles > 1) issue_tile(1);
-    if (F8 && ntiles > 2) issue_tile(2);
-  };
-  auto run_pass = [&](const bool full, float (&mx_all)[2], const bool issued) {
-    if (!issued) issue_first();
-    if constexpr (F8) {
-      if (ntiles > 0) {
-        wait_tiles(min(ntiles - 1, 2));
-        convert_tile(0);
-      }
-    }
-    for (int tt = 0; tt < ntiles; tt++) {
-      if constexpr (!F8) {
-        if (tt + 1 < ntiles) wait_vmcnt<PER>(); else wait_vmcnt<0>();
-      }
-      lds_barrier();
-      const int ahead = F8 ? 3 : 2;
-      const int dma_tt = (tt + ahead < ntiles) ? tt + ahead : -1;
-      const lds_char* tb = tiles + (F8 ? (tt & 1) : (tt % NBT)) * TILE_BYTES;
-      const uint32_t vmask = (uint32_t)__ballot((l < 32) ? (s_idx[tt * kTileRows + l] >= 0) : 0);
-
-      float tv[2][4];
-      scores(tb, vmask, tv, dma_tt, tt & 1);
-      float mx[2];
-      lane_max(tv, mx);
-      if (!full) {
-        mx_all[0] = fmaxf(mx_all[0], mx[0]);
-        mx_all[1] = fmaxf(mx_all[1], mx[1]);
-        if (F8 && tt + 1 < ntiles) {
-          wait_tiles(min(ntiles - tt - 2, 2));
-          convert_tile(tt + 1);
-        }
-        continue;
-      }
-      if (!have_ref) {                                     // uniform: first tile with a valid row
-        wg_max(mx);
-        m_ref[0] = mx[0];
-        m_ref[1] = mx[1];
-        have_ref = true;
-      }
-      if (fmaxf(mx[0] - m_ref[0], mx[1] - m_ref[1]) > kRefHeadroom) s_flag = 1;
-      uint64_t pk[2];
+    f32x4 O[4][8];
+    // O[64 heads x 128 ch] += P(i)[64 x 32] . V(i)[32 x 128]
+    auto pv = [&](int i) {
+      const lds_char* lb = lat_buf(i);
+      const lds_char* pb = pbuf + (i & 1) * (4 * 64 * 16);
+      constexpr int VPF = 3;                                // V reads kept in flight (n-blocks)
+      s16x4 vr[VPF + 1][2];
 #pragma unroll
-      for (int nbq = 0; nbq < 2; nbq++) {
-        const float msub = (m_ref[nbq] == -INFINITY) ? 0.0f : m_ref[nbq];
-        float pr[4];
-#pragma unroll
-        for (int r = 0; r < 4; r++) pr[r] = fast_exp2(tv[nbq][r] - msub);
-        l_lane[nbq] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        pk[nbq] = (uint64_t)pack_bf16x2(pr[0], pr[1]) | ((uint64_t)pack_bf16x2(pr[2], pr[3]) << 32);
-        // A operand of m-block 2hg + nbq, elements 4rh .. 4rh+3
-        lds_st64(pbuf + ((2 * hg + nbq) * 64 + l) * 16 + 8 * rh, pk[nbq]);
+      for (int nb = 0; nb < VPF; nb++) {
+        vr[nb][0] = lds_read_tr16(lb + vbase[0][nb & 3] + 4096 * (nb >> 2));
+        vr[nb][1] = lds_read_tr16(lb + vbase[1][nb & 3] + 4096 * (nb >> 2));
       }
-      lds_barrier();
-      if (F8 && tt + 1 < ntiles) {
-        wait_tiles(min(ntiles - tt - 2, 2));
-        convert_tile(tt + 1);
-      }
-
       bf16x8 pa[4];
 #pragma unroll
-      for (int mb = 0; mb < 4; mb++) pa[mb] = lds_ld128(pbuf + (mb * 64 + l) * 16);
-      if constexpr (S8::GROUP && F8) {
+      for (int mb = 0; mb < 4; mb++) pa[mb] = lds_ld128(pb + (mb * 64 + l) * 16);
+      if constexpr (S::GROUP) {
         // wave w's channels are group w: P[h][j] * scale[j][w] (elements 0..3 of
         // the operand are rows 4lg .. 4lg+3, elements 4..7 rows 16+4lg .. 16+4lg+3)
-        const lds_char* rw = rsc + 4 * (((tt & 1) * S8::G + w) * kTileRows + 4 * lg);
+        const lds_char* rw = rsc_buf(i) + 4 * (wr * kTileRows + 4 * lg);
         const f32x4 sa = *(const __attribute__((address_space(3))) f32x4*)rw;
         const f32x4 sb = *(const __attribute__((address_space(3))) f32x4*)(rw + 64);
 #pragma unroll
         for (int mb = 0; mb < 4; mb++) pa[mb] = scale_bf16x8(pa[mb], sa, sb);
-      }
-
-      // O[64 heads x 128 ch] += P[64 x 32] . V[32 x 128]; V reads run two n-blocks ahead
-      constexpr int VPF = 2;
-      s16x4 vr[VPF + 1][2];
-#pragma unroll
-      for (int nb = 0; nb < VPF; nb++) {
-        vr[nb][0] = lds_read_tr16(tb + vbase[0][nb & 3] + 4096 * (nb >> 2));
-        vr[nb][1] = lds_read_tr16(tb + vbase[1][nb & 3] + 4096 * (nb >> 2));
       }
 #pragma unroll
       for (int nb = 0; nb < 8; nb++) {
@@ -529,8 +586,8 @@ smla_attn_kernel(KParams p) {
         const s16x4 v1 = vr[nb % (VPF + 1)][1];
         if (nb + VPF < 8) {
           const int n2 = nb + VPF;
-          vr[n2 % (VPF + 1)][0] = lds_read_tr16(tb + vbase[0][n2 & 3] + 4096 * (n2 >> 2));
-          vr[n2 % (VPF + 1)][1] = lds_read_tr16(tb + vbase[1][n2 & 3] + 4096 * (n2 >> 2));
+          vr[n2 % (VPF + 1)][0] = lds_read_tr16(lb + vbase[0][n2 & 3] + 4096 * (n2 >> 2));
+          vr[n2 % (VPF + 1)][1] = lds_read_tr16(lb + vbase[1][n2 & 3] + 4096 * (n2 >> 2));
         }
         __builtin_amdgcn_sched_barrier(0);
         const bf16x8 bv = concat_bf16x4(v0, v1);
@@ -538,117 +595,74 @@ smla_attn_kernel(KParams p) {
         for (int mb = 0; mb < 4; mb++) O[mb][nb] = mfma16x16x32(pa[mb], bv, O[mb][nb]);
         __builtin_amdgcn_sched_barrier(0);
       }
-    }
-  };
+    };
 
-  // The first tile copies go out before Q is loaded, so the two latencies
-  // overlap (the first wait on Q also covers those copies).
-  issue_first();
-  // ---- Q^T as the B operand of 16x16x32: lane holds head hb + 32hg + 16nbq + li,
-  //      channels 32ks + 8lg .. +8 (ks < 16 latent, ks >= 16 rope)
-  //      The 16 latent k-steps stay in registers; the rope k-steps (D = 576) are
-  //      staged in LDS in the same lane layout and read once per tile.
+    // one pass over the tiles, the same barriers as s_pass. Tiles 0 and 1 are
+    // copied (and tile 0 converted) before the pass's first barrier.
+    auto o_pass = [&](const bool full, const bool issued) {
 #pragma unroll
-  for (int nbq = 0; nbq < 2; nbq++) {
-    const int head = hb + 32 * hg + 16 * nbq + li;
-    const bool valid = head < H;
-    const int hq = valid ? head : 0;
-    const uint16_t* qn = p.q_nope + t * p.qn_st + hq * p.qn_sh + 8 * lg;
+      for (int mb = 0; mb < 4; mb++)
 #pragma unroll
-    for (int ks = 0; ks < kLatKS; ks++) q[nbq][ks] = *(const bf16x8*)(qn + 32 * ks);
-    if (!valid) {
-#pragma unroll
-      for (int ks = 0; ks < kLatKS; ks++) q[nbq][ks] = (bf16x8){};
-    }
-    if (QKS > kLatKS) {
-      const uint16_t* qr = p.q_rope + t * p.qr_st + hq * p.qr_sh + 8 * lg;
-#pragma unroll
-      for (int ks = kLatKS; ks < QKS; ks++) {
-        bf16x8 v = *(const bf16x8*)(qr + 32 * (ks - kLatKS));
-        if (!valid) v = (bf16x8){};
-        lds_st128(qrope + (((w * 2 + nbq) * (QKS - kLatKS) + (ks - kLatKS)) * 64 + l) * 16, v);
+        for (int nb = 0; nb < 8; nb++) O[mb][nb] = (f32x4){};
+      if (!issued) {
+        if (ntiles > 0) issue_tile(0);
+        if (ntiles > 1) issue_tile(1);
       }
+      if (ntiles > 0) {
+        wait_tiles(ntiles > 1 ? 1 : 0);                     // tile 0 has landed
+        convert_tile(0);
+      }
+      lds_barrier();                                       // pass start
+      for (int i = 0; i <= ntiles; i++) {
+        if (i + 2 < ntiles) issue_tile(i + 2);
+        if (full && i == 0) lds_barrier();                 // matches the S-waves' reference exchange
+        if (full && i >= 1) pv(i - 1);
+        if (i + 1 < ntiles) {
+          wait_tiles(i + 2 < ntiles ? 1 : 0);             // tile i+1 has landed
+          convert_tile(i + 1);
+        }
+        lds_barrier();
+      }
+    };
+
+    for (int attempt = 0; attempt < 2; attempt++) {
+      o_pass(true, false);
+      if (!s_flag) break;                                  // uniform (after the pass's last barrier)
+      o_pass(false, false);
+      lds_barrier();                                       // matches the S-waves' final maximum exchange
     }
-  }
 
-
-  for (int attempt = 0; attempt < 2; attempt++) {
+    // ---- epilogue (O side)
+    lds_barrier();                                         // E1: row sums written
+    lds_barrier();                                         // E2: inverse sums written
+    // Stage the normalised O block [64 heads][512 ch] as bf16 in latent buffers
+    // 0-1 (idle now), then all waves write whole 16-byte chunks. O lane layout:
+    // m-block mb, n-block nb: head 16mb + 4lg + r, channel 128w + 16nb + li. Two
+    // heads of one channel are rounded together (v_cvt_pk_bf16_f32). Staged row
+    // h, byte b sits at h*1024 + (b ^ (((h >> 2) & 3) << 5)): the 4 head groups
+    // of one store instruction fall in different banks.
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int mb = 0; mb < 4; mb++)
+    for (int mb = 0; mb < 4; mb++) {
 #pragma unroll
-      for (int nb = 0; nb < 8; nb++) O[mb][nb] = (f32x4){};
-    l_lane[0] = l_lane[1] = 0.0f;
-    float unused[2] = {-INFINITY, -INFINITY};
-    run_pass(true, unused, attempt == 0);
-    lds_barrier();
-    if (!s_flag) break;                                    // uniform
-    // exact per-head maximum, then the full pass again
-    float mx_all[2] = {-INFINITY, -INFINITY};
-    run_pass(false, mx_all, false);
-    wg_max(mx_all);
-    m_ref[0] = mx_all[0];
-    m_ref[1] = mx_all[1];
-    if (threadIdx.x == 0) s_flag = 0;
-    lds_barrier();
-  }
-
-  // ---- epilogue: row sums, normalise, LSE, write
+      for (int rp = 0; rp < 2; rp++) {
+        const int h0 = 16 * mb + 4 * lg + 2 * rp;
+        const float sc0 = s_inv[h0], sc1 = s_inv[h0 + 1];
 #pragma unroll
-  for (int nbq = 0; nbq < 2; nbq++) {
-    float v = l_lane[nbq];
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    l_lane[nbq] = v;
-  }
-  if (lg == 0) {
-    s_l[w * 32 + li] = l_lane[0];
-    s_l[w * 32 + 16 + li] = l_lane[1];
-  }
-  lds_barrier();             // LDS-only barriers from here on: stores are never waited for
-  if (rh == 0 && lg == 0) {
-#pragma unroll
-    for (int nbq = 0; nbq < 2; nbq++) {
-      const float lt = s_l[w * 32 + 16 * nbq + li] + s_l[(w ^ 2) * 32 + 16 * nbq + li];
-      const int hl = 32 * hg + 16 * nbq + li;        // head within the block
-      s_inv[hl] = (lt > 0.0f) ? p.out_mult / lt : 0.0f;
-      const float lse_v = (lt > 0.0f) ? (m_ref[nbq] + log2f(lt)) * 0.69314718055994531f : -INFINITY;
-      const int head = hb + hl;
-      if (head < H) {
-        if (p.splits == 1) {
-          if (p.lse) p.lse[(int64_t)t * p.lse_st + head] = lse_v;
-        } else {
-          p.part_lse[((int64_t)split * T + t) * H + head] = lse_v;
+        for (int nb = 0; nb < 8; nb++) {
+          const int off = (2 * (128 * wr + 16 * nb + li)) ^ (lg << 5);
+          const f32x2 v = {O[mb][nb][2 * rp] * sc0, O[mb][nb][2 * rp + 1] * sc1};
+          const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+          *(__attribute__((address_space(3))) uint16_t*)(lat + h0 * 1024 + off) = (uint16_t)pk;
+          *(__attribute__((address_space(3))) uint16_t*)(lat + (h0 + 1) * 1024 + off) = (uint16_t)(pk >> 16);
         }
       }
     }
+    lds_barrier();                                         // E3
   }
-  lds_barrier();
-  // Stage the normalised O block [64 heads][512 ch] as bf16 in the (now idle)
-  // tile buffers, then write whole 16-byte chunks. O lane layout: m-block mb,
-  // n-block nb: head 16mb + 4lg + r, channel 128w + 16nb + li. Two heads of one
-  // channel are rounded together (v_cvt_pk_bf16_f32). Staged row h, byte b
-  // sits at h*1024 + (b ^ (((h >> 2) & 3) << 5)): the 4 head groups of one
-  // store instruction fall in different banks.
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  lds_char* ostage = tiles;
-#pragma unroll
-  for (int mb = 0; mb < 4; mb++) {
-#pragma unroll
-    for (int rp = 0; rp < 2; rp++) {
-      const int h0 = 16 * mb + 4 * lg + 2 * rp;
-      const float sc0 = s_inv[h0], sc1 = s_inv[h0 + 1];
-#pragma unroll
-      for (int nb = 0; nb < 8; nb++) {
-        const int off = (2 * (128 * w + 16 * nb + li)) ^ (lg << 5);
-        const f32x2 v = {O[mb][nb][2 * rp] * sc0, O[mb][nb][2 * rp + 1] * sc1};
-        const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-        *(__attribute__((address_space(3))) uint16_t*)(ostage + h0 * 1024 + off) = (uint16_t)pk;
-        *(__attribute__((address_space(3))) uint16_t*)(ostage + (h0 + 1) * 1024 + off) = (uint16_t)(pk >> 16);
-      }
-    }
-  }
-  lds_barrier();
+
+  // ---- all waves: write the staged block
   uint16_t* dst_base;
   int64_t dst_sh;
   if (p.splits == 1) {
@@ -660,11 +674,11 @@ smla_attn_kernel(KParams p) {
   }
   const int hmax = min(64, H - hb);
 #pragma unroll
-  for (int k = 0; k < 16; k++) {
-    const int id = k * 256 + threadIdx.x;
+  for (int k = 0; k < 8; k++) {
+    const int id = k * 512 + threadIdx.x;
     const int hl = id >> 6, c16 = id & 63;
     if (hl < hmax) {
-      const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(ostage + hl * 1024 + ((16 * c16) ^ (((hl >> 2) & 3) << 5)));
+      const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(lat + hl * 1024 + ((16 * c16) ^ (((hl >> 2) & 3) << 5)));
       *(u32x4*)(dst_base + (int64_t)hl * dst_sh + 8 * c16) = v;
     }
   }
@@ -740,7 +754,7 @@ size_t workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t topk, int3
 
 template <int D, int FMT>
 static void launch_kernel(const KParams& kp, int grid, hipStream_t stream) {
-  smla_attn_kernel<D, FMT><<<grid, 256, 0, stream>>>(kp);
+  smla_attn_kernel<D, FMT><<<grid, 512, 0, stream>>>(kp);
 }
 
 hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, bool longest_first,
