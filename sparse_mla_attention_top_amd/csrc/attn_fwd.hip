@@ -70,10 +70,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // Reference maximum policy. O and the running sum are accumulated against a
 // per-head reference m (base-2 units) fixed at the first tile; p = 2^(t - m)
-// stays finite in bf16/fp32 while t - m <= 64. If a later score exceeds m + 64
-// the workgroup restarts: a max-only pass finds the exact per-head maximum,
-// then the full pass runs with it.
-constexpr float kRefHeadroom = 64.0f;
+// stays finite in bf16/fp32 while t - m <= 64. If a row sum of a pass exceeds
+// 2^64 (so some later score may exceed m + 64) or is not finite, the workgroup
+// restarts: a max-only pass finds the exact per-head maximum, then the full
+// pass runs with it.
+constexpr float kRefLimit = 18446744073709551616.0f;    // 2^64
 constexpr int kLatKS = kDLatent / 32;                  // k-steps over the 512 latent channels
 constexpr int kLatBytes = kTileRows * kDLatent * 2;    // bf16 latent part of a tile (32 KB)
 constexpr int kRopeBytes = kTileRows * 64 * 2;         // bf16 rope part of a tile (4 KB)
@@ -246,6 +247,8 @@ smla_attn_kernel(KParams p) {
     }
     // complete here, so that the compiler puts no wait on the Q registers inside the loop
     wait_vmcnt<0>();
+    // the S-wave's MFMAs go first on its SIMD; the O-wave's fill the softmax time
+    __builtin_amdgcn_s_setprio(2);
 
     // K reads (A operand of 16x16x32): row 16rh + li, chunk 4ks + lg; k-steps
     // 0..15 in the latent buffer at kbase[ks & 1] + 4096 (ks >> 1), 16..17 in
@@ -254,12 +257,13 @@ smla_attn_kernel(KParams p) {
 #pragma unroll
     for (int j = 0; j < 2; j++) kbase[j] = tile_pos(16 * rh + li, 4 * j + lg);
 
-    // S^T[16 rows x 32 heads] of the wave for tile i, base-2 units, masked. Lane
-    // holds rows 16rh + 4lg + r (r = 0..3) of heads 32hg + 16nbq + li. Group
-    // format: the k-steps of channel group g = ks / 4 accumulate apart; each
-    // group's partial sums are scaled by the rows' group scales and added into
-    // t0 / t1 two k-steps into the next group (when its MFMAs are done).
-    auto scores = [&](int i, uint32_t vmask, float (&tv)[2][4]) {
+    // S^T[16 rows x 32 heads] of the wave for tile i (unscaled sums). Lane holds
+    // rows 16rh + 4lg + r (r = 0..3) of heads 32hg + 16nbq + li. Group
+    // format: the k-steps of channel group g = ks / 4 accumulate apart; at the
+    // end of a group its partial sums are scaled by the rows' group scales and
+    // added into t0 / t1 (the wait for those MFMAs is covered by the O-wave on
+    // the same SIMD).
+    auto scores = [&](int i, f32x4& r0, f32x4& r1) {
       const lds_char* lb = lat_buf(i);
       const lds_char* rb = rope_buf(i);
       auto kaddr = [&](auto ks_c) -> const lds_char* {
@@ -268,10 +272,10 @@ smla_attn_kernel(KParams p) {
         else return rb + kbase[ks & 1] + 4096 * (ks >> 1) - kLatBytes;
       };
       f32x4 s0 = {}, s1 = {}, s2 = {}, s3 = {};   // even / odd k-steps: 4 independent chains
-      f32x4 t0 = {}, t1 = {}, o0 = {}, o1 = {}, o2 = {}, o3 = {}, osc = {};
+      f32x4 t0 = {}, t1 = {};
       const lds_char* rs = rsc_buf(i) + 4 * (16 * rh + 4 * lg);
       (void)rs;
-      constexpr int PF = S::GROUP ? 4 : 6;        // K operand reads kept in flight
+      constexpr int PF = S::GROUP ? 2 : 6;        // K operand reads kept in flight
       bf16x8 a[PF];
       static_for<PF>([&](auto ks_c) { a[decltype(ks_c)::value] = lds_ld128(kaddr(ks_c)); });
       static_for<QKS>([&](auto ks_c) {
@@ -279,32 +283,25 @@ smla_attn_kernel(KParams p) {
         const bf16x8 cur = a[ks % PF];
         if constexpr (ks + PF < QKS) a[ks % PF] = lds_ld128(kaddr(std::integral_constant<int, ks + PF>{}));
         if constexpr (S::GROUP && (ks & 3) == 0 && ks > 0) {
-          // group ks/4 - 1 is complete: keep its chains and their scales, start afresh
-          o0 = s0; o1 = s1; o2 = s2; o3 = s3;
+          // group ks/4 - 1 is complete: scale and add it, start afresh
+          const f32x4 gsc = *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * (ks / 4 - 1));
+          t0 += gsc * (s0 + s2);
+          t1 += gsc * (s1 + s3);
           s0 = (f32x4){}; s1 = (f32x4){}; s2 = (f32x4){}; s3 = (f32x4){};
-          osc = *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * (ks / 4 - 1));
         }
         __builtin_amdgcn_sched_barrier(0);          // keep the read-ahead ahead of the MFMAs
         const bf16x8 b0 = q[0][ks], b1 = q[1][ks];
-        if constexpr ((ks & 1) == 0) {
+        if constexpr ((ks & 1) == 0 || S::GROUP) {        // group format: two chains (registers)
           s0 = mfma16x16x32(cur, b0, s0);
           s1 = mfma16x16x32(cur, b1, s1);
         } else {
           s2 = mfma16x16x32(cur, b0, s2);
           s3 = mfma16x16x32(cur, b1, s3);
         }
-        if constexpr (S::GROUP && (ks & 3) == 2 && ks > 4) {
-          t0 += osc * (o0 + o2);
-          t1 += osc * (o1 + o3);
-        }
         __builtin_amdgcn_sched_barrier(0);
       });
       if constexpr (S::GROUP) {
         constexpr int gl = (QKS - 1) / 4;               // last group
-        if constexpr ((QKS - 1) % 4 < 2 && gl > 0) {    // the group before it was not folded yet
-          t0 += osc * (o0 + o2);
-          t1 += osc * (o1 + o3);
-        }
         const f32x4 lsc = *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * gl);
         s0 = t0 + lsc * (s0 + s2);
         s1 = t1 + lsc * (s1 + s3);
@@ -312,12 +309,8 @@ smla_attn_kernel(KParams p) {
         s0 += s2;
         s1 += s3;
       }
-#pragma unroll
-      for (int r = 0; r < 4; r++) {
-        const bool ok = (vmask >> (16 * rh + 4 * lg + r)) & 1;
-        tv[0][r] = ok ? s0[r] * p.scale_log2 : -INFINITY;
-        tv[1][r] = ok ? s1[r] * p.scale_log2 : -INFINITY;
-      }
+      r0 = s0;
+      r1 = s1;
     };
     // maximum over the workgroup's 32 rows (both row halves), per head; one
     // barrier, which the O-waves match
@@ -342,22 +335,37 @@ smla_attn_kernel(KParams p) {
     float l_lane[2] = {0.0f, 0.0f};
     bool have_ref = false;                                 // workgroup-uniform
 
+    // Scores in base-2 units, masked rows at -inf (for the maxima).
+    auto scaled = [&](const f32x4& r0, const f32x4& r1, uint32_t vmask, float (&tv)[2][4], float (&mx)[2]) {
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        const bool ok = (vmask >> (16 * rh + 4 * lg + r)) & 1;
+        tv[0][r] = ok ? r0[r] * p.scale_log2 : -INFINITY;
+        tv[1][r] = ok ? r1[r] * p.scale_log2 : -INFINITY;
+      }
+#pragma unroll
+      for (int nbq = 0; nbq < 2; nbq++)
+        mx[nbq] = fmaxf(fmaxf(tv[nbq][0], tv[nbq][1]), fmaxf(tv[nbq][2], tv[nbq][3]));
+    };
+
     // one pass over the tiles; full = softmax and P, otherwise only the
     // per-head maximum (into mx_all). Barriers: one per tile, plus the
-    // reference exchange in tile 0 of a full pass.
+    // reference exchange in tile 0 of a full pass. A full pass ends by
+    // flagging a rerun if a row sum left the range the reference guarantees
+    // (some p = 2^(t - m) above 2^64, or not finite).
     auto s_pass = [&](const bool full, float (&mx_all)[2]) {
       l_lane[0] = l_lane[1] = 0.0f;
-      lds_barrier();                                       // pass start: tiles 0 (and 1) are in LDS
+      lds_barrier();                                       // pass start: tile 0 is in LDS
       for (int i = 0; i <= ntiles; i++) {
         const bool have = i < ntiles;
+        f32x4 r0 = {}, r1 = {};
+        uint32_t vmask = 0;
         float tv[2][4];
         float mx[2] = {-INFINITY, -INFINITY};
         if (have) {
-          const uint32_t vmask = (uint32_t)__ballot((l < 32) ? (s_idx[i * kTileRows + l] >= 0) : 0);
-          scores(i, vmask, tv);
-#pragma unroll
-          for (int nbq = 0; nbq < 2; nbq++)
-            mx[nbq] = fmaxf(fmaxf(tv[nbq][0], tv[nbq][1]), fmaxf(tv[nbq][2], tv[nbq][3]));
+          vmask = (uint32_t)__ballot((l < 32) ? (s_idx[i * kTileRows + l] >= 0) : 0);
+          scores(i, r0, r1);
+          if (!full || i == 0) scaled(r0, r1, vmask, tv, mx);
         }
         if (!full) {
           mx_all[0] = fmaxf(mx_all[0], mx[0]);
@@ -366,28 +374,36 @@ smla_attn_kernel(KParams p) {
           continue;
         }
         if (i == 0) {                                      // the reference: tile 0's maximum
-          float m0[2] = {mx[0], mx[1]};                    // (the exchange barrier always runs:
-          wg_max(m0);                                      //  the O-waves match it)
+          wg_max(mx);                                      // (its barrier always runs: the O-waves match it)
           if (!have_ref) {                                 // a rerun keeps the exact maximum
-            m_ref[0] = m0[0];
-            m_ref[1] = m0[1];
+            m_ref[0] = mx[0];
+            m_ref[1] = mx[1];
             have_ref = true;
           }
         }
         if (have) {
-          if (fmaxf(mx[0] - m_ref[0], mx[1] - m_ref[1]) > kRefHeadroom) s_flag = 1;
           lds_char* pb = pbuf + (i & 1) * (4 * 64 * 16);
+          const bool all_valid = vmask == 0xffffffffu;    // uniform
 #pragma unroll
           for (int nbq = 0; nbq < 2; nbq++) {
-            const float msub = (m_ref[nbq] == -INFINITY) ? 0.0f : m_ref[nbq];
+            const float nm = (m_ref[nbq] == -INFINITY) ? 0.0f : -m_ref[nbq];
+            const f32x4& rs = nbq ? r1 : r0;
             float pr[4];
 #pragma unroll
-            for (int r = 0; r < 4; r++) pr[r] = fast_exp2(tv[nbq][r] - msub);
+            for (int r = 0; r < 4; r++) pr[r] = fast_exp2(fmaf(rs[r], p.scale_log2, nm));
+            if (!all_valid) {
+#pragma unroll
+              for (int r = 0; r < 4; r++)
+                if (!((vmask >> (16 * rh + 4 * lg + r)) & 1)) pr[r] = 0.0f;
+            }
             l_lane[nbq] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
             const uint64_t pk = (uint64_t)pack_bf16x2(pr[0], pr[1]) | ((uint64_t)pack_bf16x2(pr[2], pr[3]) << 32);
             // A operand of m-block 2hg + nbq, elements 4rh .. 4rh+3
             lds_st64(pb + ((2 * hg + nbq) * 64 + l) * 16 + 8 * rh, pk);
           }
+        } else {
+          // end of the pass: 2^64 bounds every p while the reference holds
+          if (!(l_lane[0] <= kRefLimit) || !(l_lane[1] <= kRefLimit)) s_flag = 1;
         }
         lds_barrier();
       }
