@@ -108,8 +108,11 @@ struct Shape {
   static constexpr int ST_BYTES = ST_SC + (GROUP ? 4 * 256 : 0);
   static constexpr int NSTAGE = F8 ? 2 : 0;
   static constexpr int NRSC = GROUP ? 3 : 0;           // row-scale sets (tiles i-1, i, i+1)
-  // copy instructions per O-wave per tile
-  static constexpr int NDMA = F8 ? 4 + (ROPE ? 1 : 0) + (GROUP ? 1 : 0) : D / 64;
+  // copy instructions per wave per tile. FP8: latent segments 0-1, the rope
+  // part and the scales are copied (and converted) by the O-waves, latent
+  // segments 2-3 by the S-waves; bf16: all by the O-waves.
+  static constexpr int NDMA_O = F8 ? 2 + (ROPE ? 1 : 0) + (GROUP ? 1 : 0) : D / 64;
+  static constexpr int NDMA_S = F8 ? 2 : 0;
   static_assert(D == kDLatent || D == kDLatent + 64, "rope part must be 64 channels");
   static_assert(8 * G <= 64, "scales of 8 rows fit one instruction");
 };
@@ -121,7 +124,7 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 smla_attn_kernel(KParams p) {
   using S = Shape<D, FMT>;
   constexpr bool F8 = S::F8;
-  constexpr int QKS = S::QKS, NLAT = S::NLAT, NROPE = S::NROPE, NDMA = S::NDMA;
+  constexpr int QKS = S::QKS, NLAT = S::NLAT, NROPE = S::NROPE;
 
   __shared__ __attribute__((aligned(16))) char s_lat[NLAT * kLatBytes];
   __shared__ __attribute__((aligned(16))) char s_rope[(NROPE ? NROPE * kRopeBytes : 16)];
@@ -220,12 +223,142 @@ smla_attn_kernel(KParams p) {
   auto rope_buf = [&](int i) -> lds_char* { return rope + (NROPE ? (i % (NROPE ? NROPE : 1)) * kRopeBytes : 0); };
   auto rsc_buf = [&](int i) -> lds_char* { return rsc + (S::GROUP ? (i % (S::NRSC ? S::NRSC : 1)) * S::G * kTileRows * 4 : 0); };
 
+  // ---- tile copies (and FP8 conversion), shared by both roles
+  const int wu = __builtin_amdgcn_readfirstlane(wr);
+  const uint32_t kv_stride = (uint32_t)p.kv_row_stride;
+  const uint32_t lat_addr = (uint32_t)(uintptr_t)lat;
+  const uint32_t rope_addr = (uint32_t)(uintptr_t)rope;
+  const uint32_t stage_addr = (uint32_t)(uintptr_t)stage;
+  // bf16 cache: copy u of O-wave w fills block 4u + w of the tile (segment u,
+  // bytes 128u .. 128u+127, of rows 8w .. 8w+7; segment 8 is the rope part).
+  // Lane l loads row 8w + l/8, logical chunk (l & 7) ^ swz(row): the same row
+  // and column for every u, so one address per tile serves all copies
+  // through the immediate offset 128u.
+  const int drow = 8 * wu + (l >> 3);
+  const uint32_t dcol = (uint32_t)(16 * ((l & 7) ^ swz(drow)));
+  // FP8 cache: latent chunk l & 7 of row 8w + l/8 (segment u at offset 128u);
+  // rope chunk l & 3 of row 8w + l/4; scale l % G of row 8w + l/G.
+  const int srow = min(l / S::G, 7), sgrp = l % S::G;
+  struct Src {
+    const uint8_t* lat;
+    const uint8_t* rope;
+    const float* sc;
+  };
+  auto sources = [&](int i) -> Src {
+    Src s;
+    const int base = i * kTileRows + 8 * wu;
+    if constexpr (!F8) {
+      s.lat = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + (l >> 3)], 0) * kv_stride + dcol);
+    } else {
+      s.lat = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + (l >> 3)], 0) * kv_stride + 16 * (l & 7));
+      if constexpr (S::ROPE)
+        s.rope = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + ((l >> 2) & 7)], 0) * kv_stride + kDLatent + 16 * (l & 3));
+      if constexpr (S::GROUP)
+        s.sc = p.group_scales + ((uint64_t)(uint32_t)max(s_idx[base + srow], 0) * S::G + sgrp);
+    }
+    return s;
+  };
+  // FP8 latent segment u of this wave's rows of tile i -> stage
+  auto issue_seg = [&](const Src& s, int i, auto u_c) {
+    constexpr int u = decltype(u_c)::value;
+    const uint32_t sb = stage_addr + (i % (S::NSTAGE ? S::NSTAGE : 1)) * S::ST_BYTES;
+    dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(sb + (4 * u + wu) * 1024));
+  };
+  // O-wave copies of tile i
+  auto issue_tile_o = [&](int i) {
+    const Src s = sources(i);
+    if constexpr (!F8) {
+      static_for<S::NDMA_O>([&](auto u_c) {
+        constexpr int u = decltype(u_c)::value;
+        if constexpr (u < 8)
+          dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(lat_addr + (i % NLAT) * kLatBytes + (4 * u + wu) * 1024));
+        else
+          dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(rope_addr + (i % (NROPE ? NROPE : 1)) * kRopeBytes + wu * 1024));
+      });
+    } else {
+      issue_seg(s, i, std::integral_constant<int, 0>{});
+      issue_seg(s, i, std::integral_constant<int, 1>{});
+      const uint32_t sb = stage_addr + (i % (S::NSTAGE ? S::NSTAGE : 1)) * S::ST_BYTES;
+      if constexpr (S::ROPE) {
+        if (l < 32) dma_16b<0>(s.rope, __builtin_amdgcn_readfirstlane(sb + S::ST_ROPE + wu * 512));
+      }
+      if constexpr (S::GROUP) {
+        if (l < 8 * S::G) dma_4b(s.sc, __builtin_amdgcn_readfirstlane(sb + S::ST_SC + wu * 256));
+      }
+    }
+  };
+  // S-wave copies of tile i (FP8: latent segments 2-3)
+  auto issue_tile_s = [&](int i) {
+    if constexpr (F8) {
+      const Src s = sources(i);
+      issue_seg(s, i, std::integral_constant<int, 2>{});
+      issue_seg(s, i, std::integral_constant<int, 3>{});
+    }
+  };
+  // FP8: staged latent segment u of this wave's rows of tile i -> bf16 tile i
+  // (exact E4M3 values)
+  auto convert_seg = [&](int i, auto u_c) {
+    constexpr int u = decltype(u_c)::value;
+    const lds_char* st = stage + (i % (S::NSTAGE ? S::NSTAGE : 1)) * S::ST_BYTES;
+    lds_char* lb = lat_buf(i);
+    const int r = 8 * wr + (l >> 3);
+    const u32x4 raw = *(const __attribute__((address_space(3))) u32x4*)(st + (4 * u + wr) * 1024 + 16 * l);
+    u32x4 lo, hi;
+    e4m3x16_to_bf16<false>(raw, 1.0f, lo, hi);
+    const int k = 8 * u + (l & 7);
+    *(__attribute__((address_space(3))) u32x4*)(lb + tile_pos(r, 2 * k)) = lo;
+    *(__attribute__((address_space(3))) u32x4*)(lb + tile_pos(r, 2 * k + 1)) = hi;
+  };
+  // O-wave conversion of tile i: segments 0-1, the rope part, and (group
+  // format) all the rows' scales -> row-scale set i ([group][row])
+  auto convert_tile_o = [&](int i) {
+    if constexpr (F8) {
+      const lds_char* st = stage + (i % (S::NSTAGE ? S::NSTAGE : 1)) * S::ST_BYTES;
+      convert_seg(i, std::integral_constant<int, 0>{});
+      convert_seg(i, std::integral_constant<int, 1>{});
+      if constexpr (S::GROUP) {
+        const int r = 8 * wr + (l >> 3);
+        static_for<4>([&](auto u_c) {
+          constexpr int u = decltype(u_c)::value;
+          const float sc = *(const __attribute__((address_space(3))) float*)(st + S::ST_SC + wr * 256 + 4 * ((l >> 3) * S::G + u));
+          *(__attribute__((address_space(3))) float*)(rsc_buf(i) + 4 * (u * kTileRows + r)) = sc;
+        });
+      }
+      if constexpr (S::ROPE) {
+        if (l < 32) {
+          const int r2 = 8 * wr + (l >> 2);
+          const u32x4 raw = *(const __attribute__((address_space(3))) u32x4*)(st + S::ST_ROPE + wr * 512 + 16 * l);
+          if constexpr (S::GROUP) {
+            const float sc = *(const __attribute__((address_space(3))) float*)(st + S::ST_SC + wr * 256 + 4 * ((l >> 2) * S::G + 4));
+            *(__attribute__((address_space(3))) float*)(rsc_buf(i) + 4 * (4 * kTileRows + r2)) = sc;
+          }
+          u32x4 lo, hi;
+          e4m3x16_to_bf16<false>(raw, 1.0f, lo, hi);
+          const int k = (l & 3);                            // chunks 64 + 2k, 65 + 2k: rope buffer
+          lds_char* rb = rope_buf(i);
+          *(__attribute__((address_space(3))) u32x4*)(rb + tile_pos(r2, 64 + 2 * k) - kLatBytes) = lo;
+          *(__attribute__((address_space(3))) u32x4*)(rb + tile_pos(r2, 65 + 2 * k) - kLatBytes) = hi;
+        }
+      }
+    }
+  };
+  // S-wave conversion of tile i (FP8: segments 2-3)
+  auto convert_tile_s = [&](int i) {
+    if constexpr (F8) {
+      convert_seg(i, std::integral_constant<int, 2>{});
+      convert_seg(i, std::integral_constant<int, 3>{});
+    }
+  };
+
   if (is_s) {
     // ======================================================================
     // S-waves: QK^T, softmax, P
     // ======================================================================
     // Q^T as the B operand of 16x16x32: lane holds head hb + 32hg + 16nbq + li,
     // channels 32ks + 8lg .. +8 (ks < 16 latent, ks >= 16 rope). Heads past h are zero.
+    // FP8: this wave's copies of tiles 0 and 1 go out before Q
+    if (ntiles > 0) issue_tile_s(0);
+    if (ntiles > 1) issue_tile_s(1);
     bf16x8 q[2][QKS];
 #pragma unroll
     for (int nbq = 0; nbq < 2; nbq++) {
@@ -247,8 +380,6 @@ smla_attn_kernel(KParams p) {
     }
     // complete here, so that the compiler puts no wait on the Q registers inside the loop
     wait_vmcnt<0>();
-    // the S-wave's MFMAs go first on its SIMD; the O-wave's fill the softmax time
-    __builtin_amdgcn_s_setprio(2);
 
     // K reads (A operand of 16x16x32): row 16rh + li, chunk 4ks + lg; k-steps
     // 0..15 in the latent buffer at kbase[ks & 1] + 4096 (ks >> 1), 16..17 in
@@ -353,11 +484,22 @@ smla_attn_kernel(KParams p) {
     // reference exchange in tile 0 of a full pass. A full pass ends by
     // flagging a rerun if a row sum left the range the reference guarantees
     // (some p = 2^(t - m) above 2^64, or not finite).
-    auto s_pass = [&](const bool full, float (&mx_all)[2]) {
+    auto s_pass = [&](const bool full, float (&mx_all)[2], const bool issued) {
       l_lane[0] = l_lane[1] = 0.0f;
+      if constexpr (F8) {                                  // this wave's share of tile 0
+        if (!issued) {
+          if (ntiles > 0) issue_tile_s(0);
+          if (ntiles > 1) issue_tile_s(1);
+        }
+        if (ntiles > 0) {
+          if (ntiles > 1) wait_vmcnt<S::NDMA_S>(); else wait_vmcnt<0>();
+          convert_tile_s(0);
+        }
+      }
       lds_barrier();                                       // pass start: tile 0 is in LDS
       for (int i = 0; i <= ntiles; i++) {
         const bool have = i < ntiles;
+        if (F8 && i + 2 < ntiles) issue_tile_s(i + 2);
         f32x4 r0 = {}, r1 = {};
         uint32_t vmask = 0;
         float tv[2][4];
@@ -367,9 +509,16 @@ smla_attn_kernel(KParams p) {
           scores(i, r0, r1);
           if (!full || i == 0) scaled(r0, r1, vmask, tv, mx);
         }
+        auto convert_next = [&]() {                        // this wave's share of tile i+1
+          if (F8 && i + 1 < ntiles) {
+            if (i + 2 < ntiles) wait_vmcnt<S::NDMA_S>(); else wait_vmcnt<0>();
+            convert_tile_s(i + 1);
+          }
+        };
         if (!full) {
           mx_all[0] = fmaxf(mx_all[0], mx[0]);
           mx_all[1] = fmaxf(mx_all[1], mx[1]);
+          convert_next();
           lds_barrier();
           continue;
         }
@@ -405,17 +554,18 @@ smla_attn_kernel(KParams p) {
           // end of the pass: 2^64 bounds every p while the reference holds
           if (!(l_lane[0] <= kRefLimit) || !(l_lane[1] <= kRefLimit)) s_flag = 1;
         }
+        convert_next();
         lds_barrier();
       }
     };
 
     for (int attempt = 0; attempt < 2; attempt++) {
       float unused[2] = {-INFINITY, -INFINITY};
-      s_pass(true, unused);
+      s_pass(true, unused, attempt == 0);
       if (!s_flag) break;                                  // uniform (after the pass's last barrier)
       // exact per-head maximum, then the full pass again
       float mx_all[2] = {-INFINITY, -INFINITY};
-      s_pass(false, mx_all);
+      s_pass(false, mx_all, false);
       wg_max(mx_all);
       m_ref[0] = mx_all[0];
       m_ref[1] = mx_all[1];
@@ -458,107 +608,6 @@ smla_attn_kernel(KParams p) {
     // ======================================================================
     // O-waves: tile copies (and FP8 conversion), P.V
     // ======================================================================
-    const int wu = __builtin_amdgcn_readfirstlane(wr);
-    const uint32_t kv_stride = (uint32_t)p.kv_row_stride;
-    const uint32_t lat_addr = (uint32_t)(uintptr_t)lat;
-    const uint32_t rope_addr = (uint32_t)(uintptr_t)rope;
-    const uint32_t stage_addr = (uint32_t)(uintptr_t)stage;
-    // bf16 cache: copy u of wave w fills block 4u + w of the tile (segment u,
-    // bytes 128u .. 128u+127, of rows 8w .. 8w+7; segment 8 is the rope part).
-    // Lane l loads row 8w + l/8, logical chunk (l & 7) ^ swz(row): the same row
-    // and column for every u, so one address per tile serves all copies
-    // through the immediate offset 128u.
-    const int drow = 8 * wu + (l >> 3);
-    const uint32_t dcol = (uint32_t)(16 * ((l & 7) ^ swz(drow)));
-    // FP8 cache: latent chunk l & 7 of row 8w + l/8; rope chunk l & 3 of row
-    // 8w + l/4; scale l % G of row 8w + l/G.
-    const int srow = min(l / S::G, 7), sgrp = l % S::G;
-    struct Src {
-      const uint8_t* lat;
-      const uint8_t* rope;
-      const float* sc;
-    };
-    auto sources = [&](int i) -> Src {
-      Src s;
-      const int base = i * kTileRows + 8 * wu;
-      if constexpr (!F8) {
-        s.lat = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + (l >> 3)], 0) * kv_stride + dcol);
-      } else {
-        s.lat = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + (l >> 3)], 0) * kv_stride + 16 * (l & 7));
-        if constexpr (S::ROPE)
-          s.rope = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + ((l >> 2) & 7)], 0) * kv_stride + kDLatent + 16 * (l & 3));
-        if constexpr (S::GROUP)
-          s.sc = p.group_scales + ((uint64_t)(uint32_t)max(s_idx[base + srow], 0) * S::G + sgrp);
-      }
-      return s;
-    };
-    // copy instruction u (0 .. NDMA-1) of tile i
-    auto issue_one = [&](const Src& s, int i, auto u_c) {
-      constexpr int u = decltype(u_c)::value;
-      if constexpr (!F8) {
-        if constexpr (u < 8) {
-          dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(lat_addr + (i % NLAT) * kLatBytes + (4 * u + wu) * 1024));
-        } else {
-          dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(rope_addr + (i % (NROPE ? NROPE : 1)) * kRopeBytes + wu * 1024));
-        }
-      } else {
-        const uint32_t sb = stage_addr + (i % S::NSTAGE) * S::ST_BYTES;
-        if constexpr (u < 4) {
-          dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(sb + (4 * u + wu) * 1024));
-        } else if constexpr (u == 4 && S::ROPE) {
-          if (l < 32) dma_16b<0>(s.rope, __builtin_amdgcn_readfirstlane(sb + S::ST_ROPE + wu * 512));
-        } else {
-          if (l < 8 * S::G) dma_4b(s.sc, __builtin_amdgcn_readfirstlane(sb + S::ST_SC + wu * 256));
-        }
-      }
-    };
-    auto issue_tile = [&](int i) {
-      const Src s = sources(i);
-      static_for<NDMA>([&](auto u_c) { issue_one(s, i, u_c); });
-    };
-    // wait until at most n (0 or 1) tiles' copies of this wave are outstanding
-    auto wait_tiles = [&](int n) {
-      if (n >= 1) wait_vmcnt<NDMA>(); else wait_vmcnt<0>();
-    };
-    // FP8: this wave's rows of staged tile i -> bf16 tile i (exact E4M3 values);
-    // group format: the rows' scales -> row-scale set i ([group][row]).
-    auto convert_tile = [&](int i) {
-      if constexpr (F8) {
-        const lds_char* st = stage + (i % S::NSTAGE) * S::ST_BYTES;
-        lds_char* lb = lat_buf(i);
-        const int r = 8 * wr + (l >> 3);
-        static_for<4>([&](auto u_c) {
-          constexpr int u = decltype(u_c)::value;
-          const u32x4 raw = *(const __attribute__((address_space(3))) u32x4*)(st + (4 * u + wr) * 1024 + 16 * l);
-          if constexpr (S::GROUP) {
-            const float sc = *(const __attribute__((address_space(3))) float*)(st + S::ST_SC + wr * 256 + 4 * ((l >> 3) * S::G + u));
-            *(__attribute__((address_space(3))) float*)(rsc_buf(i) + 4 * (u * kTileRows + r)) = sc;
-          }
-          u32x4 lo, hi;
-          e4m3x16_to_bf16<false>(raw, 1.0f, lo, hi);
-          const int k = 8 * u + (l & 7);
-          *(__attribute__((address_space(3))) u32x4*)(lb + tile_pos(r, 2 * k)) = lo;
-          *(__attribute__((address_space(3))) u32x4*)(lb + tile_pos(r, 2 * k + 1)) = hi;
-        });
-        if constexpr (S::ROPE) {
-          if (l < 32) {
-            const int r2 = 8 * wr + (l >> 2);
-            const u32x4 raw = *(const __attribute__((address_space(3))) u32x4*)(st + S::ST_ROPE + wr * 512 + 16 * l);
-            if constexpr (S::GROUP) {
-              const float sc = *(const __attribute__((address_space(3))) float*)(st + S::ST_SC + wr * 256 + 4 * ((l >> 2) * S::G + 4));
-              *(__attribute__((address_space(3))) float*)(rsc_buf(i) + 4 * (4 * kTileRows + r2)) = sc;
-            }
-            u32x4 lo, hi;
-            e4m3x16_to_bf16<false>(raw, 1.0f, lo, hi);
-            const int k = (l & 3);                          // chunks 64 + 2k, 65 + 2k: rope buffer
-            lds_char* rb = rope_buf(i);
-            *(__attribute__((address_space(3))) u32x4*)(rb + tile_pos(r2, 64 + 2 * k) - kLatBytes) = lo;
-            *(__attribute__((address_space(3))) u32x4*)(rb + tile_pos(r2, 65 + 2 * k) - kLatBytes) = hi;
-          }
-        }
-      }
-    };
-
     // V transposing reads (B operand of P.V): in 16-lane group lg, lane li = 4e + q
     // reads row 4lg + e (then 16 + 4lg + e), channels 128w + 16nb + 4q .. +3,
     // at vbase[half][nb & 3] + 4096 (nb >> 2).
@@ -621,21 +670,21 @@ smla_attn_kernel(KParams p) {
 #pragma unroll
         for (int nb = 0; nb < 8; nb++) O[mb][nb] = (f32x4){};
       if (!issued) {
-        if (ntiles > 0) issue_tile(0);
-        if (ntiles > 1) issue_tile(1);
+        if (ntiles > 0) issue_tile_o(0);
+        if (ntiles > 1) issue_tile_o(1);
       }
       if (ntiles > 0) {
-        wait_tiles(ntiles > 1 ? 1 : 0);                     // tile 0 has landed
-        convert_tile(0);
+        if (ntiles > 1) wait_vmcnt<S::NDMA_O>(); else wait_vmcnt<0>();   // tile 0 has landed
+        convert_tile_o(0);
       }
       lds_barrier();                                       // pass start
       for (int i = 0; i <= ntiles; i++) {
-        if (i + 2 < ntiles) issue_tile(i + 2);
+        if (i + 2 < ntiles) issue_tile_o(i + 2);
         if (full && i == 0) lds_barrier();                 // matches the S-waves' reference exchange
         if (full && i >= 1) pv(i - 1);
         if (i + 1 < ntiles) {
-          wait_tiles(i + 2 < ntiles ? 1 : 0);             // tile i+1 has landed
-          convert_tile(i + 1);
+          if (i + 2 < ntiles) wait_vmcnt<S::NDMA_O>(); else wait_vmcnt<0>();   // tile i+1 has landed
+          convert_tile_o(i + 1);
         }
         lds_barrier();
       }
