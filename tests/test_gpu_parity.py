@@ -216,6 +216,26 @@ def test_deterministic_bitwise():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
 
 
+def test_split_workspace_reused_across_shapes():
+    """One caller-owned workspace serves decode calls of different shapes and
+    split counts: 4 splits with each token's workgroups on one XCD (8 tokens),
+    then 64 splits (the most a top-k of 2048 allows) with 3 tokens spread over
+    XCDs, then the first case again."""
+    say("split workspace reuse")
+    ca = I.random_case(T=8, h=128, d_rope=64, topk=1024, num_slots=3000, seed=15)
+    cb = I.random_case(T=3, h=64, d_rope=64, topk=2048, num_slots=5000, seed=16, lengths=[2048, 1500, 37])
+    need = max(smla.decode_workspace_size(8, 128, 1024, 4), smla.decode_workspace_size(3, 64, 2048, 64))
+    assert smla.decode_num_splits(3, 64, 2048, 64) == 64
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    for c, splits in ((ca, 4), (cb, 64), (ca, 4)):
+        q, kv, idx, ln = c.q.to(DEV), c.kv_src.to(DEV), c.indices.to(DEV), c.lengths.to(DEV)
+        o, l = smla.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, topk_length=ln,
+                               num_splits=splits, workspace=ws)
+        torch.cuda.synchronize()
+        compare(o, l, oracle_for(c.q, bits(c.kv_src), c.indices.numpy(), 0.07, c.lengths.numpy()),
+                f"ws splits={splits}")
+
+
 def test_strided_query_and_output_views():
     """q_nope / q_rope as views of one [T, h, 576] tensor and an output with a
     padded head stride."""
