@@ -257,7 +257,8 @@ def main() -> int:
     ms_per_step = dt / steps * 1e3
     tokens_per_s = T * steps / dt
 
-    # attention kernel duration: HIP events around the kernel, queue backed up first
+    # attention kernel duration: HIP events that the library hands to hipExtLaunchKernel, which
+    # sets them from the kernel's own start and end timestamps (queue backed up first)
     n_ev = min(steps, 120)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
     for a, b in evs:          # torch creates the HIP events on first record

@@ -181,9 +181,10 @@ int smla_cache_write(const void* kv_c, int64_t kv_c_stride, const void* k_pe, in
 /*
  * Profiling hook (not part of the computation). When set for the calling
  * thread, every following smla_decode_fwd / smla_prefill_fwd call records
- * `start` (a hipEvent_t) on its stream immediately before the main attention
- * kernel and `end` immediately after it, so the kernel's own duration can be
- * read with hipEventElapsedTime while the split combine is excluded. Pass
+ * the main attention kernel through hipExtLaunchKernel with `start` and
+ * `end` (hipEvent_t, created with timing): the events take that kernel's own
+ * start and end timestamps, so hipEventElapsedTime gives its duration (the
+ * split combine, a separate kernel, is excluded). Pass
  * NULL, NULL to clear. The events are owned by the caller.
  */
 int smla_set_timing_events(void* start, void* end);

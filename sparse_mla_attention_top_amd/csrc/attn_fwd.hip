@@ -24,6 +24,7 @@
 #include "smla_device.h"
 #include "smla_internal.h"
 
+#include <hip/hip_ext.h>
 #include <math.h>
 
 namespace smla {
@@ -63,9 +64,11 @@ __device__ __forceinline__ void lds_st64(lds_char* p, uint64_t v) {
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // Reference maximum policy. O and the running sum are accumulated against a
@@ -817,9 +820,18 @@ size_t workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t topk, int3
   return n * kDLatent * sizeof(uint16_t) + n * sizeof(float);
 }
 
+// With timing events the launch goes through hipExtLaunchKernel, which sets
+// the events from the kernel's own start and end timestamps.
 template <int D, int FMT>
-static void launch_kernel(const KParams& kp, int grid, hipStream_t stream) {
+static hipError_t launch_kernel(const KParams& kp, int grid, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  if (ev0 || ev1) {
+    KParams arg = kp;
+    void* args[] = {&arg};
+    return hipExtLaunchKernel((const void*)smla_attn_kernel<D, FMT>, dim3(grid), dim3(512), args, 0, stream,
+                              ev0, ev1, 0);
+  }
   smla_attn_kernel<D, FMT><<<grid, 512, 0, stream>>>(kp);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, bool longest_first,
@@ -855,19 +867,15 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
   }
   const int per_tok = kp.head_blocks * splits;
   const int grid = kp.xcd_group ? 8 * ((a.num_tokens + 7) / 8) * per_tok : a.num_tokens * per_tok;
-  if (a.ev_start) {
-    hipError_t er = hipEventRecord(a.ev_start, stream);
-    if (er != hipSuccess) return er;
-  }
   const bool rope = a.d_rope == 64;
+  const hipEvent_t e0 = a.ev_start, e1 = a.ev_end;
+  hipError_t e;
   switch (a.kv_format) {
-    case 0: rope ? launch_kernel<576, 0>(kp, grid, stream) : launch_kernel<512, 0>(kp, grid, stream); break;
-    case 1: rope ? launch_kernel<576, 1>(kp, grid, stream) : launch_kernel<512, 1>(kp, grid, stream); break;
-    case 2: rope ? launch_kernel<576, 2>(kp, grid, stream) : launch_kernel<512, 2>(kp, grid, stream); break;
+    case 0: e = rope ? launch_kernel<576, 0>(kp, grid, stream, e0, e1) : launch_kernel<512, 0>(kp, grid, stream, e0, e1); break;
+    case 1: e = rope ? launch_kernel<576, 1>(kp, grid, stream, e0, e1) : launch_kernel<512, 1>(kp, grid, stream, e0, e1); break;
+    case 2: e = rope ? launch_kernel<576, 2>(kp, grid, stream, e0, e1) : launch_kernel<512, 2>(kp, grid, stream, e0, e1); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && a.ev_end) e = hipEventRecord(a.ev_end, stream);
   if (e != hipSuccess || splits == 1) return e;
   const int64_t total = (int64_t)a.num_tokens * a.num_heads * (kDLatent / 8);
   smla_combine_kernel<<<(int)((total + 255) / 256), 256, 0, stream>>>(

@@ -67,6 +67,26 @@ def test_convert_invalid_corners_bitexact():
         assert (g == go).all() and (v == vo).all()
 
 
+@pytest.mark.parametrize("max_blocks", [4096, 4097, 9000])
+def test_convert_long_block_tables_bitexact(max_blocks):
+    """Block-table rows up to 4096 entries are staged in LDS, longer ones are
+    read entry by entry; both sides of that limit, with a top-k wider than
+    one pass of the kernel (2048 entries), invalid entries and a bad request."""
+    rng = np.random.default_rng(18 + max_blocks)
+    R, B, T, K = 3, 16, 9, 2500
+    bt = rng.permutation(R * max_blocks).reshape(R, max_blocks).astype(np.int32)
+    bt[1, ::7] = -1
+    req = rng.integers(0, R, T).astype(np.int32)
+    loc = rng.integers(-2, max_blocks * B + 5, (T, K)).astype(np.int32)
+    go, vo = O.convert_indices(req, bt, loc, B)
+    req[4] = R                     # outside [0, num_reqs): the kernel gives the row all -1
+    say(f"convert long table max_blocks={max_blocks}")
+    g, v = _gpu_convert(torch.from_numpy(req), torch.from_numpy(bt), torch.from_numpy(loc), B)
+    keep = np.arange(T) != 4
+    assert (g[keep] == go[keep]).all() and (v[keep] == vo[keep]).all()
+    assert (g[4] == -1).all() and v[4] == 0
+
+
 # ---------------------------------------------------------------------------
 # attention on the workload specs
 # ---------------------------------------------------------------------------
