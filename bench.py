@@ -175,6 +175,8 @@ def main() -> int:
     ap.add_argument("--rotate", type=int, default=6, help="independent cache copies cycled through (cold L2/MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-convert", action="store_true",
+                    help="run smla_convert_indices as its own kernel in the step instead of in the attention kernel")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -206,17 +208,24 @@ def main() -> int:
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     splits = smla.decode_num_splits(T, H, K) if entry == "decode" else 1
 
+    # the global indices and valid counts, for the byte / FLOP counts and the
+    # CPU baseline (the step below converts again, inside the attention kernel)
+    smla.convert_indices(req, bt, loc, out=gidx, valid_counts=vcnt)
+    torch.cuda.synchronize()
+
     def step(k: int):
-        smla.convert_indices(req, bt, loc, out=gidx, valid_counts=vcnt)
         c = k % R
+        if args.separate_convert:
+            smla.convert_indices(req, bt, loc, out=gidx, valid_counts=vcnt)
+            idx, conv = gidx, dict(topk_length=vcnt)
+        else:                       # request-local indices, converted by the attention kernel
+            idx, conv = loc, dict(block_table=bt, req_id=req, block_size=I.BLOCK_SIZE)
         if entry == "decode":
-            smla.decode_fwd(qn, qr, caches[c], gidx, spec.softmax_scale, kv_format=spec.kv_format,
-                            topk_length=vcnt, k_scale=kscales[c], group_scales=gscales[c],
-                            out=out, lse=lse, workspace=ws)
+            smla.decode_fwd(qn, qr, caches[c], idx, spec.softmax_scale, kv_format=spec.kv_format,
+                            k_scale=kscales[c], group_scales=gscales[c], out=out, lse=lse, workspace=ws, **conv)
         else:
-            smla.prefill_fwd(qn, qr, caches[c], gidx, spec.softmax_scale, kv_format=spec.kv_format,
-                             topk_length=vcnt, k_scale=kscales[c], group_scales=gscales[c],
-                             out=out, lse=lse)
+            smla.prefill_fwd(qn, qr, caches[c], idx, spec.softmax_scale, kv_format=spec.kv_format,
+                             k_scale=kscales[c], group_scales=gscales[c], out=out, lse=lse, **conv)
 
     # eager warmup and the eager reference of step 0
     for k in range(args.warmup):
@@ -311,6 +320,7 @@ def main() -> int:
         "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config, "num_tokens": T, "heads": H,
                    "topk": K, "entry": f"smla_{entry}_fwd", "splits": splits, "cache_copies_rotated": R,
                    "kv_storage": ["bf16", "e4m3 per-tensor scale", "e4m3 per-row x 128-group scales"][spec.kv_format],
+                   "index_conversion": "separate kernel" if args.separate_convert else "in the attention kernel",
                    "timing": "HIP graph of R steps replayed; cold L2/MALL by cache rotation"},
         "tflops": round(tflops, 2),
         "pct_of_path_roofline": round(100 * roofline_time / (dt / steps), 2),

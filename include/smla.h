@@ -91,7 +91,8 @@ typedef struct {
   const float* group_scales;    /* SMLA_KV_FP8_E4M3_GROUP128: [num_slots][ceil(D/128)] */
 
   /* Global slot indices [T][topk] int32 (row stride indices_stride), as
-   * produced by smla_convert_indices; negative = invalid. */
+   * produced by smla_convert_indices; negative = invalid. (Request-local
+   * indices when the fused conversion below is used.) */
   const int32_t* indices;
   int64_t indices_stride;
   int32_t topk;                 /* 1..2048 */
@@ -112,6 +113,20 @@ typedef struct {
 
   /* Decode only: number of top-k splits, 0 = choose from the shapes. */
   int32_t num_splits;
+
+  /* Optional fused index conversion (the operation of smla_convert_indices,
+   * done by the attention kernel while it stages a row's indices). When
+   * block_table is not NULL, `indices` holds request-local indices (the
+   * topk_local input of smla_convert_indices) and entry l of row t is used
+   * as slot block_table[r][l / block_size] * block_stride_rows
+   * + l % block_size, r = req_id[t]; an entry that smla_convert_indices would
+   * turn into -1 is skipped. block_stride_rows = 0 means block_size. No valid
+   * counts are produced (a -1 tail needs none). NULL = `indices` are global. */
+  const int32_t* req_id;        /* [T] int32 */
+  const int32_t* block_table;   /* [num_reqs][bt_row_stride] int32, first max_blocks used */
+  int32_t num_reqs, max_blocks;
+  int64_t bt_row_stride;
+  int32_t block_size, block_stride_rows;
 } smla_attn_args;
 
 /*
@@ -188,6 +203,10 @@ int smla_cache_write(const void* kv_c, int64_t kv_c_stride, const void* k_pe, in
  * NULL, NULL to clear. The events are owned by the caller.
  */
 int smla_set_timing_events(void* start, void* end);
+
+/* sizeof(smla_attn_args) as this library was built (for bindings that lay
+ * the struct out themselves). */
+size_t smla_attn_args_size(void);
 
 /* Thread-local description of the last non-OK return ("" if none). */
 const char* smla_last_error(void);

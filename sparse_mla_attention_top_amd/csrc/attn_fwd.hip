@@ -41,6 +41,13 @@ struct KParams {
   int64_t idx_stride;
   int32_t topk;
   const int32_t* topk_length;
+  // fused index conversion (block_table != nullptr: indices are request-local)
+  const int32_t* req_id;
+  const int32_t* block_table;
+  int32_t num_reqs, max_blocks;
+  int64_t bt_stride;
+  int32_t block_size, block_shift;   // block_shift = log2(block_size) if a power of two, else -1
+  int32_t block_stride_rows;
   int32_t num_tokens, num_heads;
   float scale_log2;   // softmax scale * log2(e)
   float out_mult;
@@ -192,10 +199,41 @@ smla_attn_kernel(KParams p) {
   const int32_t* irow = p.indices + (int64_t)t * p.idx_stride + row0;
   constexpr int kIdxPerThread = kMaxTopk / 512;
   int gi[kIdxPerThread];
+  const bool convert = p.block_table != nullptr;
+  const int rq = convert ? p.req_id[t] : 0;                // loaded with the indices
 #pragma unroll
   for (int k = 0; k < kIdxPerThread; k++) {
     const int j = threadIdx.x + 512 * k;
     gi[k] = (j < cap) ? irow[j] : -1;
+  }
+  if (convert) {
+    // request-local index lc -> block_table[req][lc / B] * stride + lc % B
+    // (the rule of smla_convert_indices; anything it maps to -1 stays -1)
+    const bool req_ok = rq >= 0 && rq < p.num_reqs;
+    const int32_t* bt = p.block_table + (int64_t)(req_ok ? rq : 0) * p.bt_stride;
+    int blk[kIdxPerThread], off[kIdxPerThread], e[kIdxPerThread];
+#pragma unroll
+    for (int k = 0; k < kIdxPerThread; k++) {
+      const int lc = gi[k];
+      blk[k] = p.max_blocks;
+      off[k] = 0;
+      if (lc >= 0) {
+        if (p.block_shift >= 0) {
+          blk[k] = lc >> p.block_shift;
+          off[k] = lc & (p.block_size - 1);
+        } else {
+          blk[k] = lc / p.block_size;
+          off[k] = lc - blk[k] * p.block_size;
+        }
+      }
+      e[k] = -1;
+      if (req_ok && blk[k] < p.max_blocks) e[k] = bt[blk[k]];
+    }
+#pragma unroll
+    for (int k = 0; k < kIdxPerThread; k++) {
+      const int64_t g = (int64_t)e[k] * p.block_stride_rows + off[k];
+      gi[k] = (e[k] >= 0 && g < p.num_slots) ? (int)g : -1;
+    }
   }
   int len = p.topk;
   if (p.topk_length) len = min(max(p.topk_length[t], 0), p.topk);
@@ -844,6 +882,16 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
   kp.group_scales = a.group_scales;
   kp.indices = a.indices; kp.idx_stride = a.idx_stride; kp.topk = a.topk;
   kp.topk_length = a.topk_length;
+  kp.req_id = a.req_id;
+  kp.block_table = a.block_table;
+  kp.num_reqs = a.num_reqs;
+  kp.max_blocks = a.max_blocks;
+  kp.bt_stride = a.bt_row_stride;
+  kp.block_size = a.block_size;
+  kp.block_shift = -1;
+  if (a.block_table && a.block_size > 0 && (a.block_size & (a.block_size - 1)) == 0)
+    kp.block_shift = __builtin_ctz((unsigned)a.block_size);
+  kp.block_stride_rows = a.block_stride_rows;
   kp.num_tokens = a.num_tokens; kp.num_heads = a.num_heads;
   kp.scale_log2 = a.softmax_scale * 1.4426950408889634f;
   kp.out_mult = 1.0f;

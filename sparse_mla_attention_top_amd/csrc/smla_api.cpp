@@ -72,6 +72,14 @@ int check_attn(const smla_attn_args* a, bool decode) {
   if (!aligned16(a->out) || a->out_stride_tok % 8 || a->out_stride_head % 8)
     return fail(SMLA_ERR_INVALID_ARG, "out must be 16-byte aligned with strides that are multiples of 8 elements");
   if (a->lse && a->lse_stride_tok < a->num_heads) return fail(SMLA_ERR_INVALID_ARG, "lse_stride_tok < num_heads");
+  if (a->block_table) {
+    if (!a->req_id) return fail(SMLA_ERR_INVALID_ARG, "req_id is NULL with a block table");
+    if (a->num_reqs < 1 || a->max_blocks < 1 || a->bt_row_stride < a->max_blocks)
+      return fail(SMLA_ERR_INVALID_ARG, "block table shape invalid (num_reqs=%d max_blocks=%d stride=%lld)",
+                  a->num_reqs, a->max_blocks, (long long)a->bt_row_stride);
+    if (a->block_size < 1 || a->block_stride_rows < 0)
+      return fail(SMLA_ERR_INVALID_ARG, "block_size=%d block_stride_rows=%d", a->block_size, a->block_stride_rows);
+  }
   if (a->kv_format == SMLA_KV_FP8_E4M3_GROUP128 && !a->group_scales)
     return fail(SMLA_ERR_INVALID_ARG, "group_scales is NULL for the group-scaled FP8 format");
   if (a->kv_format == SMLA_KV_FP8_E4M3_PER_TENSOR && !(std::isfinite(a->k_scale) && a->k_scale > 0))
@@ -109,6 +117,13 @@ smla::AttnArgs to_internal(const smla_attn_args* a) {
   r.out_sh = a->out_stride_head;
   r.lse = a->lse;
   r.lse_st = a->lse_stride_tok;
+  r.req_id = a->req_id;
+  r.block_table = a->block_table;
+  r.num_reqs = a->num_reqs;
+  r.max_blocks = a->max_blocks;
+  r.bt_row_stride = a->bt_row_stride;
+  r.block_size = a->block_size;
+  r.block_stride_rows = a->block_stride_rows == 0 ? a->block_size : a->block_stride_rows;
   r.ev_start = g_ev_start;
   r.ev_end = g_ev_end;
   return r;
@@ -120,7 +135,9 @@ extern "C" {
 
 const char* smla_last_error(void) { return g_err; }
 
-const char* smla_version(void) { return "smla 0.1 gfx950"; }
+const char* smla_version(void) { return "smla 0.2 gfx950"; }
+
+size_t smla_attn_args_size(void) { return sizeof(smla_attn_args); }
 
 int smla_set_timing_events(void* start, void* end) {
   if ((start == nullptr) != (end == nullptr)) return fail(SMLA_ERR_INVALID_ARG, "set both events or neither");

@@ -53,6 +53,12 @@ struct AttnArgs {
   int64_t out_st, out_sh;
   float* lse;
   int64_t lse_st;
+  // fused index conversion (block_table != nullptr: indices are request-local)
+  const int32_t* req_id;
+  const int32_t* block_table;
+  int32_t num_reqs, max_blocks;
+  int64_t bt_row_stride;
+  int32_t block_size, block_stride_rows;
   hipEvent_t ev_start, ev_end;   // optional, recorded around the main kernel
 };
 

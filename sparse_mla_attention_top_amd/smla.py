@@ -32,6 +32,7 @@ EXPORTED = (
     "smla_set_timing_events",
     "smla_last_error",
     "smla_version",
+    "smla_attn_args_size",
 )
 
 
@@ -69,6 +70,13 @@ class AttnArgs(ctypes.Structure):
         ("lse", ctypes.c_void_p),
         ("lse_stride_tok", ctypes.c_int64),
         ("num_splits", ctypes.c_int32),
+        ("req_id", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("num_reqs", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+        ("bt_row_stride", ctypes.c_int64),
+        ("block_size", ctypes.c_int32),
+        ("block_stride_rows", ctypes.c_int32),
     ]
 
 
@@ -99,6 +107,11 @@ def load() -> ctypes.CDLL:
     lib.smla_cache_write.restype = ctypes.c_int
     lib.smla_set_timing_events.argtypes = [vp, vp]
     lib.smla_set_timing_events.restype = ctypes.c_int
+    lib.smla_attn_args_size.argtypes = []
+    lib.smla_attn_args_size.restype = sz
+    if lib.smla_attn_args_size() != ctypes.sizeof(AttnArgs):
+        raise RuntimeError(f"{LIB_PATH}: smla_attn_args is {lib.smla_attn_args_size()} bytes, "
+                           f"the binding lays out {ctypes.sizeof(AttnArgs)}: rebuild the library")
     lib.smla_last_error.argtypes = []
     lib.smla_last_error.restype = ctypes.c_char_p
     lib.smla_version.argtypes = []
@@ -182,7 +195,8 @@ def _check_kv(kv_cache: torch.Tensor, kv_format: int, width: int, S: int,
 
 
 def _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk_length, k_scale,
-               group_scales, out, lse, num_splits) -> Tuple[AttnArgs, torch.Tensor, Optional[torch.Tensor]]:
+               group_scales, out, lse, num_splits, block_table=None, req_id=None, block_size=64,
+               block_stride_rows=0) -> Tuple[AttnArgs, torch.Tensor, Optional[torch.Tensor]]:
     _need(q_nope.dtype == torch.bfloat16 and q_nope.dim() == 3 and q_nope.shape[2] == 512 and q_nope.stride(2) == 1,
           "q_nope must be bf16 [T, h, 512] with unit channel stride")
     T, H, _ = q_nope.shape
@@ -222,6 +236,17 @@ def _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk
     a.lse = _ptr(lse)
     a.lse_stride_tok = lse.stride(0) if lse is not None else 0
     a.num_splits = int(num_splits)
+    if block_table is not None:
+        _need(req_id is not None and req_id.dtype == torch.int32 and req_id.numel() == T and req_id.is_contiguous(),
+              "req_id must be contiguous int32 [T] with a block table")
+        _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.stride(1) == 1,
+              "block_table must be int32 [num_reqs, max_blocks]")
+        a.req_id = _ptr(req_id)
+        a.block_table = _ptr(block_table)
+        a.num_reqs, a.max_blocks = block_table.shape
+        a.bt_row_stride = block_table.stride(0)
+        a.block_size = int(block_size)
+        a.block_stride_rows = int(block_stride_rows)
     return a, out, lse
 
 
@@ -235,13 +260,16 @@ def decode_num_splits(num_tokens: int, num_heads: int, topk: int, num_splits: in
 
 def decode_fwd(q_nope, q_rope, kv_cache, indices, softmax_scale, kv_format=KV_BF16, topk_length=None,
                k_scale=1.0, group_scales=None, out=None, lse=None, return_lse=True, num_splits=0,
-               workspace=None, stream=None):
-    """Sparse MLA decode forward. Returns (out [T,h,512] bf16, lse [T,h] fp32 or None)."""
+               workspace=None, stream=None, block_table=None, req_id=None, block_size=64, block_stride_rows=0):
+    """Sparse MLA decode forward. Returns (out [T,h,512] bf16, lse [T,h] fp32 or None).
+    With ``block_table`` (and ``req_id``), ``indices`` are request-local and are
+    converted inside the attention kernel."""
     T, H = q_nope.shape[:2]
     if lse is None and return_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=q_nope.device)
     a, out, lse = _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk_length,
-                             k_scale, group_scales, out, lse, num_splits)
+                             k_scale, group_scales, out, lse, num_splits, block_table, req_id, block_size,
+                             block_stride_rows)
     need = decode_workspace_size(T, H, indices.shape[1], num_splits) if T > 0 else 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
@@ -252,13 +280,16 @@ def decode_fwd(q_nope, q_rope, kv_cache, indices, softmax_scale, kv_format=KV_BF
 
 
 def prefill_fwd(q_nope, q_rope, kv_cache, indices, softmax_scale, kv_format=KV_BF16, topk_length=None,
-                k_scale=1.0, group_scales=None, out=None, lse=None, return_lse=False, stream=None):
-    """Sparse MLA prefill forward (no split). Returns (out, lse or None)."""
+                k_scale=1.0, group_scales=None, out=None, lse=None, return_lse=False, stream=None,
+                block_table=None, req_id=None, block_size=64, block_stride_rows=0):
+    """Sparse MLA prefill forward (no split). Returns (out, lse or None). ``block_table``
+    as for decode_fwd."""
     T, H = q_nope.shape[:2]
     if lse is None and return_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=q_nope.device)
     a, out, lse = _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk_length,
-                             k_scale, group_scales, out, lse, 0)
+                             k_scale, group_scales, out, lse, 0, block_table, req_id, block_size,
+                             block_stride_rows)
     rc = load().smla_prefill_fwd(ctypes.byref(a), _stream(stream))
     _check("smla_prefill_fwd", rc)
     return out, lse

@@ -35,18 +35,18 @@ def _quantize(rows_bits: np.ndarray, kv_format: int, k_scale: float = 1.0):
 
 
 def _attend(entry, q, codes_dev, scales_dev, kv_format, k_scale, idx_dev, scale, lengths_dev=None,
-            num_splits=0):
+            num_splits=0, **conv):
     d_rope = q.shape[2] - 512
     qd = q.to(DEV)
     qn, qr = qd[..., :512], (qd[..., 512:] if d_rope else None)
     if entry == "decode":
         out, lse = smla.decode_fwd(qn, qr, codes_dev, idx_dev, scale, kv_format=kv_format,
                                    topk_length=lengths_dev, k_scale=k_scale, group_scales=scales_dev,
-                                   num_splits=num_splits)
+                                   num_splits=num_splits, **conv)
     else:
         out, lse = smla.prefill_fwd(qn, qr, codes_dev, idx_dev, scale, kv_format=kv_format,
                                     topk_length=lengths_dev, k_scale=k_scale, group_scales=scales_dev,
-                                    return_lse=True)
+                                    return_lse=True, **conv)
     torch.cuda.synchronize()
     return out, lse
 
@@ -211,6 +211,12 @@ def _full_size(name, sample=None):
     st = torch.as_tensor(sel, device=DEV)
     err, lerr = compare(out[st], lse[st], ref, name, _k(spec.kv_format))
     print(f"{name} full size: out err {err:.2e} lse err {lerr:.2e}")
+    # the same launch with the conversion done by the attention kernel: the
+    # same global rows in the same order, so the same bits
+    say(f"fp8 full size {name}, fused conversion")
+    out2, lse2 = _attend("decode", q, kv, gs, spec.kv_format, k_scale, w.topk_local.to(DEV), spec.softmax_scale,
+                         block_table=w.block_table.to(DEV), req_id=w.req_id.to(DEV), block_size=I.BLOCK_SIZE)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(lse, lse2)
 
 
 def test_nope_fp8_full_size():

@@ -87,6 +87,74 @@ def test_convert_long_block_tables_bitexact(max_blocks):
     assert (g[4] == -1).all() and v[4] == 0
 
 
+def _fused_vs_separate(q, kv, req, bt, loc, scale, entry, block_size, stride=0, num_splits=0):
+    """(out, lse) of convert + attention and of attention with the conversion
+    fused, on the same inputs."""
+    qd = q.to(DEV)
+    qn, qr = qd[..., :512], (qd[..., 512:] if q.shape[2] > 512 else None)
+    kvd, reqd, btd, locd = kv.to(DEV), req.to(DEV), bt.to(DEV), loc.to(DEV)
+    gidx, vcnt = smla.convert_indices(reqd, btd, locd, block_size=block_size, block_stride_rows=stride)
+    conv = dict(block_table=btd, req_id=reqd, block_size=block_size, block_stride_rows=stride)
+    # no row lengths on either side: invalid entries need not form a tail here
+    if entry == "decode":
+        a = smla.decode_fwd(qn, qr, kvd, gidx, scale, num_splits=num_splits)
+        b = smla.decode_fwd(qn, qr, kvd, locd, scale, num_splits=num_splits, **conv)
+    else:
+        a = smla.prefill_fwd(qn, qr, kvd, gidx, scale, return_lse=True)
+        b = smla.prefill_fwd(qn, qr, kvd, locd, scale, return_lse=True, **conv)
+    torch.cuda.synchronize()
+    return a, b, gidx, vcnt
+
+
+@pytest.mark.parametrize("name,entry", [("tiny", "decode"), ("tiny_late", "prefill"), ("decode_bf16", "decode"),
+                                        ("prefill_bf16", "prefill")])
+def test_fused_conversion_is_bitexact(name, entry):
+    """Attention with the index conversion done by the attention kernel gives
+    the same bits as smla_convert_indices followed by attention on global
+    indices (the same rows, in the same order, through the same arithmetic)."""
+    spec = I.SPECS[name]
+    say(f"fused conversion {name} {entry}")
+    w = I.generate(spec)
+    kv = w.kv_src.view(spec.num_blocks, I.BLOCK_SIZE, spec.d)
+    (o1, l1), (o2, l2), _, _ = _fused_vs_separate(w.q, kv, w.req_id, w.block_table, w.topk_local,
+                                                  spec.softmax_scale, entry, I.BLOCK_SIZE)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("block_size,stride", [(16, 0), (48, 0), (16, 40)])
+def test_fused_conversion_invalid_corners(block_size, stride):
+    """Fused conversion with a table holding -1 and negative entries, local
+    indices below 0 and past the table, a request id out of range (its row
+    becomes empty: out 0, LSE -inf), a block size that is not a power of two
+    and a table stride other than the block size; bit-exact against the
+    separate path and within tolerance of the oracle."""
+    rng = np.random.default_rng(19 + block_size + stride)
+    R, MB, T, K = 4, 9, 11, 300
+    rows = (stride if stride else block_size)
+    S = R * MB * rows + block_size
+    bt = rng.permutation(R * MB).reshape(R, MB).astype(np.int32)
+    bt[1, 2] = -1
+    bt[3, 0] = -7
+    req = rng.integers(0, R, T).astype(np.int32)
+    loc = rng.integers(-3, MB * block_size + 9, (T, K)).astype(np.int32)
+    g = torch.Generator().manual_seed(20 + block_size)
+    q = torch.randn((T, 64, 576), generator=g).to(torch.bfloat16)
+    kv = torch.randn((S, 576), generator=g).to(torch.bfloat16)
+    go, vo = O.convert_indices(req, bt, loc, block_size, stride if stride else block_size)
+    req_bad = req.copy()
+    req_bad[5] = R
+    say(f"fused conversion corners B={block_size} stride={stride}")
+    for entry, splits in (("decode", 3), ("prefill", 0)):
+        (o1, l1), (o2, l2), _, _ = _fused_vs_separate(q, kv, torch.from_numpy(req_bad), torch.from_numpy(bt),
+                                                      torch.from_numpy(loc), 0.06, entry, block_size, stride, splits)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+        keep = np.arange(T) != 5
+        ref = oracle_for(q[torch.from_numpy(np.nonzero(keep)[0])], bits(kv), go[keep], 0.06)
+        compare(o2[torch.as_tensor(np.nonzero(keep)[0], device=DEV)],
+                l2[torch.as_tensor(np.nonzero(keep)[0], device=DEV)], ref, f"fused {entry}")
+        assert (o2[5] == 0).all() and torch.isneginf(l2[5]).all()
+
+
 # ---------------------------------------------------------------------------
 # attention on the workload specs
 # ---------------------------------------------------------------------------
