@@ -175,6 +175,7 @@ def main() -> int:
     ap.add_argument("--rotate", type=int, default=6, help="independent cache copies cycled through (cold L2/MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--splits", type=int, default=0, help="decode top-k splits (0 = the library's plan)")
     ap.add_argument("--separate-convert", action="store_true",
                     help="run smla_convert_indices as its own kernel in the step instead of in the attention kernel")
     args = ap.parse_args()
@@ -204,9 +205,9 @@ def main() -> int:
     vcnt = torch.empty((T,), dtype=torch.int32, device=dev)
     out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((T, H), dtype=torch.float32, device=dev)
-    ws_bytes = smla.decode_workspace_size(T, H, K) if entry == "decode" else 0
+    ws_bytes = smla.decode_workspace_size(T, H, K, args.splits) if entry == "decode" else 0
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    splits = smla.decode_num_splits(T, H, K) if entry == "decode" else 1
+    splits = smla.decode_num_splits(T, H, K, args.splits) if entry == "decode" else 1
 
     # the global indices and valid counts, for the byte / FLOP counts and the
     # CPU baseline (the step below converts again, inside the attention kernel)
@@ -222,7 +223,8 @@ def main() -> int:
             idx, conv = loc, dict(block_table=bt, req_id=req, block_size=I.BLOCK_SIZE)
         if entry == "decode":
             smla.decode_fwd(qn, qr, caches[c], idx, spec.softmax_scale, kv_format=spec.kv_format,
-                            k_scale=kscales[c], group_scales=gscales[c], out=out, lse=lse, workspace=ws, **conv)
+                            k_scale=kscales[c], group_scales=gscales[c], out=out, lse=lse, workspace=ws,
+                            num_splits=args.splits, **conv)
         else:
             smla.prefill_fwd(qn, qr, caches[c], idx, spec.softmax_scale, kv_format=spec.kv_format,
                              k_scale=kscales[c], group_scales=gscales[c], out=out, lse=lse, **conv)

@@ -401,22 +401,70 @@ smla_attn_kernel(KParams p) {
     if (ntiles > 0) issue_tile_s(0);
     if (ntiles > 1) issue_tile_s(1);
     bf16x8 q[2][QKS];
+    if constexpr (!F8) {
+      // bf16 cache: the two row halves need the same Q. Each loads half of
+      // the k-steps and the halves are swapped through LDS that tiles 0 and 1
+      // leave idle (latent buffers 2, 3; rope buffer 2 and the P block).
+      auto qslot = [&](int nbq, int ks) -> lds_char* {
+        if (ks < kLatKS) return lat + (2 + hg) * kLatBytes + ((nbq * kLatKS + ks) * 64 + l) * 16;
+        lds_char* base = hg ? pbuf : rope + 2 * kRopeBytes;
+        return base + ((nbq * 2 + (ks - kLatKS)) * 64 + l) * 16;
+      };
+      constexpr int H0 = QKS / 2, H1 = QKS - QKS / 2;
+      auto load_half = [&](auto off_c, auto cnt_c) {
+        constexpr int off = decltype(off_c)::value, cnt = decltype(cnt_c)::value;
 #pragma unroll
-    for (int nbq = 0; nbq < 2; nbq++) {
-      const int head = hb + 32 * hg + 16 * nbq + li;
-      const bool valid = head < H;
-      const int hq = valid ? head : 0;
-      const uint16_t* qn = p.q_nope + t * p.qn_st + hq * p.qn_sh + 8 * lg;
+        for (int nbq = 0; nbq < 2; nbq++) {
+          const int head = hb + 32 * hg + 16 * nbq + li;
+          const bool valid = head < H;
+          const int hq = valid ? head : 0;
+          const uint16_t* qn = p.q_nope + t * p.qn_st + hq * p.qn_sh + 8 * lg;
+          const uint16_t* qr = p.q_rope + t * p.qr_st + hq * p.qr_sh + 8 * lg;
+          static_for<cnt>([&](auto k_c) {
+            constexpr int ks = off + decltype(k_c)::value;
+            if constexpr (ks < kLatKS) q[nbq][ks] = *(const bf16x8*)(qn + 32 * ks);
+            else q[nbq][ks] = *(const bf16x8*)(qr + 32 * (ks - kLatKS));
+          });
+          wait_vmcnt<0>();
+          static_for<cnt>([&](auto k_c) {
+            constexpr int ks = off + decltype(k_c)::value;
+            if (!valid) q[nbq][ks] = (bf16x8){};
+            *(__attribute__((address_space(3))) bf16x8*)qslot(nbq, ks) = q[nbq][ks];
+          });
+        }
+      };
+      auto get_half = [&](auto off_c, auto cnt_c) {
+        constexpr int off = decltype(off_c)::value, cnt = decltype(cnt_c)::value;
 #pragma unroll
-      for (int ks = 0; ks < kLatKS; ks++) q[nbq][ks] = *(const bf16x8*)(qn + 32 * ks);
-      if (QKS > kLatKS) {
-        const uint16_t* qr = p.q_rope + t * p.qr_st + hq * p.qr_sh + 8 * lg;
+        for (int nbq = 0; nbq < 2; nbq++)
+          static_for<cnt>([&](auto k_c) {
+            constexpr int ks = off + decltype(k_c)::value;
+            q[nbq][ks] = *(const __attribute__((address_space(3))) bf16x8*)qslot(nbq, ks);
+          });
+      };
+      if (rh == 0) load_half(std::integral_constant<int, 0>{}, std::integral_constant<int, H0>{});
+      else load_half(std::integral_constant<int, H0>{}, std::integral_constant<int, H1>{});
+      lds_barrier();                                       // both halves are in LDS (the O-waves match it)
+      if (rh == 0) get_half(std::integral_constant<int, H0>{}, std::integral_constant<int, H1>{});
+      else get_half(std::integral_constant<int, 0>{}, std::integral_constant<int, H0>{});
+    } else {
 #pragma unroll
-        for (int ks = kLatKS; ks < QKS; ks++) q[nbq][ks] = *(const bf16x8*)(qr + 32 * (ks - kLatKS));
-      }
-      if (!valid) {
+      for (int nbq = 0; nbq < 2; nbq++) {
+        const int head = hb + 32 * hg + 16 * nbq + li;
+        const bool valid = head < H;
+        const int hq = valid ? head : 0;
+        const uint16_t* qn = p.q_nope + t * p.qn_st + hq * p.qn_sh + 8 * lg;
 #pragma unroll
-        for (int ks = 0; ks < QKS; ks++) q[nbq][ks] = (bf16x8){};
+        for (int ks = 0; ks < kLatKS; ks++) q[nbq][ks] = *(const bf16x8*)(qn + 32 * ks);
+        if (QKS > kLatKS) {
+          const uint16_t* qr = p.q_rope + t * p.qr_st + hq * p.qr_sh + 8 * lg;
+#pragma unroll
+          for (int ks = kLatKS; ks < QKS; ks++) q[nbq][ks] = *(const bf16x8*)(qr + 32 * (ks - kLatKS));
+        }
+        if (!valid) {
+#pragma unroll
+          for (int ks = 0; ks < QKS; ks++) q[nbq][ks] = (bf16x8){};
+        }
       }
     }
     // complete here, so that the compiler puts no wait on the Q registers inside the loop
@@ -731,8 +779,13 @@ smla_attn_kernel(KParams p) {
       }
     };
 
+    if constexpr (!F8) {
+      if (ntiles > 0) issue_tile_o(0);
+      if (ntiles > 1) issue_tile_o(1);
+      lds_barrier();                                       // matches the S-waves' Q exchange
+    }
     for (int attempt = 0; attempt < 2; attempt++) {
-      o_pass(true, false);
+      o_pass(true, !F8 && attempt == 0);
       if (!s_flag) break;                                  // uniform (after the pass's last barrier)
       o_pass(false, false);
       lds_barrier();                                       // matches the S-waves' final maximum exchange
