@@ -121,8 +121,11 @@ struct Shape {
   // copy instructions per wave per tile. FP8: latent segments 0-1, the rope
   // part and the scales are copied (and converted) by the O-waves, latent
   // segments 2-3 by the S-waves; bf16: all by the O-waves.
-  static constexpr int NDMA_O = F8 ? 2 + (ROPE ? 1 : 0) + (GROUP ? 1 : 0) : D / 64;
-  static constexpr int NDMA_S = F8 ? 2 : 0;
+  // FP8: latent segments [0, SEG_O) are copied and converted by the O-waves,
+  // [SEG_O, 4) by the S-waves (moving more to either side measured slower)
+  static constexpr int SEG_O = 2;
+  static constexpr int NDMA_O = F8 ? SEG_O + (ROPE ? 1 : 0) + (GROUP ? 1 : 0) : D / 64;
+  static constexpr int NDMA_S = F8 ? 4 - SEG_O : 0;
   static_assert(D == kDLatent || D == kDLatent + 64, "rope part must be 64 channels");
   static_assert(8 * G <= 64, "scales of 8 rows fit one instruction");
 };
@@ -317,8 +320,7 @@ smla_attn_kernel(KParams p) {
           dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(rope_addr + (i % (NROPE ? NROPE : 1)) * kRopeBytes + wu * 1024));
       });
     } else {
-      issue_seg(s, i, std::integral_constant<int, 0>{});
-      issue_seg(s, i, std::integral_constant<int, 1>{});
+      static_for<S::SEG_O>([&](auto u_c) { issue_seg(s, i, u_c); });
       const uint32_t sb = stage_addr + (i % (S::NSTAGE ? S::NSTAGE : 1)) * S::ST_BYTES;
       if constexpr (S::ROPE) {
         if (l < 32) dma_16b<0>(s.rope, __builtin_amdgcn_readfirstlane(sb + S::ST_ROPE + wu * 512));
@@ -332,49 +334,63 @@ smla_attn_kernel(KParams p) {
   auto issue_tile_s = [&](int i) {
     if constexpr (F8) {
       const Src s = sources(i);
-      issue_seg(s, i, std::integral_constant<int, 2>{});
-      issue_seg(s, i, std::integral_constant<int, 3>{});
+      static_for<4 - S::SEG_O>([&](auto u_c) {
+        issue_seg(s, i, std::integral_constant<int, S::SEG_O + decltype(u_c)::value>{});
+      });
     }
   };
-  // FP8: staged latent segment u of this wave's rows of tile i -> bf16 tile i
-  // (exact E4M3 values)
-  auto convert_seg = [&](int i, auto u_c) {
+  // FP8 conversion of this wave's rows of tile i into bf16 tile i (exact
+  // E4M3 values). A wave first issues every stage read of its share, then
+  // converts and writes: one LDS round trip instead of one per piece.
+  auto stage_of = [&](int i) -> const lds_char* { return stage + (i % (S::NSTAGE ? S::NSTAGE : 1)) * S::ST_BYTES; };
+  // latent segment u (bytes 128u .. 128u+127 of the row): read, then write
+  auto seg_read = [&](int i, auto u_c) -> u32x4 {
     constexpr int u = decltype(u_c)::value;
-    const lds_char* st = stage + (i % (S::NSTAGE ? S::NSTAGE : 1)) * S::ST_BYTES;
+    return *(const __attribute__((address_space(3))) u32x4*)(stage_of(i) + (4 * u + wr) * 1024 + 16 * l);
+  };
+  auto seg_write = [&](int i, auto u_c, const u32x4 raw) {
+    constexpr int u = decltype(u_c)::value;
     lds_char* lb = lat_buf(i);
     const int r = 8 * wr + (l >> 3);
-    const u32x4 raw = *(const __attribute__((address_space(3))) u32x4*)(st + (4 * u + wr) * 1024 + 16 * l);
     u32x4 lo, hi;
     e4m3x16_to_bf16<false>(raw, 1.0f, lo, hi);
     const int k = 8 * u + (l & 7);
     *(__attribute__((address_space(3))) u32x4*)(lb + tile_pos(r, 2 * k)) = lo;
     *(__attribute__((address_space(3))) u32x4*)(lb + tile_pos(r, 2 * k + 1)) = hi;
   };
-  // O-wave conversion of tile i: segments 0-1, the rope part, and (group
-  // format) all the rows' scales -> row-scale set i ([group][row])
+  // O-wave share: segments [0, SEG_O), the rope part, and (group format) all
+  // the rows' scales -> row-scale set i ([group][row])
   auto convert_tile_o = [&](int i) {
     if constexpr (F8) {
-      const lds_char* st = stage + (i % (S::NSTAGE ? S::NSTAGE : 1)) * S::ST_BYTES;
-      convert_seg(i, std::integral_constant<int, 0>{});
-      convert_seg(i, std::integral_constant<int, 1>{});
+      const lds_char* st = stage_of(i);
+      u32x4 raw[S::SEG_O];
+      static_for<S::SEG_O>([&](auto u_c) { raw[decltype(u_c)::value] = seg_read(i, u_c); });
+      float sc[4] = {}, rsc = 0.0f;
+      u32x4 rraw = {};
+      const int r2 = 8 * wr + (min(l, 31) >> 2);           // rope: lanes 0..31 hold 8 rows x 4 chunks
+      if constexpr (S::GROUP)
+        static_for<4>([&](auto u_c) {
+          constexpr int u = decltype(u_c)::value;
+          sc[u] = *(const __attribute__((address_space(3))) float*)(st + S::ST_SC + wr * 256 + 4 * ((l >> 3) * S::G + u));
+        });
+      if constexpr (S::ROPE) {
+        rraw = *(const __attribute__((address_space(3))) u32x4*)(st + S::ST_ROPE + wr * 512 + 16 * min(l, 31));
+        if constexpr (S::GROUP)
+          rsc = *(const __attribute__((address_space(3))) float*)(st + S::ST_SC + wr * 256 + 4 * ((r2 - 8 * wr) * S::G + 4));
+      }
+      static_for<S::SEG_O>([&](auto u_c) { seg_write(i, u_c, raw[decltype(u_c)::value]); });
       if constexpr (S::GROUP) {
         const int r = 8 * wr + (l >> 3);
         static_for<4>([&](auto u_c) {
           constexpr int u = decltype(u_c)::value;
-          const float sc = *(const __attribute__((address_space(3))) float*)(st + S::ST_SC + wr * 256 + 4 * ((l >> 3) * S::G + u));
-          *(__attribute__((address_space(3))) float*)(rsc_buf(i) + 4 * (u * kTileRows + r)) = sc;
+          *(__attribute__((address_space(3))) float*)(rsc_buf(i) + 4 * (u * kTileRows + r)) = sc[u];
         });
       }
       if constexpr (S::ROPE) {
         if (l < 32) {
-          const int r2 = 8 * wr + (l >> 2);
-          const u32x4 raw = *(const __attribute__((address_space(3))) u32x4*)(st + S::ST_ROPE + wr * 512 + 16 * l);
-          if constexpr (S::GROUP) {
-            const float sc = *(const __attribute__((address_space(3))) float*)(st + S::ST_SC + wr * 256 + 4 * ((l >> 2) * S::G + 4));
-            *(__attribute__((address_space(3))) float*)(rsc_buf(i) + 4 * (4 * kTileRows + r2)) = sc;
-          }
+          if constexpr (S::GROUP) *(__attribute__((address_space(3))) float*)(rsc_buf(i) + 4 * (4 * kTileRows + r2)) = rsc;
           u32x4 lo, hi;
-          e4m3x16_to_bf16<false>(raw, 1.0f, lo, hi);
+          e4m3x16_to_bf16<false>(rraw, 1.0f, lo, hi);
           const int k = (l & 3);                            // chunks 64 + 2k, 65 + 2k: rope buffer
           lds_char* rb = rope_buf(i);
           *(__attribute__((address_space(3))) u32x4*)(rb + tile_pos(r2, 64 + 2 * k) - kLatBytes) = lo;
@@ -383,11 +399,17 @@ smla_attn_kernel(KParams p) {
       }
     }
   };
-  // S-wave conversion of tile i (FP8: segments 2-3)
+  // S-wave share: segments [SEG_O, 4)
   auto convert_tile_s = [&](int i) {
     if constexpr (F8) {
-      convert_seg(i, std::integral_constant<int, 2>{});
-      convert_seg(i, std::integral_constant<int, 3>{});
+      constexpr int NS = 4 - S::SEG_O;
+      u32x4 raw[NS];
+      static_for<NS>([&](auto u_c) {
+        raw[decltype(u_c)::value] = seg_read(i, std::integral_constant<int, S::SEG_O + decltype(u_c)::value>{});
+      });
+      static_for<NS>([&](auto u_c) {
+        seg_write(i, std::integral_constant<int, S::SEG_O + decltype(u_c)::value>{}, raw[decltype(u_c)::value]);
+      });
     }
   };
 
