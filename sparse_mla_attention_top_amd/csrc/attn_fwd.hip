@@ -14,13 +14,17 @@
 //     softmax (base 2, fixed per-head reference, see below) and P (bf16) into
 //     a double-buffered LDS block.
 //   O-waves (4..7): the tile copies (global_load_lds_dwordx4 straight into
-//     LDS; for FP8 caches into a stage, then converted to bf16 by the wave that
-//     copied it), and O += P.V one tile behind the S-waves: wave 4+w owns O for
-//     all 64 heads x latent channels 128w..128w+127 in accumulator registers,
+//     LDS), and O += P.V one tile behind the S-waves: wave 4+w owns O for all
+//     64 heads x latent channels 128w..128w+127 in accumulator registers,
 //     A = P from LDS, B = V read with ds_read_b64_tr_b16 from the same tile
 //     (V is the first 512 channels of the gathered row, no second gather).
+//   FP8 caches: rows land in a stage as E4M3 bytes and each wave converts the
+//     rows it copied into the bf16 tile; the latent segments are shared
+//     between the roles (Shape::SEG_O).
 // So on every SIMD one wave's softmax / conversion work overlaps the other's
-// MFMAs, and one barrier per tile orders both roles.
+// MFMAs, and one barrier per tile orders both roles. Before the loop all
+// threads stage the row's indices (converting request-local indices through
+// the block table when one is given) and the S-waves load Q.
 #include "smla_device.h"
 #include "smla_internal.h"
 
