@@ -22,6 +22,15 @@ What is computed, with the passage each step follows:
   gathered K = [c_kv | k_rope], V = c_kv, SDPA with the given scale; FlashMLA
   sparse API docs, ``_forward_fp8_kv_mixed_batch``: LSE per (token, head),
   rows with no valid slot give (0, -inf)).
+* ``dcp_filter_convert`` -- one context-parallel rank's share of a top-k row
+  of request token positions: the positions this rank stores, converted to
+  its local cache slots through its own block table, -1 elsewhere, optionally
+  compacted to the front (vLLM FlashMLA sparse backend, ``forward_mqa``: the
+  ``triton_filter_and_convert_dcp_index`` call with dcp_size, dcp_rank,
+  cp_kv_cache_interleave_size and compact_valid_to_front). The pages do not
+  print the placement; the reading used here is the plain interleave: with
+  interleave I over W ranks, position p is on rank (p // I) % W at local
+  position (p // (I W)) I + p % I.
 * ``merge_partials`` -- combine partial (out, lse) pairs computed over
   disjoint slices of a row: the identity element is (0, -inf) (FlashMLA
   sparse API docs, ``_forward_fp8_kv_mixed_batch``, the cross-rank LSE merge).
@@ -200,6 +209,42 @@ def _attention(q, cache, kv_format, indices, softmax_scale, topk_length, k_scale
     if not outs:
         return np.zeros((0, h, d_v)), np.zeros((0, h)), np.zeros((0, h, d_v))
     return np.stack(outs), np.stack(lses), (np.stack(mags) if magnitude else None)
+
+
+def dcp_owner_local(pos: np.ndarray, dcp_size: int, interleave: int):
+    """(rank, local position) of request token positions pos >= 0 under the
+    interleaved placement: runs of ``interleave`` consecutive positions go to
+    ranks 0, 1, ..., W-1 in turn, and each rank stores its runs back to back."""
+    pos = np.asarray(pos, dtype=np.int64)
+    run = pos // interleave
+    rank = run % dcp_size
+    local = (run // dcp_size) * interleave + pos % interleave
+    return rank, local
+
+
+def dcp_filter_convert(req_id: np.ndarray, block_table: np.ndarray, topk_tokens: np.ndarray,
+                       dcp_size: int, dcp_rank: int, interleave: int, block_size: int,
+                       block_stride_rows: Optional[int] = None, compact_valid_to_front: bool = False):
+    """Rank ``dcp_rank``'s view of top-k rows of request token positions.
+    Returns (local slots [T, K] int32, valid_counts [T] int32).
+
+    An entry p < 0, or a position stored on another rank, becomes -1. A
+    position this rank stores is converted like ``convert_indices`` from its
+    local position, through this rank's block table. With
+    ``compact_valid_to_front`` the valid entries of a row come first, in
+    their order, followed by -1."""
+    loc = np.asarray(topk_tokens, dtype=np.int64)
+    rank, local = dcp_owner_local(np.maximum(loc, 0), dcp_size, interleave)
+    mine = (loc >= 0) & (rank == dcp_rank)
+    local = np.where(mine, local, -1)
+    out, valid = convert_indices(req_id, block_table, local, block_size, block_stride_rows)
+    if compact_valid_to_front:
+        packed = np.full_like(out, -1)
+        for t in range(out.shape[0]):
+            keep = out[t][out[t] >= 0]
+            packed[t, :keep.size] = keep
+        out = packed
+    return out, valid
 
 
 def merge_partials(outs: np.ndarray, lses: np.ndarray):

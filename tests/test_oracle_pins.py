@@ -342,6 +342,94 @@ def test_split_merge_identity():
     assert (eo == 0).all() and np.isneginf(el).all()
 
 
+# ---------------------------------------------------------------------------
+# context-parallel (DCP) shard filter and merge
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("W,I", [(1, 1), (2, 1), (3, 2), (4, 64), (8, 16)])
+def test_dcp_placement_partitions_positions(W, I):
+    """Every position is stored by exactly one rank, and each rank's local
+    positions of a request's first N tokens are exactly 0 .. N_r - 1 in
+    token order (no gap, no collision)."""
+    for N in (1, 7, 63, 64, 65, 300, 1000):
+        pos = np.arange(N)
+        rank, local = O.dcp_owner_local(pos, W, I)
+        assert ((rank >= 0) & (rank < W)).all()
+        total = 0
+        for r in range(W):
+            lr = local[rank == r]
+            assert lr.tolist() == list(range(lr.size))          # in order, dense
+            total += lr.size
+        assert total == N
+
+
+def test_dcp_single_rank_is_plain_conversion():
+    rng = np.random.default_rng(21)
+    R, MB, B, T, K = 3, 9, 16, 13, 70
+    bt = rng.permutation(R * MB).reshape(R, MB).astype(np.int32)
+    req = rng.integers(0, R, T)
+    loc = rng.integers(-2, MB * B + 4, (T, K))
+    for I in (1, 5, 64):
+        g1, v1 = O.dcp_filter_convert(req, bt, loc, 1, 0, I, B)
+        g0, v0 = O.convert_indices(req, bt, loc, B)
+        assert (g1 == g0).all() and (v1 == v0).all()
+
+
+def test_dcp_ranks_split_the_valid_entries_and_compaction_keeps_order():
+    rng = np.random.default_rng(22)
+    W, I, R, MB, B, T, K = 4, 3, 2, 12, 16, 9, 50
+    req = rng.integers(0, R, T)
+    loc = rng.integers(-1, W * MB * B, (T, K))
+    counts = np.zeros(T, dtype=np.int64)
+    for r in range(W):
+        bt = rng.permutation(R * MB).reshape(R, MB).astype(np.int32)
+        g, v = O.dcp_filter_convert(req, bt, loc, W, r, I, B)
+        gc, vc = O.dcp_filter_convert(req, bt, loc, W, r, I, B, compact_valid_to_front=True)
+        assert (v == vc).all()
+        for t in range(T):
+            assert gc[t, :v[t]].tolist() == g[t][g[t] >= 0].tolist() and (gc[t, v[t]:] == -1).all()
+        counts += v
+    # every non-negative position inside the tables is valid on exactly one rank
+    assert (counts == (loc >= 0).sum(axis=1)).all()
+
+
+def test_dcp_sharded_attention_merges_to_the_whole():
+    """A request's cache spread over W ranks by the placement, each rank's
+    attention over its filtered indices, merged by LSE: the unsharded result
+    (rows a rank does not see come out as the merge identity (0, -inf))."""
+    rng = np.random.default_rng(23)
+    W, I, B, N, T, h, K, scale = 3, 4, 8, 200, 5, 4, 48, 0.07
+    rows = _rand_bf16(rng, (N, 576))                       # token position p -> row
+    q = O.bf16_bits_to_f64(_rand_bf16(rng, (T, h, 576)))
+    topk = np.stack([rng.permutation(N)[:K] for _ in range(T)])
+    topk[1, 10:] = -1
+    topk[2, :] = I * np.arange(K) * W % N                  # only rank 0's runs ...
+    topk[2] = np.where(topk[2] // I % W == 0, topk[2], -1)  # ... so ranks 1, 2 see an empty row
+    req = np.zeros(T, dtype=np.int64)
+    whole_bt = np.arange((N + B - 1) // B, dtype=np.int32)[None]
+    whole_cache = np.zeros((whole_bt.size * B, 576), dtype=np.uint16)
+    whole_cache[:N] = rows
+    g, _ = O.convert_indices(req, whole_bt, topk, B)
+    out, lse = O.attention(q, whole_cache, O.KV_BF16, g, scale)
+    rank, local = O.dcp_owner_local(np.arange(N), W, I)
+    parts_o, parts_l = [], []
+    for r in range(W):
+        n_r = int((rank == r).sum())
+        nb = (n_r + B - 1) // B
+        bt = rng.permutation(nb + 2)[:nb].astype(np.int32)[None]      # scattered blocks
+        cache_r = np.zeros(((nb + 2) * B, 576), dtype=np.uint16)
+        for p in np.nonzero(rank == r)[0]:
+            cache_r[bt[0, local[p] // B] * B + local[p] % B] = rows[p]
+        g_r, _ = O.dcp_filter_convert(req, bt, topk, W, r, I, B)
+        o, l = O.attention(q, cache_r, O.KV_BF16, g_r, scale)
+        if r > 0:
+            assert (o[2] == 0).all() and np.isneginf(l[2]).all()
+        parts_o.append(o)
+        parts_l.append(l)
+    mo, ml = O.merge_partials(np.stack(parts_o), np.stack(parts_l))
+    assert np.abs(mo - out).max() < 1e-12 and np.abs(ml - lse).max() < 1e-12
+
+
 def test_fp8_per_tensor_dequant_is_code_times_scale():
     rng = np.random.default_rng(12)
     codes = rng.integers(0, 256, (8, 512)).astype(np.uint8)
