@@ -176,6 +176,12 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="decode top-k splits (0 = the library's plan)")
+    ap.add_argument("--dcp", type=int, default=1,
+                    help="context-parallel ranks simulated on this GPU: times one rank's step (shard filter, "
+                         "decode on the rank's share of the cache, merge of all ranks' partials); decode_bf16 only")
+    ap.add_argument("--dcp-interleave", type=int, default=64, help="positions per run of the context-parallel placement")
+    ap.add_argument("--dcp-keep-positions", action="store_true",
+                    help="shard filter without compaction (the -1 entries stay where they are)")
     ap.add_argument("--separate-convert", action="store_true",
                     help="run smla_convert_indices as its own kernel in the step instead of in the attention kernel")
     args = ap.parse_args()
@@ -191,6 +197,8 @@ def main() -> int:
     from sparse_mla_attention_top_amd import inputs as I
     from sparse_mla_attention_top_amd import smla
 
+    if args.dcp > 1:
+        return run_dcp(args)
     dev = "cuda"
     spec = I.SPECS[args.config]
     entry = ENTRY[args.config]
@@ -329,6 +337,164 @@ def main() -> int:
         "attn_kernel_us": round(kern_ms * 1e3, 3),
         "alg_bytes_per_step": alg_bytes,
         "alg_flops_per_step": flops,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def run_dcp(args) -> int:
+    """One context-parallel rank's decode step, timed on this GPU: the rank's
+    shard filter over the top-k rows of request positions, the decode over its
+    share of the cache, and the merge of all ranks' partials (the other ranks'
+    partials are computed once, outside the timed region). The cache is laid out
+    over the ranks by the interleaved placement; the merged output is checked
+    against the unsharded decode."""
+    import numpy as np
+    import torch
+
+    from sparse_mla_attention_top_amd import inputs as I
+    from sparse_mla_attention_top_amd import smla
+
+    if args.config != "decode_bf16":
+        print("--dcp is measured on decode_bf16", file=sys.stderr)
+        return 2
+    dev = "cuda"
+    W, IL, B = args.dcp, args.dcp_interleave, I.BLOCK_SIZE
+    # compaction puts a rank's entries first, so its tiles hold only its rows
+    compact = not args.dcp_keep_positions
+    spec = I.SPECS[args.config]
+    w = I.generate(spec, kv_device=dev)
+    T, H, K = spec.num_tokens, spec.heads, spec.topk
+    nreq, ctx = spec.num_requests, spec.ctx_len
+    kv = w.kv_src                                                # [S, 576] bf16, global slots
+    bt, req, pos = w.block_table.to(dev), w.req_id.to(dev), w.topk_local.to(dev)
+    q = w.q.to(dev)
+    qn, qr = q[..., :512], q[..., 512:]
+    # placement of every (request, position): owning rank and local position
+    p_all = torch.arange(ctx, device=dev, dtype=torch.int64)
+    run = p_all // IL
+    owner, local = run % W, (run // W) * IL + p_all % IL
+    gen = torch.Generator(device="cpu").manual_seed(spec.seed * 1000 + 77)
+    R = max(1, args.rotate)
+    rank_caches, rank_tables = [], []
+    for r in range(W):
+        mine = torch.nonzero(owner == r).flatten()
+        n_r = mine.numel()
+        nb = (n_r + B - 1) // B
+        tab = torch.randperm(nreq * nb, generator=gen).view(nreq, nb).to(torch.int32).to(dev)
+        src = (bt[:, mine // B].long() * B + (mine % B)[None, :]).flatten()          # global slots
+        dst = (tab[:, local[mine] // B].long() * B + (local[mine] % B)[None, :]).flatten()
+        cache = torch.zeros((nreq * nb * B, spec.d), dtype=torch.bfloat16, device=dev)
+        cache[dst] = kv[src]
+        copies = [cache] + ([cache.clone() for _ in range(R - 1)] if r == 0 else [])
+        rank_caches.append(copies)
+        rank_tables.append(tab)
+    part_o = torch.empty((W, T, H, 512), dtype=torch.bfloat16, device=dev)
+    part_l = torch.empty((W, T, H), dtype=torch.float32, device=dev)
+    loc = torch.empty((T, K), dtype=torch.int32, device=dev)
+    out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(smla.decode_workspace_size(T, H, K), 16), dtype=torch.uint8, device=dev)
+    for r in range(1, W):                                        # the other ranks, once
+        lr, _ = smla.dcp_filter_convert(req, rank_tables[r], pos, W, r, IL, block_size=B, want_valid_counts=False,
+                                        compact_valid_to_front=compact)
+        smla.decode_fwd(qn, qr, rank_caches[r][0], lr, spec.softmax_scale, out=part_o[r], lse=part_l[r])
+
+    def step(k: int):
+        smla.dcp_filter_convert(req, rank_tables[0], pos, W, 0, IL, block_size=B, out=loc, want_valid_counts=False,
+                                compact_valid_to_front=compact)
+        smla.decode_fwd(qn, qr, rank_caches[0][k % R], loc, spec.softmax_scale, out=part_o[0], lse=part_l[0],
+                        workspace=ws)
+        smla.merge_partials(part_o, part_l, out=out, lse=lse)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    # the merged result against the unsharded decode
+    whole_o, whole_l = smla.decode_fwd(qn, qr, kv.view(spec.num_blocks, B, spec.d), pos, spec.softmax_scale,
+                                       block_table=bt, req_id=req, block_size=B)
+    torch.cuda.synchronize()
+    derr = (out.float() - whole_o.float()).abs().max().item()
+    lerr = (lse - whole_l).abs().max().item()
+    assert derr <= 2e-2 and lerr <= 2e-3, (derr, lerr)
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        step(0)
+        torch.cuda.current_stream().synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for k in range(R):
+                step(k)
+    torch.cuda.synchronize()
+    ref_o, ref_l = out.clone(), lse.clone()
+    g.replay()
+    torch.cuda.synchronize()
+    step(0)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)) and torch.equal(lse, ref_l)
+    replays = max(1, (args.steps + R - 1) // R)
+    steps = replays * R
+    t0 = time.perf_counter()
+    for _ in range(replays):
+        g.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+
+    # the rank's attention kernel alone (kernel timestamps)
+    n_ev = min(steps, 120)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    for a, b in evs:
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)
+    for k in range(n_ev):
+        smla.set_timing_events(*evs[k])
+        step(k)
+    smla.set_timing_events(None, None)
+    torch.cuda.synchronize()
+    kern_ms = sum(hip_elapsed_ms(a, b) for a, b in evs) / n_ev
+
+    # algorithmic bytes of the rank's attention: its rows, Q, its partial, indices
+    loc_np = loc.cpu().numpy()
+    rows0 = np.unique(loc_np[loc_np >= 0]).size
+    alg_bytes = rows0 * 1152 + T * H * 576 * 2 + T * H * (1024 + 4) + T * K * 4
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle on the rank's partial: global slots of the positions it owns
+        gidx, _ = smla.convert_indices(req, bt, pos)
+        own0 = (owner[pos.long()] == 0)
+        gmask = torch.where(own0, gidx, torch.full_like(gidx, -1)).cpu().numpy()
+        cpu = cpu_baseline(w, gmask, np.full(T, K, dtype=np.int32), args.cpu_seconds, 1.0)
+    line = {
+        "metric": "sparse-MLA context-parallel decode step, one rank of W (shard filter + attention on the "
+                  "rank's share + W-way LSE merge): query tokens/s",
+        "value": round(T * steps / dt, 1),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dt / steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.config] + f"; context spread over {W} simulated ranks, "
+                   f"interleave {IL}, rank 0 timed", "name": args.config, "dcp_size": W, "dcp_interleave": IL,
+                   "filter": "compact_valid_to_front" if compact else "positions kept",
+                   "num_tokens": T, "heads": H, "topk": K, "rank_rows_gathered": int(rows0),
+                   "cache_copies_rotated": R, "merged_vs_unsharded_max_abs": [derr, lerr],
+                   "timing": "HIP graph of R steps replayed; the other ranks' partials precomputed"},
+        "attn_kernel_us": round(kern_ms * 1e3, 3),
+        "alg_bytes_per_step": int(alg_bytes),
         "roofline": roof,
         "cpu_baseline": cpu,
     }

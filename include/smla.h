@@ -152,6 +152,58 @@ int smla_convert_indices(const int32_t* req_id, const int32_t* block_table,
                          int32_t* global_out, int64_t global_stride,
                          int32_t* valid_counts, void* stream);
 
+/*
+ * Context-parallel shard filter: one rank's view of top-k rows of request
+ * token positions (vLLM FlashMLA sparse backend, forward_mqa: the
+ * triton_filter_and_convert_dcp_index call with dcp_size, dcp_rank,
+ * cp_kv_cache_interleave_size and compact_valid_to_front). The pages name the
+ * parameters but print no placement; the one used is the plain interleave:
+ * runs of `interleave` consecutive positions of a request go to ranks 0, 1,
+ * .., dcp_size-1 in turn and each rank stores its runs back to back, so
+ * position p is on rank (p / I) % W at local position (p / (I W)) I + p % I.
+ * For entry p of row t with r = req_id[t]:
+ *     local_out[t][j] = block_table[r][q / block_size] * block_stride_rows
+ *                       + q % block_size,   q = the local position of p,
+ * if p >= 0, p is on rank dcp_rank and the lookup is valid as for
+ * smla_convert_indices (this rank's block table); else -1. With
+ * compact_valid_to_front != 0 the valid entries of a row come first in
+ * their order, then -1 (otherwise each entry keeps its position).
+ * valid_counts[t] (optional) = entries != -1. local_out may alias topk_tokens.
+ *   req_id [T] int32; block_table [num_reqs][bt_row_stride] int32 (this
+ *   rank's, first max_blocks used); topk_tokens [T][topk] int32 (row stride
+ *   topk_tokens_stride); local_out [T][topk] int32 (row stride local_stride).
+ * block_stride_rows = 0 means block_size.
+ */
+int smla_dcp_filter_convert(const int32_t* req_id, const int32_t* block_table, int32_t num_reqs,
+                            int32_t max_blocks, int64_t bt_row_stride, const int32_t* topk_tokens,
+                            int64_t topk_tokens_stride, int32_t num_tokens, int32_t topk,
+                            int32_t dcp_size, int32_t dcp_rank, int32_t interleave,
+                            int32_t block_size, int32_t block_stride_rows,
+                            int32_t compact_valid_to_front, int32_t* local_out,
+                            int64_t local_stride, int32_t* valid_counts, void* stream);
+
+/*
+ * Merge of partial attention results over disjoint parts of the same rows by
+ * their LSE, the cross-rank merge of the FlashMLA sparse docs
+ * (_forward_fp8_kv_mixed_batch; (0, -inf) is the identity):
+ *     lse[t][i] = ln sum_r exp(lse_r[t][i]),
+ *     out[t][i] = sum_r exp(lse_r[t][i] - lse[t][i]) * out_r[t][i]
+ * and (0, -inf) where every part is (0, -inf). The decode splits use the
+ * same kernel.
+ *   part_out bf16: part r, token t, head i, channel c at
+ *     part_out[r*stride_part + t*stride_tok + i*stride_head + c], c < 512;
+ *   part_lse fp32 at part_lse[r*lse_stride_part + t*lse_stride_tok + i];
+ *   out bf16 [T][h][512] by its strides; lse fp32 [T][h] or NULL.
+ * part_out and out 16-byte aligned, their strides multiples of 8 elements.
+ */
+int smla_merge_partials(const void* part_out, int64_t part_out_stride_part,
+                        int64_t part_out_stride_tok, int64_t part_out_stride_head,
+                        const float* part_lse, int64_t part_lse_stride_part,
+                        int64_t part_lse_stride_tok, int32_t num_parts, int32_t num_tokens,
+                        int32_t num_heads, void* out, int64_t out_stride_tok,
+                        int64_t out_stride_head, float* lse, int64_t lse_stride_tok,
+                        void* stream);
+
 /* Bytes of caller-owned device workspace smla_decode_fwd needs for these
  * shapes (0 when no split is used). num_splits = 0 means automatic. */
 size_t smla_decode_workspace_size(int32_t num_tokens, int32_t num_heads, int32_t topk,

@@ -55,7 +55,7 @@ struct KParams {
   int32_t num_tokens, num_heads;
   float scale_log2;   // softmax scale * log2(e)
   float out_mult;
-  int32_t splits, split_rows, longest_first;
+  int32_t splits, longest_first;
   int32_t head_blocks;  // 1 (<= 64 heads) or 2
   int32_t xcd_group;    // 1: all workgroups of token t run on XCD t % 8
   uint16_t* out;
@@ -197,13 +197,14 @@ smla_attn_kernel(KParams p) {
     if (p.longest_first) t = T - 1 - t;
   }
   const int hb = 64 * hblk;
-  const int row0 = split * p.split_rows;
-  const int cap = max(0, min(p.topk, row0 + p.split_rows) - row0);   // entries of this split
 
-  // ---- the split's index entries -> LDS (-1 marks an entry that does not take
-  //      part). Loaded without waiting for the row length; tiles past the last
-  //      valid entry (an invalid tail) are not visited.
-  const int32_t* irow = p.indices + (int64_t)t * p.idx_stride + row0;
+  // ---- the row's index entries -> LDS (-1 marks an entry that does not take
+  //      part), loaded without waiting for the row length. A split takes its
+  //      share of the entries up to the last valid one, so rows with an
+  //      invalid tail (short rows, a context-parallel shard compacted to the
+  //      front) spread over the splits too; tiles past the last valid entry
+  //      are not visited.
+  const int32_t* irow = p.indices + (int64_t)t * p.idx_stride;
   constexpr int kIdxPerThread = kMaxTopk / 512;
   int gi[kIdxPerThread];
   const bool convert = p.block_table != nullptr;
@@ -211,7 +212,7 @@ smla_attn_kernel(KParams p) {
 #pragma unroll
   for (int k = 0; k < kIdxPerThread; k++) {
     const int j = threadIdx.x + 512 * k;
-    gi[k] = (j < cap) ? irow[j] : -1;
+    gi[k] = (j < p.topk) ? irow[j] : -1;
   }
   if (convert) {
     // request-local index lc -> block_table[req][lc / B] * stride + lc % B
@@ -244,7 +245,7 @@ smla_attn_kernel(KParams p) {
   }
   int len = p.topk;
   if (p.topk_length) len = min(max(p.topk_length[t], 0), p.topk);
-  const int nrows = max(0, min(len, row0 + p.split_rows) - row0);
+  const int nrows = len;
   const int span = (nrows + kTileRows - 1) / kTileRows * kTileRows;
   int last = 0;
 #pragma unroll
@@ -264,7 +265,12 @@ smla_attn_kernel(KParams p) {
   int nlast = 0;
 #pragma unroll
   for (int k = 0; k < 8; k++) nlast = max(nlast, s_last[k]);
-  const int ntiles = (nlast + kTileRows - 1) / kTileRows;
+  // this split's entries [row0, row1): an equal, tile-aligned share of [0, nlast)
+  const int per = ((nlast + p.splits - 1) / p.splits + kTileRows - 1) / kTileRows * kTileRows;
+  const int row0 = min(split * per, nlast);
+  const int row1 = min(nlast, row0 + per);
+  const int ntiles = (row1 - row0 + kTileRows - 1) / kTileRows;
+  const int32_t* sidx = s_idx + row0;                      // entries of tile i: sidx[32 i ..]
 
   // address of chunk c (16 bytes of a bf16 row) of tile row r in bf16 tile i
   auto lat_buf = [&](int i) -> lds_char* { return lat + (i % NLAT) * kLatBytes; };
@@ -296,13 +302,13 @@ smla_attn_kernel(KParams p) {
     Src s;
     const int base = i * kTileRows + 8 * wu;
     if constexpr (!F8) {
-      s.lat = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + (l >> 3)], 0) * kv_stride + dcol);
+      s.lat = p.kv + ((uint64_t)(uint32_t)max(sidx[base + (l >> 3)], 0) * kv_stride + dcol);
     } else {
-      s.lat = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + (l >> 3)], 0) * kv_stride + 16 * (l & 7));
+      s.lat = p.kv + ((uint64_t)(uint32_t)max(sidx[base + (l >> 3)], 0) * kv_stride + 16 * (l & 7));
       if constexpr (S::ROPE)
-        s.rope = p.kv + ((uint64_t)(uint32_t)max(s_idx[base + ((l >> 2) & 7)], 0) * kv_stride + kDLatent + 16 * (l & 3));
+        s.rope = p.kv + ((uint64_t)(uint32_t)max(sidx[base + ((l >> 2) & 7)], 0) * kv_stride + kDLatent + 16 * (l & 3));
       if constexpr (S::GROUP)
-        s.sc = p.group_scales + ((uint64_t)(uint32_t)max(s_idx[base + srow], 0) * S::G + sgrp);
+        s.sc = p.group_scales + ((uint64_t)(uint32_t)max(sidx[base + srow], 0) * S::G + sgrp);
     }
     return s;
   };
@@ -620,7 +626,7 @@ smla_attn_kernel(KParams p) {
         float tv[2][4];
         float mx[2] = {-INFINITY, -INFINITY};
         if (have) {
-          vmask = (uint32_t)__ballot((l < 32) ? (s_idx[i * kTileRows + l] >= 0) : 0);
+          vmask = (uint32_t)__ballot((l < 32) ? (sidx[i * kTileRows + l] >= 0) : 0);
           scores(i, r0, r1);
           if (!full || i == 0) scaled(r0, r1, vmask, tv, mx);
         }
@@ -869,11 +875,13 @@ smla_attn_kernel(KParams p) {
   }
 }
 
-// Merge split partials by their LSE: lse = ln sum_s exp(lse_s),
+// Merge partial results by their LSE: lse = ln sum_s exp(lse_s),
 // out = sum_s exp(lse_s - lse) * O_s; (0, -inf) is the identity. Partials are
-// the normalised O_s in bf16.
+// the normalised O_s in bf16 (the decode splits, or the context-parallel
+// ranks' outputs: the cross-rank merge of the FlashMLA sparse docs).
 __global__ void __launch_bounds__(256)
-smla_combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict__ part_lse, int splits,
+smla_combine_kernel(const uint16_t* __restrict__ part_o, int64_t po_rank, int64_t po_tok, int64_t po_head,
+                    const float* __restrict__ part_lse, int64_t pl_rank, int64_t pl_tok, int splits,
                     int T, int H, uint16_t* __restrict__ out, int64_t out_st, int64_t out_sh,
                     float* __restrict__ lse, int64_t lse_st) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one thread = 8 channels
@@ -883,16 +891,18 @@ smla_combine_kernel(const uint16_t* __restrict__ part_o, const float* __restrict
   const int64_t th = gid / (kDLatent / 8);
   const int head = (int)(th % H);
   const int t = (int)(th / H);
+  const float* pl = part_lse + (int64_t)t * pl_tok + head;
+  const uint16_t* po = part_o + (int64_t)t * po_tok + (int64_t)head * po_head + 8 * c8;
   float m = -INFINITY;
-  for (int s = 0; s < splits; s++) m = fmaxf(m, part_lse[((int64_t)s * T + t) * H + head]);
+  for (int s = 0; s < splits; s++) m = fmaxf(m, pl[s * pl_rank]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float tot = 0.0f;
   if (m != -INFINITY) {
     for (int s = 0; s < splits; s++) {
-      const float ls = part_lse[((int64_t)s * T + t) * H + head];
+      const float ls = pl[s * pl_rank];
       const float wgt = (ls == -INFINITY) ? 0.0f : expf(ls - m);
       tot += wgt;
-      const u32x4 o = *(const u32x4*)(part_o + (((int64_t)s * T + t) * H + head) * kDLatent + 8 * c8);
+      const u32x4 o = *(const u32x4*)(po + s * po_rank);
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         acc[2 * i] += wgt * __builtin_bit_cast(float, o[i] << 16);
@@ -925,10 +935,6 @@ int32_t plan_splits(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t
   return max(1, min(s, max_splits));
 }
 
-static int32_t split_rows_for(int32_t topk, int32_t splits) {
-  int32_t r = (topk + splits - 1) / splits;
-  return (r + kTileRows - 1) / kTileRows * kTileRows;
-}
 
 size_t workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t splits) {
   (void)topk;
@@ -980,7 +986,6 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
     kp.out_mult = a.k_scale;
   }
   kp.splits = splits;
-  kp.split_rows = split_rows_for(a.topk, splits);
   kp.longest_first = longest_first ? 1 : 0;
   kp.head_blocks = a.num_heads > 64 ? 2 : 1;
   kp.xcd_group = a.num_tokens >= 8 ? 1 : 0;
@@ -1004,9 +1009,28 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || splits == 1) return e;
-  const int64_t total = (int64_t)a.num_tokens * a.num_heads * (kDLatent / 8);
+  MergeArgs m;
+  m.part_o = kp.part_o;
+  m.po_head = kDLatent;
+  m.po_tok = (int64_t)a.num_heads * kDLatent;
+  m.po_rank = (int64_t)a.num_tokens * m.po_tok;
+  m.part_lse = kp.part_lse;
+  m.pl_tok = a.num_heads;
+  m.pl_rank = (int64_t)a.num_tokens * a.num_heads;
+  m.parts = splits;
+  m.num_tokens = a.num_tokens;
+  m.num_heads = a.num_heads;
+  m.out = a.out; m.out_st = a.out_st; m.out_sh = a.out_sh;
+  m.lse = a.lse; m.lse_st = a.lse_st;
+  return launch_merge(m, stream);
+}
+
+hipError_t launch_merge(const MergeArgs& m, hipStream_t stream) {
+  const int64_t total = (int64_t)m.num_tokens * m.num_heads * (kDLatent / 8);
+  if (total == 0) return hipSuccess;
   smla_combine_kernel<<<(int)((total + 255) / 256), 256, 0, stream>>>(
-      kp.part_o, kp.part_lse, splits, a.num_tokens, a.num_heads, a.out, a.out_st, a.out_sh, a.lse, a.lse_st);
+      m.part_o, m.po_rank, m.po_tok, m.po_head, m.part_lse, m.pl_rank, m.pl_tok, m.parts, m.num_tokens,
+      m.num_heads, m.out, m.out_st, m.out_sh, m.lse, m.lse_st);
   return hipGetLastError();
 }
 

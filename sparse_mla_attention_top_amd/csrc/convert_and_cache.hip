@@ -63,6 +63,92 @@ convert_indices_kernel(const int32_t* __restrict__ req_id, const int32_t* __rest
   }
 }
 
+// Context-parallel shard filter (vLLM FlashMLA sparse backend, forward_mqa:
+// triton_filter_and_convert_dcp_index with dcp_size, dcp_rank,
+// cp_kv_cache_interleave_size and compact_valid_to_front). Entry p of row t
+// is a request token position; runs of `interleave` positions go to ranks 0,
+// 1, .., W-1 in turn and each rank stores its runs back to back, so p is on
+// rank (p / I) % W at local position (p / (I W)) I + p % I. Positions stored
+// on this rank are converted through this rank's block table as in
+// convert_indices_kernel, everything else becomes -1. With compact, the valid
+// entries of a row are written first in their order, then -1.
+// One workgroup per row, 8 consecutive entries per thread; the compaction
+// offsets come from a workgroup prefix sum of the per-thread counts.
+__global__ void __launch_bounds__(256)
+dcp_filter_kernel(const int32_t* __restrict__ req_id, const int32_t* __restrict__ block_table,
+                  int32_t num_reqs, int32_t max_blocks, int64_t bt_row_stride,
+                  const int32_t* __restrict__ topk_tokens, int64_t in_stride, int32_t topk,
+                  int32_t dcp_size, int32_t dcp_rank, int32_t interleave,
+                  int32_t block_size, int32_t block_stride_rows, int32_t compact,
+                  int32_t* __restrict__ out, int64_t out_stride, int32_t* __restrict__ valid_counts) {
+  __shared__ int s_wave[4];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t* src = topk_tokens + (int64_t)t * in_stride;
+  int32_t* dst = out + (int64_t)t * out_stride;
+  const int r = req_id[t];
+  const bool req_ok = (r >= 0) && (r < num_reqs);
+  const int32_t* bt = block_table + (int64_t)(req_ok ? r : 0) * bt_row_stride;
+  constexpr int PER = 8;
+  int running = 0;                                      // valid entries in earlier passes (uniform)
+  for (int base = 0; base < topk; base += 256 * PER) {
+    int g[PER];
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < PER; k++) {
+      const int j = base + PER * threadIdx.x + k;
+      const int pos = (j < topk) ? src[j] : -1;
+      int v = -1;
+      if (pos >= 0) {
+        const int run = pos / interleave;
+        if (run % dcp_size == dcp_rank) {
+          const int local = (run / dcp_size) * interleave + (pos - run * interleave);
+          const int blk = local / block_size;
+          if (req_ok && blk < max_blocks) {
+            const int e = bt[blk];
+            if (e >= 0) v = e * block_stride_rows + (local - blk * block_size);
+          }
+        }
+      }
+      g[k] = v;
+      c += (v >= 0);
+    }
+    if (!compact) {
+#pragma unroll
+      for (int k = 0; k < PER; k++) {
+        const int j = base + PER * threadIdx.x + k;
+        if (j < topk) dst[j] = g[k];
+      }
+    }
+    // workgroup prefix sum of the per-thread counts (thread order = entry order)
+    int x = c;
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) s_wave[wave] = x;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      const int sw = s_wave[w];
+      before += (w < wave) ? sw : 0;
+      total += sw;
+    }
+    __syncthreads();                                    // s_wave is rewritten by the next pass
+    if (compact) {
+      int at = running + before + x - c;                // exclusive offset of this thread's first valid entry
+#pragma unroll
+      for (int k = 0; k < PER; k++)
+        if (g[k] >= 0) dst[at++] = g[k];
+    }
+    running += total;
+  }
+  if (compact)
+    for (int j = running + threadIdx.x; j < topk; j += 256) dst[j] = -1;
+  if (valid_counts && threadIdx.x == 0) valid_counts[t] = running;
+}
+
 // E4M3FN code of an fp32 value: round to nearest, ties to even, |y| >= 448
 // saturates to 448, NaN -> 0x7F (sign kept). Integer implementation of the
 // OCP E4M3 format (bias 7, 3 mantissa bits, min normal 2^-6, step 2^-9 below).
@@ -152,6 +238,15 @@ hipError_t launch_convert(const ConvertArgs& a, hipStream_t stream) {
       a.req_id, a.block_table, a.num_reqs, a.max_blocks, a.bt_row_stride, a.topk_local,
       a.topk_local_stride, a.topk, a.block_size, a.block_stride_rows, a.global_out,
       a.global_stride, a.valid_counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_dcp_filter(const DcpFilterArgs& a, hipStream_t stream) {
+  if (a.num_tokens == 0) return hipSuccess;
+  dcp_filter_kernel<<<a.num_tokens, 256, 0, stream>>>(
+      a.req_id, a.block_table, a.num_reqs, a.max_blocks, a.bt_row_stride, a.topk_tokens, a.in_stride, a.topk,
+      a.dcp_size, a.dcp_rank, a.interleave, a.block_size, a.block_stride_rows, a.compact ? 1 : 0, a.out,
+      a.out_stride, a.valid_counts);
   return hipGetLastError();
 }
 

@@ -169,6 +169,67 @@ int smla_convert_indices(const int32_t* req_id, const int32_t* block_table, int3
   return hip_status(smla::launch_convert(a, (hipStream_t)stream), "convert_indices launch");
 }
 
+int smla_dcp_filter_convert(const int32_t* req_id, const int32_t* block_table, int32_t num_reqs,
+                            int32_t max_blocks, int64_t bt_row_stride, const int32_t* topk_tokens,
+                            int64_t topk_tokens_stride, int32_t num_tokens, int32_t topk, int32_t dcp_size,
+                            int32_t dcp_rank, int32_t interleave, int32_t block_size, int32_t block_stride_rows,
+                            int32_t compact_valid_to_front, int32_t* local_out, int64_t local_stride,
+                            int32_t* valid_counts, void* stream) {
+  if (num_tokens < 0 || topk < 0) return fail(SMLA_ERR_INVALID_ARG, "num_tokens/topk < 0");
+  if (dcp_size < 1 || dcp_rank < 0 || dcp_rank >= dcp_size)
+    return fail(SMLA_ERR_INVALID_ARG, "dcp_rank=%d outside 0..dcp_size-1 (dcp_size=%d)", dcp_rank, dcp_size);
+  if (interleave < 1) return fail(SMLA_ERR_INVALID_ARG, "interleave=%d must be >= 1", interleave);
+  if (block_size < 1) return fail(SMLA_ERR_INVALID_ARG, "block_size=%d must be >= 1", block_size);
+  if (block_stride_rows < 0) return fail(SMLA_ERR_INVALID_ARG, "block_stride_rows < 0");
+  if (num_reqs < 1 || max_blocks < 1 || bt_row_stride < max_blocks)
+    return fail(SMLA_ERR_INVALID_ARG, "block table shape invalid (num_reqs=%d max_blocks=%d stride=%lld)",
+                num_reqs, max_blocks, (long long)bt_row_stride);
+  if (topk_tokens_stride < topk || local_stride < topk) return fail(SMLA_ERR_INVALID_ARG, "row strides must be >= topk");
+  if (num_tokens == 0) return ok();
+  if (!req_id || !block_table || (topk > 0 && (!topk_tokens || !local_out)))
+    return fail(SMLA_ERR_INVALID_ARG, "NULL pointer argument");
+  smla::DcpFilterArgs a{req_id, block_table, num_reqs, max_blocks, bt_row_stride, topk_tokens, topk_tokens_stride,
+                        num_tokens, topk, dcp_size, dcp_rank, interleave, block_size,
+                        block_stride_rows == 0 ? block_size : block_stride_rows, compact_valid_to_front != 0,
+                        local_out, local_stride, valid_counts};
+  return hip_status(smla::launch_dcp_filter(a, (hipStream_t)stream), "dcp_filter_convert launch");
+}
+
+int smla_merge_partials(const void* part_out, int64_t part_out_stride_part, int64_t part_out_stride_tok,
+                        int64_t part_out_stride_head, const float* part_lse, int64_t part_lse_stride_part,
+                        int64_t part_lse_stride_tok, int32_t num_parts, int32_t num_tokens, int32_t num_heads,
+                        void* out, int64_t out_stride_tok, int64_t out_stride_head, float* lse,
+                        int64_t lse_stride_tok, void* stream) {
+  if (num_parts < 1 || num_tokens < 0 || num_heads < 1)
+    return fail(SMLA_ERR_INVALID_ARG, "num_parts=%d num_tokens=%d num_heads=%d", num_parts, num_tokens, num_heads);
+  if (num_tokens == 0) return ok();
+  if (!part_out || !part_lse || !out) return fail(SMLA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned16(part_out) || !aligned16(out) || part_out_stride_part % 8 || part_out_stride_tok % 8 ||
+      part_out_stride_head % 8 || out_stride_tok % 8 || out_stride_head % 8)
+    return fail(SMLA_ERR_INVALID_ARG, "part_out/out must be 16-byte aligned with strides that are multiples of 8 elements");
+  if (part_out_stride_head < 512 && num_heads > 1) return fail(SMLA_ERR_INVALID_ARG, "part_out_stride_head < 512");
+  if (out_stride_head < 512 && num_heads > 1) return fail(SMLA_ERR_INVALID_ARG, "out_stride_head < 512");
+  if (part_lse_stride_tok < num_heads || (lse && lse_stride_tok < num_heads))
+    return fail(SMLA_ERR_INVALID_ARG, "LSE token stride < num_heads");
+  smla::MergeArgs m;
+  m.part_o = (const uint16_t*)part_out;
+  m.po_rank = part_out_stride_part;
+  m.po_tok = part_out_stride_tok;
+  m.po_head = part_out_stride_head;
+  m.part_lse = part_lse;
+  m.pl_rank = part_lse_stride_part;
+  m.pl_tok = part_lse_stride_tok;
+  m.parts = num_parts;
+  m.num_tokens = num_tokens;
+  m.num_heads = num_heads;
+  m.out = (uint16_t*)out;
+  m.out_st = out_stride_tok;
+  m.out_sh = out_stride_head;
+  m.lse = lse;
+  m.lse_st = lse_stride_tok;
+  return hip_status(smla::launch_merge(m, (hipStream_t)stream), "merge_partials launch");
+}
+
 int32_t smla_decode_num_splits(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t num_splits) {
   return smla::plan_splits(num_tokens, num_heads, topk, num_splits);
 }

@@ -19,6 +19,34 @@ struct ConvertArgs {
   int32_t* valid_counts;
 };
 
+struct DcpFilterArgs {
+  const int32_t* req_id;
+  const int32_t* block_table;
+  int32_t num_reqs, max_blocks;
+  int64_t bt_row_stride;
+  const int32_t* topk_tokens;
+  int64_t in_stride;
+  int32_t num_tokens, topk, dcp_size, dcp_rank, interleave, block_size, block_stride_rows;
+  bool compact;
+  int32_t* out;
+  int64_t out_stride;
+  int32_t* valid_counts;
+};
+
+// Partial results to merge by LSE: out_r [T][H][512] bf16 and lse_r [T][H],
+// part r at part_o + r * po_rank (elements) and part_lse + r * pl_rank.
+struct MergeArgs {
+  const uint16_t* part_o;
+  int64_t po_rank, po_tok, po_head;
+  const float* part_lse;
+  int64_t pl_rank, pl_tok;
+  int32_t parts, num_tokens, num_heads;
+  uint16_t* out;
+  int64_t out_st, out_sh;
+  float* lse;
+  int64_t lse_st;
+};
+
 struct CacheWriteArgs {
   const uint16_t* kv_c;
   int64_t kv_c_stride;
@@ -70,6 +98,8 @@ int32_t plan_splits(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t
 size_t workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t splits);
 
 hipError_t launch_convert(const ConvertArgs& a, hipStream_t stream);
+hipError_t launch_dcp_filter(const DcpFilterArgs& a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
 // splits == 1: direct output. splits > 1: partials into workspace + combine.
 hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, bool longest_first,

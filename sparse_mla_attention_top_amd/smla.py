@@ -33,6 +33,8 @@ EXPORTED = (
     "smla_last_error",
     "smla_version",
     "smla_attn_args_size",
+    "smla_dcp_filter_convert",
+    "smla_merge_partials",
 )
 
 
@@ -95,6 +97,11 @@ def load() -> ctypes.CDLL:
     vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     lib.smla_convert_indices.argtypes = [vp, vp, i32, i32, i64, vp, i64, i32, i32, i32, i32, vp, i64, vp, vp]
     lib.smla_convert_indices.restype = ctypes.c_int
+    lib.smla_dcp_filter_convert.argtypes = [vp, vp, i32, i32, i64, vp, i64, i32, i32, i32, i32, i32, i32, i32, i32,
+                                            vp, i64, vp, vp]
+    lib.smla_dcp_filter_convert.restype = ctypes.c_int
+    lib.smla_merge_partials.argtypes = [vp, i64, i64, i64, vp, i64, i64, i32, i32, i32, vp, i64, i64, vp, i64, vp]
+    lib.smla_merge_partials.restype = ctypes.c_int
     lib.smla_decode_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.smla_decode_workspace_size.restype = sz
     lib.smla_decode_num_splits.argtypes = [i32, i32, i32, i32]
@@ -144,6 +151,12 @@ def _need(cond: bool, msg: str) -> None:
 # index conversion
 # ---------------------------------------------------------------------------
 
+def _bt_row_stride(block_table: torch.Tensor) -> int:
+    """Row stride of a [R, max_blocks] block table; a one-row table may carry any
+    stride for its size-1 dimension, so its row length is passed instead."""
+    return block_table.stride(0) if block_table.shape[0] > 1 else block_table.shape[1]
+
+
 def convert_indices(req_id: torch.Tensor, block_table: torch.Tensor, topk_local: torch.Tensor,
                     block_size: int = 64, block_stride_rows: int = 0,
                     out: Optional[torch.Tensor] = None, valid_counts: Optional[torch.Tensor] = None,
@@ -159,11 +172,59 @@ def convert_indices(req_id: torch.Tensor, block_table: torch.Tensor, topk_local:
     if valid_counts is None and want_valid_counts:
         valid_counts = torch.empty((T,), dtype=torch.int32, device=topk_local.device)
     rc = load().smla_convert_indices(_ptr(req_id), _ptr(block_table), block_table.shape[0], block_table.shape[1],
-                                     block_table.stride(0), _ptr(topk_local), topk_local.stride(0), T, K,
+                                     _bt_row_stride(block_table), _ptr(topk_local), topk_local.stride(0), T, K,
                                      block_size, block_stride_rows, _ptr(out), out.stride(0), _ptr(valid_counts),
                                      _stream(stream))
     _check("smla_convert_indices", rc)
     return out, valid_counts
+
+
+def dcp_filter_convert(req_id: torch.Tensor, block_table: torch.Tensor, topk_tokens: torch.Tensor,
+                       dcp_size: int, dcp_rank: int, interleave: int, block_size: int = 64,
+                       block_stride_rows: int = 0, compact_valid_to_front: bool = False,
+                       out: Optional[torch.Tensor] = None, valid_counts: Optional[torch.Tensor] = None,
+                       want_valid_counts: bool = True, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """One context-parallel rank's local cache slots for top-k rows of request
+    token positions (-1 where the position is on another rank)."""
+    _need(topk_tokens.dtype == torch.int32 and req_id.dtype == torch.int32 and block_table.dtype == torch.int32,
+          "int32 tensors expected")
+    _need(topk_tokens.dim() == 2 and topk_tokens.stride(1) == 1, "topk_tokens must be [T, K] with unit column stride")
+    _need(block_table.dim() == 2 and block_table.stride(1) == 1, "block_table must be [R, max_blocks]")
+    T, K = topk_tokens.shape
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.int32, device=topk_tokens.device)
+    if valid_counts is None and want_valid_counts:
+        valid_counts = torch.empty((T,), dtype=torch.int32, device=topk_tokens.device)
+    rc = load().smla_dcp_filter_convert(_ptr(req_id), _ptr(block_table), block_table.shape[0], block_table.shape[1],
+                                        _bt_row_stride(block_table), _ptr(topk_tokens), topk_tokens.stride(0), T, K,
+                                        dcp_size, dcp_rank, interleave, block_size, block_stride_rows,
+                                        1 if compact_valid_to_front else 0, _ptr(out), out.stride(0),
+                                        _ptr(valid_counts), _stream(stream))
+    _check("smla_dcp_filter_convert", rc)
+    return out, valid_counts
+
+
+def merge_partials(part_out: torch.Tensor, part_lse: torch.Tensor, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+                   stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Merge partials part_out [P, T, h, 512] bf16 / part_lse [P, T, h] fp32
+    by their LSE. Returns (out [T, h, 512] bf16, lse [T, h] fp32 or None)."""
+    _need(part_out.dtype == torch.bfloat16 and part_out.dim() == 4 and part_out.shape[3] == 512
+          and part_out.stride(3) == 1, "part_out must be bf16 [P, T, h, 512] with unit channel stride")
+    P, T, H, _ = part_out.shape
+    _need(part_lse.dtype == torch.float32 and part_lse.shape == (P, T, H) and part_lse.stride(2) == 1,
+          "part_lse must be fp32 [P, T, h]")
+    if out is None:
+        out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=part_out.device)
+    _need(out.dtype == torch.bfloat16 and out.shape == (T, H, 512) and out.stride(2) == 1, "out must be bf16 [T, h, 512]")
+    if lse is None and return_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=part_out.device)
+    rc = load().smla_merge_partials(_ptr(part_out), part_out.stride(0), part_out.stride(1), part_out.stride(2),
+                                    _ptr(part_lse), part_lse.stride(0), part_lse.stride(1), P, T, H,
+                                    _ptr(out), out.stride(0), out.stride(1), _ptr(lse),
+                                    lse.stride(0) if lse is not None else 0, _stream(stream))
+    _check("smla_merge_partials", rc)
+    return out, lse
 
 
 # ---------------------------------------------------------------------------
@@ -244,7 +305,7 @@ def _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk
         a.req_id = _ptr(req_id)
         a.block_table = _ptr(block_table)
         a.num_reqs, a.max_blocks = block_table.shape
-        a.bt_row_stride = block_table.stride(0)
+        a.bt_row_stride = _bt_row_stride(block_table)
         a.block_size = int(block_size)
         a.block_stride_rows = int(block_stride_rows)
     return a, out, lse

@@ -92,3 +92,17 @@ def test_split_plan_is_shape_only():
     assert smla.decode_num_splits(32, 128, 2048, 3) == 3
     assert smla.decode_workspace_size(32, 128, 2048) == 4 * 32 * 128 * (512 * 2 + 4)
     assert smla.decode_workspace_size(4096, 128, 2048) == 0
+
+
+def test_dcp_filter_and_merge_reject_bad_arguments():
+    lib = smla.load()
+    # dcp_rank outside 0..dcp_size-1, interleave 0
+    assert lib.smla_dcp_filter_convert(None, None, 1, 1, 1, None, 4, 1, 4, 2, 2, 1, 64, 0, 0, None, 4, None, None) == -1
+    assert lib.smla_dcp_filter_convert(None, None, 1, 1, 1, None, 4, 1, 4, 2, 0, 0, 64, 0, 0, None, 4, None, None) == -1
+    assert lib.smla_dcp_filter_convert(None, None, 1, 1, 1, None, 4, 1, 4, 2, 0, 1, 64, 0, 0, None, 4, None, None) == -1
+    assert lib.smla_last_error()
+    # no parts, and NULL pointers with tokens to merge
+    assert lib.smla_merge_partials(None, 0, 0, 0, None, 0, 0, 0, 1, 1, None, 0, 0, None, 0, None) == -1
+    assert lib.smla_merge_partials(None, 0, 0, 512, None, 0, 1, 2, 1, 1, None, 512, 512, None, 1, None) == -1
+    # zero tokens is a no-op
+    assert lib.smla_merge_partials(None, 0, 0, 512, None, 0, 1, 2, 0, 1, None, 512, 512, None, 1, None) == 0

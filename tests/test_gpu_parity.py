@@ -304,6 +304,20 @@ def test_deterministic_bitwise():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
 
 
+@pytest.mark.parametrize("splits", [2, 8, 64])
+def test_splits_share_the_valid_prefix(splits):
+    """Splits divide the entries up to the last valid one: rows of 2048, 700,
+    100, 33, 1 and 0 valid entries (a -1 tail, no row lengths given), so
+    that short rows leave some splits empty."""
+    say(f"splits share the valid prefix, splits={splits}")
+    c = I.random_case(T=6, h=64, d_rope=64, topk=2048, num_slots=4096, seed=40 + splits,
+                      lengths=[2048, 700, 100, 33, 1, 0])
+    q, kv, idx = c.q.to(DEV), c.kv_src.to(DEV), c.indices.to(DEV)
+    o, l = smla.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, num_splits=splits)
+    torch.cuda.synchronize()
+    compare(o, l, oracle_for(c.q, bits(c.kv_src), c.indices.numpy(), 0.07), f"prefix splits={splits}")
+
+
 def test_split_workspace_reused_across_shapes():
     """One caller-owned workspace serves decode calls of different shapes and
     split counts: 4 splits with each token's workgroups on one XCD (8 tokens),
