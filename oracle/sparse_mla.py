@@ -15,13 +15,26 @@ What is computed, with the passage each step follows:
 * ``dequantize_rows`` -- cache rows to fp64: bf16 exactly; E4M3FN bytes times
   the per-tensor scale or the per-token x 128-channel-group scale
   (flashinfer_mla_sparse_sm90.py, module docstring).
+* ``dequantize_rows`` for the packed 656-byte format (FlashMLA sparse
+  backend: 656 bytes per token for its FP8 cache; CUTLASS FA3 sparse backend
+  docstring, "Key differences"). The pages give the size only; the reading
+  used is the split the size allows with the group scales of the other FP8
+  format: bytes 0..511 the E4M3FN codes of the 512 latent channels, bytes
+  512..527 four little-endian fp32 scales (latent group g = channels
+  128g..128g+127), bytes 528..655 the 64 rope channels as plain bf16.
 * ``attention`` -- per query token and head: scores over the token's valid
   top-k slots, s = scale * q . k over all D channels, softmax, output
   sum_j p_j * k[:512] in the 512-dim latent space, and LSE = ln sum exp(s)
   (FA3 kernel test file, ``test_fa3_mla_correctness_vs_reference``: the
   gathered K = [c_kv | k_rope], V = c_kv, SDPA with the given scale; FlashMLA
   sparse API docs, ``_forward_fp8_kv_mixed_batch``: LSE per (token, head),
-  rows with no valid slot give (0, -inf)).
+  rows with no valid slot give (0, -inf)). Two options of the FA3 API
+  (``flash_attn_with_kvcache`` arguments ``softcap`` and ``sinks``), whose
+  formulas the pages do not print, are read as: softcap c > 0 replaces each
+  scaled logit z by c * tanh(z / c) (0 disables it); a sink is one logit per
+  head that joins the softmax denominator with a zero value row, so
+  out = sum_j e^z_j v_j / (sum_j e^z_j + e^sink) and LSE = ln of that
+  denominator; an empty row then gives (0, sink).
 * ``dcp_filter_convert`` -- one context-parallel rank's share of a top-k row
   of request token positions: the positions this rank stores, converted to
   its local cache slots through its own block table, -1 elsewhere, optionally
@@ -59,8 +72,13 @@ from . import e4m3
 KV_BF16 = 0
 KV_FP8_PER_TENSOR = 1
 KV_FP8_GROUP128 = 2
+KV_FP8_DS_MLA = 3
 D_V = 512
 GROUP = 128
+# packed row: [512 E4M3FN codes | 4 fp32 group scales | 64 bf16 rope channels]
+DS_MLA_SCALES_AT = 512
+DS_MLA_ROPE_AT = 528
+DS_MLA_ROW_BYTES = 656
 
 
 # ---------------------------------------------------------------------------
@@ -114,14 +132,39 @@ def convert_indices(req_id: np.ndarray, block_table: np.ndarray, topk_local: np.
 # dequantization
 # ---------------------------------------------------------------------------
 
+def pack_ds_mla(codes: np.ndarray, scales: np.ndarray, rope_bits: np.ndarray) -> np.ndarray:
+    """Packed rows [n, 656] uint8 from latent codes [n, 512] uint8, group
+    scales [n, 4] fp32 and rope bf16 bits [n, 64]."""
+    n = codes.shape[0]
+    out = np.empty((n, DS_MLA_ROW_BYTES), dtype=np.uint8)
+    out[:, :DS_MLA_SCALES_AT] = codes
+    out[:, DS_MLA_SCALES_AT:DS_MLA_ROPE_AT] = np.ascontiguousarray(scales, dtype="<f4").view(np.uint8)
+    out[:, DS_MLA_ROPE_AT:] = np.ascontiguousarray(rope_bits, dtype="<u2").view(np.uint8)
+    return out
+
+
+def unpack_ds_mla(rows: np.ndarray):
+    """(codes [n, 512], scales [n, 4] fp32, rope bf16 bits [n, 64]) of packed
+    rows (the first 656 bytes of each row are used)."""
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.uint8)[:, :DS_MLA_ROW_BYTES])
+    codes = rows[:, :DS_MLA_SCALES_AT]
+    scales = np.ascontiguousarray(rows[:, DS_MLA_SCALES_AT:DS_MLA_ROPE_AT]).view("<f4")
+    rope = np.ascontiguousarray(rows[:, DS_MLA_ROPE_AT:]).view("<u2")
+    return codes, scales.astype(np.float32), rope.astype(np.uint16)
+
+
 def dequantize_rows(cache: np.ndarray, kv_format: int, slots: np.ndarray,
                     k_scale: float = 1.0, group_scales: Optional[np.ndarray] = None,
                     d: Optional[int] = None) -> np.ndarray:
-    """Rows ``slots`` of a flat cache ([S, D] uint16 bf16 bits, or [S, D] uint8
-    E4M3FN codes) as float64 values."""
+    """Rows ``slots`` of a flat cache ([S, D] uint16 bf16 bits, [S, D] uint8
+    E4M3FN codes, or [S, >= 656] uint8 packed rows) as float64 values."""
     slots = np.asarray(slots, dtype=np.int64)
     if kv_format == KV_BF16:
         return bf16_bits_to_f64(cache[slots])
+    if kv_format == KV_FP8_DS_MLA:
+        codes, sc, rope = unpack_ds_mla(cache[slots])
+        lat = e4m3.decode(codes) * np.repeat(sc.astype(np.float64), GROUP, axis=1)
+        return np.concatenate([lat, bf16_bits_to_f64(rope)], axis=1)
     vals = e4m3.decode(cache[slots])
     if kv_format == KV_FP8_PER_TENSOR:
         return vals * float(np.float32(k_scale))
@@ -147,19 +190,30 @@ def valid_entries(idx_row: np.ndarray, length: Optional[int], num_slots: int) ->
 
 
 def attention_rows(q_t: np.ndarray, rows: np.ndarray, scale: float, d_v: int = D_V,
-                   magnitude: bool = False):
+                   magnitude: bool = False, softcap: float = 0.0,
+                   sinks: Optional[np.ndarray] = None):
     """One query token: q_t [h, D] and its gathered rows [v, D] (fp64).
     Returns out [h, d_v], lse [h]; with ``magnitude`` also
     mag [h, d_v] = sum_j p_j |v_j|, the size against which rounding of the
-    terms p_j v_j of the output is measured (0 for an empty row)."""
+    terms p_j v_j of the output is measured (0 for an empty row).
+    softcap > 0: logits z = softcap * tanh(scale q.k / softcap). sinks [h]:
+    one extra logit per head in the denominator, with a zero value row."""
     h = q_t.shape[0]
+    sink = None if sinks is None else np.asarray(sinks, dtype=np.float64).reshape(h)
     if rows.shape[0] == 0:
-        empty = (np.zeros((h, d_v)), np.full(h, -np.inf))
+        lse0 = np.full(h, -np.inf) if sink is None else sink.copy()
+        empty = (np.zeros((h, d_v)), lse0)
         return empty + (np.zeros((h, d_v)),) if magnitude else empty
     s = scale * (q_t @ rows.T)                      # [h, v]
+    if softcap > 0:
+        s = softcap * np.tanh(s / softcap)
     m = s.max(axis=1, keepdims=True)
+    if sink is not None:
+        m = np.maximum(m, sink[:, None])
     p = np.exp(s - m)
     l = p.sum(axis=1, keepdims=True)
+    if sink is not None:
+        l = l + np.exp(sink[:, None] - m)
     out = (p @ rows[:, :d_v]) / l
     lse = (m + np.log(l))[:, 0]
     if magnitude:
@@ -170,29 +224,32 @@ def attention_rows(q_t: np.ndarray, rows: np.ndarray, scale: float, d_v: int = D
 def attention(q: np.ndarray, cache: np.ndarray, kv_format: int, indices: np.ndarray,
               softmax_scale: float, topk_length: Optional[np.ndarray] = None,
               k_scale: float = 1.0, group_scales: Optional[np.ndarray] = None,
-              tokens: Optional[np.ndarray] = None, d_v: int = D_V):
+              tokens: Optional[np.ndarray] = None, d_v: int = D_V, softcap: float = 0.0,
+              sinks: Optional[np.ndarray] = None):
     """Sparse MLA forward over global slot indices.
 
     q: [T, h, D] float64 (already the bf16 values); cache: flat [S, D] in the
     storage format; indices: [T, K] global slots. Only the listed ``tokens``
-    (default all) are computed. Returns out [n, h, d_v], lse [n, h] fp64."""
+    (default all) are computed. Returns out [n, h, d_v], lse [n, h] fp64.
+    ``softcap`` and ``sinks`` [h] as in ``attention_rows``."""
     res = _attention(q, cache, kv_format, indices, softmax_scale, topk_length, k_scale, group_scales,
-                     tokens, d_v, False)
+                     tokens, d_v, False, softcap, sinks)
     return res[0], res[1]
 
 
 def attention_with_magnitude(q: np.ndarray, cache: np.ndarray, kv_format: int, indices: np.ndarray,
                              softmax_scale: float, topk_length: Optional[np.ndarray] = None,
                              k_scale: float = 1.0, group_scales: Optional[np.ndarray] = None,
-                             tokens: Optional[np.ndarray] = None, d_v: int = D_V):
+                             tokens: Optional[np.ndarray] = None, d_v: int = D_V,
+                             softcap: float = 0.0, sinks: Optional[np.ndarray] = None):
     """``attention`` plus mag [n, h, d_v] = sum_j p_j |v_j| per output element
     (the softmax-weighted sum of the magnitudes of the value rows)."""
     return _attention(q, cache, kv_format, indices, softmax_scale, topk_length, k_scale, group_scales,
-                      tokens, d_v, True)
+                      tokens, d_v, True, softcap, sinks)
 
 
 def _attention(q, cache, kv_format, indices, softmax_scale, topk_length, k_scale, group_scales,
-               tokens, d_v, magnitude):
+               tokens, d_v, magnitude, softcap=0.0, sinks=None):
     tokens = np.arange(q.shape[0]) if tokens is None else np.asarray(tokens)
     S = cache.shape[0]
     outs, lses, mags = [], [], []
@@ -200,7 +257,7 @@ def _attention(q, cache, kv_format, indices, softmax_scale, topk_length, k_scale
         length = None if topk_length is None else int(topk_length[t])
         sel = valid_entries(indices[t], length, S)
         rows = dequantize_rows(cache, kv_format, sel, k_scale, group_scales)
-        r = attention_rows(q[t], rows, softmax_scale, d_v, magnitude)
+        r = attention_rows(q[t], rows, softmax_scale, d_v, magnitude, softcap, sinks)
         outs.append(r[0])
         lses.append(r[1])
         if magnitude:
@@ -304,8 +361,11 @@ def cache_write(kv_c_bits: np.ndarray, k_pe_bits: Optional[np.ndarray], slot_map
                 kv_format: int, cache: np.ndarray, k_scale: float = 1.0,
                 group_scales: Optional[np.ndarray] = None) -> None:
     """Write rows [kv_c | k_pe] into ``cache`` (flat [S, D]: uint16 bf16 bits or
-    uint8 codes) at slot_mapping; slots < 0 are skipped. In group mode the
-    per-row scales go to ``group_scales`` [S, ceil(D/128)]."""
+    uint8 codes; packed format: [S, >= 656] uint8) at slot_mapping; slots < 0
+    are skipped. In group mode the per-row scales go to ``group_scales``
+    [S, ceil(D/128)]; the packed format quantizes the 512 latent channels per
+    128-channel group with the same scale rule, stores the scales in the row
+    and copies the 64 rope channels as bf16."""
     kv_c = np.asarray(kv_c_bits).view(np.uint16)
     rows = kv_c if k_pe_bits is None or np.asarray(k_pe_bits).shape[-1] == 0 else \
         np.concatenate([kv_c, np.asarray(k_pe_bits).view(np.uint16)], axis=1)
@@ -320,5 +380,10 @@ def cache_write(kv_c_bits: np.ndarray, k_pe_bits: Optional[np.ndarray], slot_map
         codes, sc = quantize_group128(rows)
         cache[slots] = codes
         group_scales[slots] = sc
+    elif kv_format == KV_FP8_DS_MLA:
+        if rows.shape[1] != D_V + 64:
+            raise ValueError("the packed format holds 512 latent + 64 rope channels")
+        codes, sc = quantize_group128(rows[:, :D_V])
+        cache[slots, :DS_MLA_ROW_BYTES] = pack_ds_mla(codes, sc, rows[:, D_V:])
     else:
         raise ValueError(kv_format)

@@ -473,12 +473,12 @@ def test_planted_mistakes_are_caught(monkeypatch):
 
     real = O.attention_rows
 
-    def no_max_in_lse(q_t, rows, scale, d_v=512, magnitude=False):   # dropped term
+    def no_max_in_lse(q_t, rows, scale, d_v=512, magnitude=False, *opts):   # dropped term
         o, l = real(q_t, rows, scale, d_v)
         s = scale * (q_t @ rows.T)
         return o, l - s.max(axis=1)
 
-    def rope_dropped(q_t, rows, scale, d_v=512, magnitude=False):     # wrong channel range
+    def rope_dropped(q_t, rows, scale, d_v=512, magnitude=False, *opts):     # wrong channel range
         return real(q_t[:, :512], rows[:, :512], scale, d_v)
 
     for bad in (no_max_in_lse, rope_dropped):
@@ -486,3 +486,155 @@ def test_planted_mistakes_are_caught(monkeypatch):
         o, l = O.attention(q, cache, O.KV_BF16, idx, 0.05)
         assert abs(l[0, 1] - bl) > 1e-6 or np.abs(o[0, 1] - bo).max() > 1e-6
         monkeypatch.setattr(O, "attention_rows", real)
+
+
+# ---------------------------------------------------------------------------
+# packed 656-byte FP8 rows (layout read from the size: 512 codes, 4 fp32
+# group scales, 64 bf16 rope channels)
+# ---------------------------------------------------------------------------
+
+def test_ds_mla_hand_built_row():
+    """A row assembled byte by byte decodes to the values worked out by hand."""
+    import struct
+    row = bytearray(656)
+    row[0] = 0x38            # 1.0      (group 0)
+    row[127] = 0xC0          # -2.0     (group 0)
+    row[128] = 0x7E          # 448      (group 1)
+    row[300] = 0x01          # 2^-9     (group 2)
+    row[511] = 0x30          # 0.5      (group 3)
+    row[512:528] = struct.pack("<4f", 0.5, 0.25, 2.0, 8.0)
+    row[528:530] = bytes([0x80, 0x3F])    # rope channel 0 = bf16 1.0
+    row[654:656] = bytes([0x40, 0xC0])    # rope channel 63 = bf16 -3.0
+    cache = np.zeros((3, 656), np.uint8)
+    cache[2] = np.frombuffer(bytes(row), np.uint8)
+    v = O.dequantize_rows(cache, O.KV_FP8_DS_MLA, np.array([2, 0]))
+    assert v.shape == (2, 576)
+    expect = np.zeros(576)
+    expect[0], expect[127], expect[128], expect[300], expect[511] = 0.5, -1.0, 112.0, 2.0 ** -8, 4.0
+    expect[512], expect[575] = 1.0, -3.0
+    assert (v[0] == expect).all()
+    assert (v[1] == 0).all()
+    assert O.DS_MLA_ROW_BYTES == 512 + 4 * 4 + 64 * 2 == 656   # the pages' bytes per token
+
+
+def test_ds_mla_cache_write_roundtrip():
+    """Packed write then read back: latent within half an E4M3 step of x per
+    group scale (each group's absmax lands on +-448 scale), rope exact,
+    negative slots skipped, bytes past 656 untouched."""
+    rng = np.random.default_rng(21)
+    T = 40
+    kv_c = _rand_bf16(rng, (T, 512))
+    k_pe = _rand_bf16(rng, (T, 64))
+    kv_c[3, 128:256] = 0                                  # an all-zero group
+    slots = rng.permutation(64)[:T].astype(np.int64)
+    slots[5] = -1
+    cache = np.full((64, 672), 0xAB, np.uint8)
+    O.cache_write(kv_c, k_pe, slots, O.KV_FP8_DS_MLA, cache)
+    keep = slots >= 0
+    assert (cache[:, 656:] == 0xAB).all()
+    untouched = np.setdiff1d(np.arange(64), slots[keep])
+    assert (cache[untouched] == 0xAB).all()
+    v = O.dequantize_rows(cache, O.KV_FP8_DS_MLA, slots[keep])
+    x = O.bf16_bits_to_f64(np.concatenate([kv_c, k_pe], axis=1))[keep]
+    assert (v[:, 512:] == x[:, 512:]).all()
+    codes, sc, rope = O.unpack_ds_mla(cache[slots[keep]])
+    for g in range(4):
+        c0, c1 = 128 * g, 128 * g + 128
+        amax = np.abs(x[:, c0:c1]).max(axis=1)
+        expect_sc = np.where(amax == 0, 1.0, (amax / 448.0).astype(np.float32))
+        assert (sc[:, g] == expect_sc.astype(np.float32)).all()
+        y = x[:, c0:c1] / sc[:, g:g + 1].astype(np.float64)
+        dec = v[:, c0:c1] / sc[:, g:g + 1].astype(np.float64)
+        assert (np.abs(dec - y) <= np.abs(y) / 16 + 2.0 ** -10 + 1e-12).all()
+        nz = amax > 0
+        assert (np.abs(dec[nz]).max(axis=1) == 448.0).all()
+
+
+def test_ds_mla_latent_matches_group_format():
+    """The packed latent decodes like the separate-scale group format with the
+    same codes and scales; the rope part like a bf16 cache."""
+    rng = np.random.default_rng(22)
+    codes = rng.integers(0, 0x7E, (7, 512)).astype(np.uint8)
+    codes[:, ::5] |= 0x80
+    scales = rng.uniform(0.001, 0.05, (7, 4)).astype(np.float32)
+    rope = _rand_bf16(rng, (7, 64))
+    packed = O.pack_ds_mla(codes, scales, rope)
+    slots = np.array([6, 1, 3])
+    a = O.dequantize_rows(packed, O.KV_FP8_DS_MLA, slots)
+    b = O.dequantize_rows(codes, O.KV_FP8_GROUP128, slots, group_scales=scales)
+    c = O.dequantize_rows(rope, O.KV_BF16, slots)
+    assert (a[:, :512] == b).all() and (a[:, 512:] == c).all()
+
+
+# ---------------------------------------------------------------------------
+# logit softcap and attention sinks
+# ---------------------------------------------------------------------------
+
+def test_softcap_closed_forms():
+    """One slot: out = its value row, lse = c tanh(s / c). Two slots: the
+    weights are e^{c tanh(s_j / c)}, written out with scalar math."""
+    rng = np.random.default_rng(23)
+    q, cache, _ = _setup(rng, T=1, h=3, K=2)
+    kv = O.bf16_bits_to_f64(cache)
+    scale, cap = 0.3, 2.5
+    idx1 = np.array([[7, -1]], np.int32)
+    o, l = O.attention(q, cache, O.KV_BF16, idx1, scale, softcap=cap)
+    for i in range(3):
+        s = scale * float(q[0, i] @ kv[7])
+        assert abs(l[0, i] - cap * math.tanh(s / cap)) < 1e-12
+        assert np.abs(o[0, i] - kv[7, :512]).max() < 1e-12
+    idx2 = np.array([[7, 11]], np.int32)
+    o, l = O.attention(q, cache, O.KV_BF16, idx2, scale, softcap=cap)
+    for i in range(3):
+        z = [cap * math.tanh(scale * float(q[0, i] @ kv[g]) / cap) for g in (7, 11)]
+        w = [math.exp(zz) for zz in z]
+        assert abs(l[0, i] - math.log(w[0] + w[1])) < 1e-12
+        ref = (w[0] * kv[7, :512] + w[1] * kv[11, :512]) / (w[0] + w[1])
+        assert np.abs(o[0, i] - ref).max() < 1e-12
+
+
+def test_softcap_bounds_logits_and_vanishes_for_large_caps():
+    rng = np.random.default_rng(24)
+    q, cache, idx = _setup(rng, T=2, h=4, K=30)
+    o0, l0 = O.attention(q, cache, O.KV_BF16, idx, 0.05)
+    o1, l1 = O.attention(q, cache, O.KV_BF16, idx, 0.05, softcap=1e7)
+    assert np.abs(o1 - o0).max() < 1e-9 and np.abs(l1 - l0).max() < 1e-9
+    # a tiny cap squeezes every logit into (-c, c): lse within ln(v) +- c
+    cap = 1e-3
+    _, lc = O.attention(q, cache, O.KV_BF16, idx, 50.0, softcap=cap)
+    v = np.array([(idx[t] >= 0).sum() for t in range(2)], np.float64)
+    assert (np.abs(lc - np.log(v)[:, None]) <= cap + 1e-12).all()
+
+
+def test_sink_closed_forms_and_identity():
+    rng = np.random.default_rng(25)
+    q, cache, idx = _setup(rng, T=2, h=3, K=12)
+    kv = O.bf16_bits_to_f64(cache)
+    scale = 0.07
+    # sink = -inf is no sink at all
+    o0, l0 = O.attention(q, cache, O.KV_BF16, idx, scale)
+    o1, l1 = O.attention(q, cache, O.KV_BF16, idx, scale, sinks=np.full(3, -np.inf))
+    assert (o1 == o0).all() and (l1 == l0).all()
+    # one slot: lse = ln(e^s + e^sink), out = V e^s / (e^s + e^sink)
+    sinks = np.array([-1.0, 0.5, 3.0])
+    o, l = O.attention(q[:1], cache, O.KV_BF16, np.array([[5, -1]], np.int32), scale, sinks=sinks)
+    for i in range(3):
+        s = scale * float(q[0, i] @ kv[5])
+        den = math.exp(s) + math.exp(sinks[i])
+        assert abs(l[0, i] - math.log(den)) < 1e-12
+        assert np.abs(o[0, i] - kv[5, :512] * math.exp(s) / den).max() < 1e-12
+    # empty row: (0, sink)
+    o, l = O.attention(q[:1], cache, O.KV_BF16, np.full((1, 4), -1, np.int32), scale, sinks=sinks)
+    assert (o == 0).all() and (l[0] == sinks).all()
+
+
+def test_sink_is_a_merge_with_a_zero_partial():
+    """The sink acts as one more partial result (0, sink) merged by LSE."""
+    rng = np.random.default_rng(26)
+    q, cache, idx = _setup(rng, T=3, h=4, K=25)
+    sinks = np.array([-2.0, 0.0, 1.5, 8.0])
+    o0, l0 = O.attention(q, cache, O.KV_BF16, idx, 0.05, softcap=4.0)
+    o1, l1 = O.attention(q, cache, O.KV_BF16, idx, 0.05, softcap=4.0, sinks=sinks)
+    zero = np.zeros_like(o0)
+    mo, ml = O.merge_partials(np.stack([o0, zero]), np.stack([l0, np.broadcast_to(sinks, l0.shape)]))
+    assert np.abs(mo - o1).max() < 1e-12 and np.abs(ml - l1).max() < 1e-12
