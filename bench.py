@@ -34,10 +34,15 @@ WORKLOAD_TEXT = {
     "longctx_fp8": "sparse MLA long-context decode, FP8 E4M3 cache [65536,64,576] with per-row x 128-channel "
                    "group scales: 64 requests x 65536 context, 4 query tokens each (256), h=128, top-k=2048 "
                    "all valid, random block table, scale 192^-0.5, out + LSE",
+    "longctx_ds_mla": "sparse MLA long-context decode, packed 656-byte FP8 rows [65536,64,656] (512 E4M3 latent "
+                      "codes, 4 fp32 group scales, 64 bf16 rope channels): 64 requests x 65536 context, 4 query "
+                      "tokens each (256), h=128, top-k=2048 all valid, random block table, scale 192^-0.5, out + LSE",
     "tiny": "tiny sparse MLA: 4 tokens, h=16, top-k=64, cache 256 x 576 bf16",
 }
 ENTRY = {"decode_bf16": "decode", "prefill_bf16": "prefill", "nope_fp8": "decode", "longctx_fp8": "decode",
-         "tiny": "decode"}
+         "longctx_ds_mla": "decode", "tiny": "decode"}
+KV_STORAGE = ["bf16", "e4m3 per-tensor scale", "e4m3 per-row x 128-group scales",
+              "packed 656-byte rows: e4m3 latent + 4 fp32 group scales + bf16 rope"]
 
 
 def source_hash() -> str:
@@ -115,6 +120,9 @@ def cpu_baseline(w, gidx_np, valid_np, min_seconds: float, k_scale: float):
         cache = rows_bits
     elif spec.kv_format == O.KV_FP8_PER_TENSOR:
         cache = O.quantize_per_tensor(rows_bits, k_scale)
+    elif spec.kv_format == O.KV_FP8_DS_MLA:
+        cache = np.zeros((rows_bits.shape[0], O.DS_MLA_ROW_BYTES), np.uint8)
+        O.cache_write(rows_bits[:, :512], rows_bits[:, 512:], np.arange(rows_bits.shape[0]), O.KV_FP8_DS_MLA, cache)
     else:
         cache, scales = O.quantize_group128(rows_bits)
     n_tok, reps = 0, 0
@@ -153,13 +161,14 @@ def build_caches(spec, w, R: int, dev):
             kscales.append(1.0)
             continue
         ks = I.per_tensor_scale_from_absmax(vals) if spec.kv_format == I.KV_FP8_PER_TENSOR else 1.0
-        cache = torch.empty((S, D), dtype=torch.uint8, device=dev)
+        width = I.kv_row_bytes(spec) if spec.kv_format == I.KV_FP8_DS_MLA else D
+        cache = torch.empty((S, width), dtype=torch.uint8, device=dev)
         gs = None
         if spec.kv_format == I.KV_FP8_GROUP128:
             gs = torch.empty((S, (D + 127) // 128), dtype=torch.float32, device=dev)
         smla.cache_write(vals[:, :512], vals[:, 512:] if spec.d_rope else None, slots, cache, spec.kv_format, ks, gs)
         torch.cuda.synchronize()
-        caches.append(cache.view(spec.num_blocks, I.BLOCK_SIZE, D))
+        caches.append(cache.view(spec.num_blocks, I.BLOCK_SIZE, width))
         gscales.append(gs)
         kscales.append(ks)
         del vals
@@ -329,7 +338,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config, "num_tokens": T, "heads": H,
                    "topk": K, "entry": f"smla_{entry}_fwd", "splits": splits, "cache_copies_rotated": R,
-                   "kv_storage": ["bf16", "e4m3 per-tensor scale", "e4m3 per-row x 128-group scales"][spec.kv_format],
+                   "kv_storage": KV_STORAGE[spec.kv_format],
                    "index_conversion": "separate kernel" if args.separate_convert else "in the attention kernel",
                    "timing": "HIP graph of R steps replayed; cold L2/MALL by cache rotation"},
         "tflops": round(tflops, 2),

@@ -65,7 +65,15 @@ typedef enum {
   SMLA_KV_FP8_E4M3_PER_TENSOR = 1,
   /* row = D OCP E4M3FN bytes; value = e4m3(byte) * group_scales[slot][c/128]
    * with group_scales a separate fp32 [num_slots][ceil(D/128)] array */
-  SMLA_KV_FP8_E4M3_GROUP128 = 2
+  SMLA_KV_FP8_E4M3_GROUP128 = 2,
+  /* Packed 656-byte row (the FP8 cache of the FlashMLA sparse backend, whose
+   * docs give 656 bytes per token but no layout; this layout is the split of
+   * that size by the group-scale rule above): bytes 0..511 the E4M3FN codes
+   * of the 512 latent channels, 512..527 four little-endian fp32 scales
+   * (latent channel c is e4m3(byte c) * scale[c / 128]), 528..655 the 64
+   * rope channels as plain bf16. Requires d_rope = 64 and group_scales =
+   * NULL; kv_row_stride_bytes >= 656 (a multiple of 16, e.g. 656). */
+  SMLA_KV_FP8_DS_MLA = 3
 } smla_kv_format;
 
 /* Arguments of the attention entry points. */
@@ -236,7 +244,11 @@ int smla_prefill_fwd(const smla_attn_args* args, void* stream);
  *   SMLA_KV_FP8_E4M3_PER_TENSOR  byte = e4m3_rne(fl32(x / k_scale)), saturated at 448;
  *   SMLA_KV_FP8_E4M3_GROUP128    per row and 128-channel group g:
  *                                scale = fl32(absmax / 448) (1 if the group is all zero),
- *                                written to group_scales[slot][g]; byte as above.
+ *                                written to group_scales[slot][g]; byte as above;
+ *   SMLA_KV_FP8_DS_MLA           (d_rope = 64) the 512 latent channels as in the group
+ *                                format with the 4 scales written into the row at bytes
+ *                                512..527, the rope channels copied as bf16 to 528..655;
+ *                                group_scales is not used.
  * Duplicate slots in one call are not allowed (which row lands is unspecified).
  *   kv_c [T][512] bf16 (row stride kv_c_stride), k_pe [T][d_rope] bf16 or NULL.
  */

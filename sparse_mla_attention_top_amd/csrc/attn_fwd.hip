@@ -106,19 +106,24 @@ constexpr int kRopeBytes = kTileRows * 64 * 2;         // bf16 rope part of a ti
 //            rows in block 4u + w (1 KB, lane l = 8 (row & 7) + chunk);
 //   rope   : (D = 576) bytes 512 .. 575 of the 8 rows, 512 B per wave
 //            (lane l < 32 = 4 (row & 7) + chunk);
-//   scales : (group format) the G = ceil(D/128) fp32 group scales of the 8
-//            rows, 8G dwords per wave (lane l < 8G = G (row & 7) + group).
+//   scales : (group formats) the G fp32 group scales of the 8 rows, 8G
+//            dwords per wave (lane l < 8G = G (row & 7) + group).
+// Packed rows (FMT 3: 512 E4M3 codes, 4 fp32 scales, 64 bf16 rope channels in
+// 656 bytes) stage only the codes and the scales; their bf16 rope part is
+// copied straight into a rope buffer (3 buffers, as for a bf16 cache).
 template <int D, int FMT>
 struct Shape {
   static constexpr bool F8 = FMT != 0;
   static constexpr bool ROPE = D > kDLatent;
-  static constexpr bool GROUP = FMT == 2;
+  static constexpr bool PACKED = FMT == 3;
+  static constexpr bool GROUP = FMT == 2 || FMT == 3;
+  static constexpr bool ROPE8 = ROPE && !PACKED;       // rope part staged as E4M3 bytes
   static constexpr int QKS = D / 32;                   // k-steps of the QK contraction
   static constexpr int NLAT = F8 ? 3 : 4;
-  static constexpr int NROPE = ROPE ? (F8 ? 2 : 3) : 0;
-  static constexpr int G = (D + 127) / 128;
+  static constexpr int NROPE = ROPE ? (ROPE8 ? 2 : 3) : 0;
+  static constexpr int G = PACKED ? 4 : (D + 127) / 128;   // scale groups (packed: the latent's)
   static constexpr int ST_ROPE = 16 * 1024;
-  static constexpr int ST_SC = ST_ROPE + (ROPE ? 4 * 512 : 0);
+  static constexpr int ST_SC = ST_ROPE + (ROPE8 ? 4 * 512 : 0);
   static constexpr int ST_BYTES = ST_SC + (GROUP ? 4 * 256 : 0);
   static constexpr int NSTAGE = F8 ? 2 : 0;
   static constexpr int NRSC = GROUP ? 3 : 0;           // row-scale sets (tiles i-1, i, i+1)
@@ -132,10 +137,16 @@ struct Shape {
   static constexpr int NDMA_S = F8 ? 4 - SEG_O : 0;
   static_assert(D == kDLatent || D == kDLatent + 64, "rope part must be 64 channels");
   static_assert(8 * G <= 64, "scales of 8 rows fit one instruction");
+  static_assert(!PACKED || ROPE, "packed rows carry the rope part");
 };
 
+// Byte offsets inside a packed row.
+constexpr int kPackedScalesAt = 512;
+constexpr int kPackedRopeAt = 528;
+
 // FMT: 0 = bf16 cache, 1 = E4M3 with one per-tensor scale, 2 = E4M3 with
-// per-row x 128-channel-group scales.
+// per-row x 128-channel-group scales in a separate array, 3 = packed rows
+// (E4M3 latent with its 4 group scales and the bf16 rope part in the row).
 template <int D, int FMT>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 smla_attn_kernel(KParams p) {
@@ -304,11 +315,17 @@ smla_attn_kernel(KParams p) {
     if constexpr (!F8) {
       s.lat = p.kv + ((uint64_t)(uint32_t)max(sidx[base + (l >> 3)], 0) * kv_stride + dcol);
     } else {
-      s.lat = p.kv + ((uint64_t)(uint32_t)max(sidx[base + (l >> 3)], 0) * kv_stride + 16 * (l & 7));
-      if constexpr (S::ROPE)
+      const uint8_t* row = p.kv + (uint64_t)(uint32_t)max(sidx[base + (l >> 3)], 0) * kv_stride;
+      s.lat = row + 16 * (l & 7);
+      if constexpr (S::ROPE8)
         s.rope = p.kv + ((uint64_t)(uint32_t)max(sidx[base + ((l >> 2) & 7)], 0) * kv_stride + kDLatent + 16 * (l & 3));
-      if constexpr (S::GROUP)
+      if constexpr (S::PACKED) {
+        // bf16 rope chunk of the same row, at its swizzled place in the rope buffer
+        s.rope = row + kPackedRopeAt + dcol;
+        s.sc = (const float*)(p.kv + (uint64_t)(uint32_t)max(sidx[base + srow], 0) * kv_stride + kPackedScalesAt) + sgrp;
+      } else if constexpr (S::GROUP) {
         s.sc = p.group_scales + ((uint64_t)(uint32_t)max(sidx[base + srow], 0) * S::G + sgrp);
+      }
     }
     return s;
   };
@@ -332,9 +349,11 @@ smla_attn_kernel(KParams p) {
     } else {
       static_for<S::SEG_O>([&](auto u_c) { issue_seg(s, i, u_c); });
       const uint32_t sb = stage_addr + (i % (S::NSTAGE ? S::NSTAGE : 1)) * S::ST_BYTES;
-      if constexpr (S::ROPE) {
+      if constexpr (S::ROPE8) {
         if (l < 32) dma_16b<0>(s.rope, __builtin_amdgcn_readfirstlane(sb + S::ST_ROPE + wu * 512));
       }
+      if constexpr (S::PACKED)
+        dma_16b<0>(s.rope, __builtin_amdgcn_readfirstlane(rope_addr + (i % (NROPE ? NROPE : 1)) * kRopeBytes + wu * 1024));
       if constexpr (S::GROUP) {
         if (l < 8 * S::G) dma_4b(s.sc, __builtin_amdgcn_readfirstlane(sb + S::ST_SC + wu * 256));
       }
@@ -383,7 +402,7 @@ smla_attn_kernel(KParams p) {
           constexpr int u = decltype(u_c)::value;
           sc[u] = *(const __attribute__((address_space(3))) float*)(st + S::ST_SC + wr * 256 + 4 * ((l >> 3) * S::G + u));
         });
-      if constexpr (S::ROPE) {
+      if constexpr (S::ROPE8) {
         rraw = *(const __attribute__((address_space(3))) u32x4*)(st + S::ST_ROPE + wr * 512 + 16 * min(l, 31));
         if constexpr (S::GROUP)
           rsc = *(const __attribute__((address_space(3))) float*)(st + S::ST_SC + wr * 256 + 4 * ((r2 - 8 * wr) * S::G + 4));
@@ -396,7 +415,7 @@ smla_attn_kernel(KParams p) {
           *(__attribute__((address_space(3))) float*)(rsc_buf(i) + 4 * (u * kTileRows + r)) = sc[u];
         });
       }
-      if constexpr (S::ROPE) {
+      if constexpr (S::ROPE8) {
         if (l < 32) {
           if constexpr (S::GROUP) *(__attribute__((address_space(3))) float*)(rsc_buf(i) + 4 * (4 * kTileRows + r2)) = rsc;
           u32x4 lo, hi;
@@ -552,7 +571,10 @@ smla_attn_kernel(KParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       });
-      if constexpr (S::GROUP) {
+      if constexpr (S::PACKED) {                        // the rope group is bf16: unscaled
+        s0 = t0 + (s0 + s2);
+        s1 = t1 + (s1 + s3);
+      } else if constexpr (S::GROUP) {
         constexpr int gl = (QKS - 1) / 4;               // last group
         const f32x4 lsc = *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * gl);
         s0 = t0 + lsc * (s0 + s2);
@@ -1006,6 +1028,10 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
     case 0: e = rope ? launch_kernel<576, 0>(kp, grid, stream, e0, e1) : launch_kernel<512, 0>(kp, grid, stream, e0, e1); break;
     case 1: e = rope ? launch_kernel<576, 1>(kp, grid, stream, e0, e1) : launch_kernel<512, 1>(kp, grid, stream, e0, e1); break;
     case 2: e = rope ? launch_kernel<576, 2>(kp, grid, stream, e0, e1) : launch_kernel<512, 2>(kp, grid, stream, e0, e1); break;
+    case 3:
+      if (!rope) return hipErrorInvalidValue;
+      e = launch_kernel<576, 3>(kp, grid, stream, e0, e1);
+      break;
     default: return hipErrorInvalidValue;
   }
   if (e != hipSuccess || splits == 1) return e;

@@ -6,7 +6,8 @@
 // per-row count of valid entries.
 // Cache write: the same branch's do_kv_cache_update (concat_and_cache_mla),
 // with the FP8 E4M3 per-tensor and per-token x 128-channel-group formats of
-// flashinfer_mla_sparse_sm90.py.
+// flashinfer_mla_sparse_sm90.py, and the 656-byte packed FP8 rows of the
+// FlashMLA sparse backend (layout: the reading of its size given with FMT 3).
 #include "smla_device.h"
 #include "smla_internal.h"
 
@@ -176,6 +177,8 @@ __device__ __forceinline__ uint32_t e4m3_encode(float y) {
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
 
 // One wave per token. Lane c8 handles channels [8*c8, 8*c8 + 8).
+// FMT 3 (packed rows): the latent's codes at bytes 0..511, its 4 group scales
+// at 512..527, the rope channels copied as bf16 to 528..655.
 template <int FMT>
 __global__ void __launch_bounds__(256)
 cache_write_kernel(const uint16_t* __restrict__ kv_c, int64_t kv_c_stride,
@@ -201,24 +204,26 @@ cache_write_kernel(const uint16_t* __restrict__ kv_c, int64_t kv_c_stride,
                                     : k_pe + (int64_t)t * k_pe_stride + (c8 - 64) * 8;
       for (int i = 0; i < 4; i++) w[i] = (uint32_t)src[2 * i] | ((uint32_t)src[2 * i + 1] << 16);
     }
-    if (FMT == 0) {
+    if (FMT == 0 || (FMT == 3 && pass == 1)) {
       if (active) {
         u32x4 v = {w[0], w[1], w[2], w[3]};
-        *(u32x4*)(cache + slot * row_stride + c8 * 16) = v;
+        const int at = FMT == 3 ? 528 + (c8 - 64) * 16 : c8 * 16;
+        *(u32x4*)(cache + slot * row_stride + at) = v;
       }
       continue;
     }
     float x[8];
     for (int i = 0; i < 8; i++) x[i] = bf16_bits_to_f32((w[i / 2] >> (16 * (i % 2))) & 0xffffu);
     float sc = k_scale;
-    if (FMT == 2) {
+    if (FMT == 2 || FMT == 3) {
       // group of 128 channels = 16 consecutive chunks = 16 consecutive lanes
       float m = 0.0f;
       for (int i = 0; i < 8; i++) m = fmaxf(m, fabsf(x[i]));
       for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
       sc = (m == 0.0f) ? 1.0f : m / 448.0f;
       int g = c8 / 16;
-      if (active && (c8 % 16) == 0 && g < G) group_scales[slot * G + g] = sc;
+      if (FMT == 2 && active && (c8 % 16) == 0 && g < G) group_scales[slot * G + g] = sc;
+      if (FMT == 3 && active && (c8 % 16) == 0) *(float*)(cache + slot * row_stride + 512 + 4 * g) = sc;
     }
     if (active) {
       uint32_t b[8];
@@ -264,11 +269,18 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream) {
                                                       a.slot_mapping, a.num_tokens, a.d_rope, a.k_scale,
                                                       a.cache, a.num_slots, a.row_stride, a.group_scales);
       break;
-    default:
+    case 2:
       cache_write_kernel<2><<<grid, 256, 0, stream>>>(a.kv_c, a.kv_c_stride, a.k_pe, a.k_pe_stride,
                                                       a.slot_mapping, a.num_tokens, a.d_rope, a.k_scale,
                                                       a.cache, a.num_slots, a.row_stride, a.group_scales);
       break;
+    case 3:
+      cache_write_kernel<3><<<grid, 256, 0, stream>>>(a.kv_c, a.kv_c_stride, a.k_pe, a.k_pe_stride,
+                                                      a.slot_mapping, a.num_tokens, a.d_rope, a.k_scale,
+                                                      a.cache, a.num_slots, a.row_stride, a.group_scales);
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -44,8 +44,11 @@ int check_attn(const smla_attn_args* a, bool decode) {
     return fail(SMLA_ERR_UNSUPPORTED, "d_rope=%d (only 0 or 64)", a->d_rope);
   if (a->topk < 1 || a->topk > smla::kMaxTopk)
     return fail(SMLA_ERR_UNSUPPORTED, "topk=%d outside 1..%d", a->topk, smla::kMaxTopk);
-  if (a->kv_format < SMLA_KV_BF16 || a->kv_format > SMLA_KV_FP8_E4M3_GROUP128)
+  if (a->kv_format < SMLA_KV_BF16 || a->kv_format > SMLA_KV_FP8_DS_MLA)
     return fail(SMLA_ERR_INVALID_ARG, "unknown kv_format %d", a->kv_format);
+  if (a->kv_format == SMLA_KV_FP8_DS_MLA && a->d_rope != 64)
+    return fail(SMLA_ERR_UNSUPPORTED, "the packed FP8 format holds 512 latent + 64 rope channels (d_rope=%d)",
+                a->d_rope);
   if (!std::isfinite(a->softmax_scale)) return fail(SMLA_ERR_INVALID_ARG, "softmax_scale not finite");
   if (a->num_tokens == 0) return SMLA_OK;
   if (!a->q_nope || !a->kv_cache || !a->indices || !a->out)
@@ -54,7 +57,7 @@ int check_attn(const smla_attn_args* a, bool decode) {
   if (a->num_slots < 1 || a->num_slots > INT32_MAX)
     return fail(SMLA_ERR_INVALID_ARG, "num_slots=%lld outside 1..2^31-1", (long long)a->num_slots);
   const int D = 512 + a->d_rope;
-  const int64_t row_bytes = a->kv_format == SMLA_KV_BF16 ? 2 * D : D;
+  const int64_t row_bytes = a->kv_format == SMLA_KV_BF16 ? 2 * D : a->kv_format == SMLA_KV_FP8_DS_MLA ? 656 : D;
   if (a->kv_row_stride_bytes < row_bytes || a->kv_row_stride_bytes % 16 != 0)
     return fail(SMLA_ERR_INVALID_ARG, "kv_row_stride_bytes=%lld must be >= %lld and a multiple of 16",
                 (long long)a->kv_row_stride_bytes, (long long)row_bytes);
@@ -86,6 +89,8 @@ int check_attn(const smla_attn_args* a, bool decode) {
     return fail(SMLA_ERR_INVALID_ARG, "k_scale must be finite and > 0");
   if (a->kv_format == SMLA_KV_FP8_E4M3_GROUP128 && ((uintptr_t)a->group_scales & 3))
     return fail(SMLA_ERR_INVALID_ARG, "group_scales must be 4-byte aligned");
+  if (a->kv_format == SMLA_KV_FP8_DS_MLA && a->group_scales)
+    return fail(SMLA_ERR_INVALID_ARG, "group_scales must be NULL for the packed FP8 format (its scales are in the row)");
   if (decode && a->num_splits < 0) return fail(SMLA_ERR_INVALID_ARG, "num_splits < 0");
   return SMLA_OK;
 }
@@ -267,15 +272,17 @@ int smla_cache_write(const void* kv_c, int64_t kv_c_stride, const void* k_pe, in
                      float* group_scales, void* stream) {
   if (num_tokens < 0) return fail(SMLA_ERR_INVALID_ARG, "num_tokens < 0");
   if (d_rope != 0 && d_rope != 64) return fail(SMLA_ERR_UNSUPPORTED, "d_rope=%d (only 0 or 64)", d_rope);
-  if (kv_format < SMLA_KV_BF16 || kv_format > SMLA_KV_FP8_E4M3_GROUP128)
+  if (kv_format < SMLA_KV_BF16 || kv_format > SMLA_KV_FP8_DS_MLA)
     return fail(SMLA_ERR_INVALID_ARG, "unknown kv_format %d", kv_format);
+  if (kv_format == SMLA_KV_FP8_DS_MLA && d_rope != 64)
+    return fail(SMLA_ERR_UNSUPPORTED, "the packed FP8 format holds 512 latent + 64 rope channels (d_rope=%d)", d_rope);
   if (num_tokens == 0) return ok();
   if (!kv_c || !slot_mapping || !kv_cache) return fail(SMLA_ERR_INVALID_ARG, "NULL pointer argument");
   if (d_rope && !k_pe) return fail(SMLA_ERR_INVALID_ARG, "k_pe is NULL with d_rope=64");
   if (kv_c_stride < 512 || (d_rope && k_pe_stride < d_rope))
     return fail(SMLA_ERR_INVALID_ARG, "source row strides too small");
   const int D = 512 + d_rope;
-  const int64_t row_bytes = kv_format == SMLA_KV_BF16 ? 2 * D : D;
+  const int64_t row_bytes = kv_format == SMLA_KV_BF16 ? 2 * D : kv_format == SMLA_KV_FP8_DS_MLA ? 656 : D;
   if (kv_row_stride_bytes < row_bytes || kv_row_stride_bytes % 16 != 0 || !aligned16(kv_cache))
     return fail(SMLA_ERR_INVALID_ARG, "cache row stride must be >= %lld and a multiple of 16, base 16-byte aligned",
                 (long long)row_bytes);

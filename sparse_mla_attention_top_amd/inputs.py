@@ -38,6 +38,7 @@ D_LATENT = 512
 KV_BF16 = 0
 KV_FP8_PER_TENSOR = 1
 KV_FP8_GROUP128 = 2
+KV_FP8_DS_MLA = 3          # packed 656-byte rows
 
 
 @dataclasses.dataclass(frozen=True)
@@ -99,6 +100,10 @@ SPECS = {
                                  2048, 192 ** -0.5, "min_pos", identity_blocks=True),
     "longctx_fp8": WorkloadSpec("longctx_fp8", 505, 64, 4, 65532, 65536, 128, 64,
                                 KV_FP8_GROUP128, 2048, 192 ** -0.5, "min_pos"),
+    # the long-context decode shape on the packed 656-byte FP8 rows of the
+    # FlashMLA sparse backend (heads padded to 64 / 128 there; here h = 128)
+    "longctx_ds_mla": WorkloadSpec("longctx_ds_mla", 606, 64, 4, 65532, 65536, 128, 64,
+                                   KV_FP8_DS_MLA, 2048, 192 ** -0.5, "min_pos"),
 }
 
 
@@ -204,6 +209,8 @@ def kv_row_bytes(spec: WorkloadSpec) -> int:
         return 2 * spec.d
     if spec.kv_format == KV_FP8_PER_TENSOR:
         return spec.d
+    if spec.kv_format == KV_FP8_DS_MLA:
+        return 656
     return spec.d + 4 * math.ceil(spec.d / 128)
 
 

@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libsmla.so")
 KV_BF16 = 0
 KV_FP8_PER_TENSOR = 1
 KV_FP8_GROUP128 = 2
+KV_FP8_DS_MLA = 3          # packed 656-byte rows: 512 E4M3 codes | 4 fp32 scales | 64 bf16 rope
+DS_MLA_ROW_BYTES = 656
 
 SMLA_OK = 0
 
@@ -253,6 +255,9 @@ def _check_kv(kv_cache: torch.Tensor, kv_format: int, width: int, S: int,
         G = (width + 127) // 128
         _need(group_scales is not None and group_scales.dtype == torch.float32 and group_scales.is_contiguous()
               and group_scales.numel() >= S * G, f"group_scales must be contiguous fp32 [num_slots, {G}]")
+    if kv_format == KV_FP8_DS_MLA:
+        _need(width >= DS_MLA_ROW_BYTES and group_scales is None,
+              "a packed FP8 cache is uint8 [..., >= 656] with its scales in the row (no group_scales)")
 
 
 def _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk_length, k_scale,

@@ -106,3 +106,19 @@ def test_dcp_filter_and_merge_reject_bad_arguments():
     assert lib.smla_merge_partials(None, 0, 0, 512, None, 0, 1, 2, 1, 1, None, 512, 512, None, 1, None) == -1
     # zero tokens is a no-op
     assert lib.smla_merge_partials(None, 0, 0, 512, None, 0, 1, 2, 0, 1, None, 512, 512, None, 1, None) == 0
+
+
+def test_packed_fp8_format_rejects_bad_arguments():
+    lib = smla.load()
+    base = dict(q_nope=16, q_rope=16, kv_cache=16, indices=16, out=16, num_slots=10, indices_stride=64,
+                out_stride_head=512, kv_format=3)
+    a = _args(kv_row_stride_bytes=656, d_rope=0, **{k: v for k, v in base.items() if k != "q_rope"})
+    assert lib.smla_prefill_fwd(ctypes.byref(a), None) == -2          # needs the rope part
+    a = _args(kv_row_stride_bytes=640, **base)
+    assert lib.smla_prefill_fwd(ctypes.byref(a), None) == -1          # row shorter than 656 bytes
+    assert b"656" in lib.smla_last_error()
+    a = _args(kv_row_stride_bytes=656, group_scales=16, **base)
+    assert lib.smla_prefill_fwd(ctypes.byref(a), None) == -1          # scales live in the row
+    assert b"group_scales" in lib.smla_last_error()
+    assert lib.smla_cache_write(16, 512, 16, 64, 16, 2, 64, 3, 1.0, 16, 4, 576, None, None) == -1  # stride < 656
+    assert lib.smla_cache_write(16, 512, None, 0, 16, 2, 0, 3, 1.0, 16, 4, 656, None, None) == -2  # no rope
