@@ -95,7 +95,7 @@ def hip_elapsed_ms(a, b) -> float:
     return ms.value
 
 
-def cpu_baseline(w, gidx_np, valid_np, min_seconds: float, k_scale: float):
+def cpu_baseline(w, gidx_np, valid_np, min_seconds: float, k_scale: float, softcap: float = 0.0, sinks=None):
     """The fp64 oracle on the host over a sample of the workload's tokens. FP8
     workloads: the rows the sample reads are quantised by the oracle's own
     quantiser (untimed set-up, as the cache write is untimed on the GPU)."""
@@ -129,7 +129,7 @@ def cpu_baseline(w, gidx_np, valid_np, min_seconds: float, k_scale: float):
     t0 = time.perf_counter()
     while True:
         O.attention(qf, cache, spec.kv_format, remap, spec.softmax_scale, topk_length=valid_np, tokens=tokens,
-                    k_scale=k_scale, group_scales=scales)
+                    k_scale=k_scale, group_scales=scales, softcap=softcap, sinks=sinks)
         n_tok += len(tokens)
         reps += 1
         if time.perf_counter() - t0 >= min_seconds:
@@ -191,6 +191,8 @@ def main() -> int:
     ap.add_argument("--dcp-interleave", type=int, default=64, help="positions per run of the context-parallel placement")
     ap.add_argument("--dcp-keep-positions", action="store_true",
                     help="shard filter without compaction (the -1 entries stay where they are)")
+    ap.add_argument("--softcap", type=float, default=0.0, help="logit softcap c (c tanh(z / c)); 0 = off")
+    ap.add_argument("--sinks", action="store_true", help="one sink logit per head (drawn N(0,1), seeded)")
     ap.add_argument("--separate-convert", action="store_true",
                     help="run smla_convert_indices as its own kernel in the step instead of in the attention kernel")
     args = ap.parse_args()
@@ -225,6 +227,10 @@ def main() -> int:
     ws_bytes = smla.decode_workspace_size(T, H, K, args.splits) if entry == "decode" else 0
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     splits = smla.decode_num_splits(T, H, K, args.splits) if entry == "decode" else 1
+    sinks = None
+    if args.sinks:
+        sinks = torch.randn(H, generator=torch.Generator().manual_seed(spec.seed + 7)).to(dev)
+    opts = dict(softcap=args.softcap, sinks=sinks)
 
     # the global indices and valid counts, for the byte / FLOP counts and the
     # CPU baseline (the step below converts again, inside the attention kernel)
@@ -241,10 +247,10 @@ def main() -> int:
         if entry == "decode":
             smla.decode_fwd(qn, qr, caches[c], idx, spec.softmax_scale, kv_format=spec.kv_format,
                             k_scale=kscales[c], group_scales=gscales[c], out=out, lse=lse, workspace=ws,
-                            num_splits=args.splits, **conv)
+                            num_splits=args.splits, **conv, **opts)
         else:
             smla.prefill_fwd(qn, qr, caches[c], idx, spec.softmax_scale, kv_format=spec.kv_format,
-                             k_scale=kscales[c], group_scales=gscales[c], out=out, lse=lse, **conv)
+                             k_scale=kscales[c], group_scales=gscales[c], out=out, lse=lse, **conv, **opts)
 
     # eager warmup and the eager reference of step 0
     for k in range(args.warmup):
@@ -321,7 +327,8 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, gidx_np, vcnt_np, args.cpu_seconds, kscales[0])
+        cpu = cpu_baseline(w, gidx_np, vcnt_np, args.cpu_seconds, kscales[0], args.softcap,
+                           None if sinks is None else sinks.cpu().numpy().astype("float64"))
 
     line = {
         "metric": "sparse-MLA query tokens/s and TFLOP/s (h=128, top-k=2048) + % of roofline",
@@ -340,6 +347,7 @@ def main() -> int:
                    "topk": K, "entry": f"smla_{entry}_fwd", "splits": splits, "cache_copies_rotated": R,
                    "kv_storage": KV_STORAGE[spec.kv_format],
                    "index_conversion": "separate kernel" if args.separate_convert else "in the attention kernel",
+                   "softcap": args.softcap, "sinks": bool(args.sinks),
                    "timing": "HIP graph of R steps replayed; cold L2/MALL by cache rotation"},
         "tflops": round(tflops, 2),
         "pct_of_path_roofline": round(100 * roofline_time / (dt / steps), 2),

@@ -135,6 +135,20 @@ typedef struct {
   int32_t num_reqs, max_blocks;
   int64_t bt_row_stride;
   int32_t block_size, block_stride_rows;
+
+  /* Optional softmax options of the FA3 API (flash_attn_with_kvcache
+   * arguments softcap and sinks; the pages give the names, not the
+   * formulas, and these are the plain readings):
+   *   softcap > 0: every scaled logit z = softmax_scale * q.k becomes
+   *     softcap * tanh(z / softcap) before the softmax; 0 = off.
+   *   sinks: fp32 [num_heads] (4-byte aligned) or NULL. sinks[i] is one more
+   *     logit of head i (natural-log units, not capped) whose value row is
+   *     zero: out = sum_j e^z_j v_j / (sum_j e^z_j + e^sinks[i]) and LSE is
+   *     the log of that denominator; a row with no valid entry gives
+   *     (0, sinks[i]). A sink enters a result once: with context-parallel
+   *     ranks merged by smla_merge_partials, give it to one rank only. */
+  float softcap;
+  const float* sinks;
 } smla_attn_args;
 
 /*

@@ -55,6 +55,12 @@ struct KParams {
   int32_t num_tokens, num_heads;
   float scale_log2;   // softmax scale * log2(e)
   float out_mult;
+  // logit softcap c (softcap_on): base-2 logits t = s * scale_log2 become
+  // c1 tanh(t / c1), c1 = c log2(e), as c1 - 2 c1 / (1 + 2^(2t / c));
+  // cap_a = 2 scale_log2 / c (applied to s), cap_t = 2 / c (applied to t)
+  int32_t softcap_on;
+  float cap_a, cap_t, cap_c1;
+  const float* sinks;  // [H] extra logits with zero value rows (direct output only), or nullptr
   int32_t splits, longest_first;
   int32_t head_blocks;  // 1 (<= 64 heads) or 2
   int32_t xcd_group;    // 1: all workgroups of token t run on XCD t % 8
@@ -117,7 +123,7 @@ struct Shape {
   static constexpr bool ROPE = D > kDLatent;
   static constexpr bool PACKED = FMT == 3;
   static constexpr bool GROUP = FMT == 2 || FMT == 3;
-  static constexpr bool ROPE8 = ROPE && !PACKED;       // rope part staged as E4M3 bytes
+  static constexpr bool ROPE8 = F8 && ROPE && !PACKED; // rope part staged as E4M3 bytes
   static constexpr int QKS = D / 32;                   // k-steps of the QK contraction
   static constexpr int NLAT = F8 ? 3 : 4;
   static constexpr int NROPE = ROPE ? (ROPE8 ? 2 : 3) : 0;
@@ -608,6 +614,13 @@ smla_attn_kernel(KParams p) {
     float m_ref[2] = {-INFINITY, -INFINITY};
     float l_lane[2] = {0.0f, 0.0f};
     bool have_ref = false;                                 // workgroup-uniform
+    // capped value of a base-2 logit (the cap is increasing, so the capped
+    // maximum is the cap of the maximum)
+    auto cap2 = [&](float t) -> float {
+      if (!p.softcap_on || t == -INFINITY) return t;
+      const float e = fast_exp2(t * p.cap_t);
+      return fmaf(-2.0f * p.cap_c1, __builtin_amdgcn_rcpf(1.0f + e), p.cap_c1);
+    };
 
     // Scores in base-2 units, masked rows at -inf (for the maxima).
     auto scaled = [&](const f32x4& r0, const f32x4& r1, uint32_t vmask, float (&tv)[2][4], float (&mx)[2]) {
@@ -626,9 +639,11 @@ smla_attn_kernel(KParams p) {
     // per-head maximum (into mx_all). Barriers: one per tile, plus the
     // reference exchange in tile 0 of a full pass. A full pass ends by
     // flagging a rerun if a row sum left the range the reference guarantees
-    // (some p = 2^(t - m) above 2^64, or not finite).
+    // (some p = 2^(t - m) above 2^64, or not finite), or if tile 0 held no
+    // valid entry (no reference) while a later tile did.
     auto s_pass = [&](const bool full, float (&mx_all)[2], const bool issued) {
       l_lane[0] = l_lane[1] = 0.0f;
+      bool seen = false;                                   // a valid entry in some tile (uniform)
       if constexpr (F8) {                                  // this wave's share of tile 0
         if (!issued) {
           if (ntiles > 0) issue_tile_s(0);
@@ -649,6 +664,7 @@ smla_attn_kernel(KParams p) {
         float mx[2] = {-INFINITY, -INFINITY};
         if (have) {
           vmask = (uint32_t)__ballot((l < 32) ? (sidx[i * kTileRows + l] >= 0) : 0);
+          seen = seen || vmask != 0;
           scores(i, r0, r1);
           if (!full || i == 0) scaled(r0, r1, vmask, tv, mx);
         }
@@ -668,8 +684,8 @@ smla_attn_kernel(KParams p) {
         if (i == 0) {                                      // the reference: tile 0's maximum
           wg_max(mx);                                      // (its barrier always runs: the O-waves match it)
           if (!have_ref) {                                 // a rerun keeps the exact maximum
-            m_ref[0] = mx[0];
-            m_ref[1] = mx[1];
+            m_ref[0] = cap2(mx[0]);
+            m_ref[1] = cap2(mx[1]);
             have_ref = true;
           }
         }
@@ -681,8 +697,17 @@ smla_attn_kernel(KParams p) {
             const float nm = (m_ref[nbq] == -INFINITY) ? 0.0f : -m_ref[nbq];
             const f32x4& rs = nbq ? r1 : r0;
             float pr[4];
+            if (p.softcap_on) {
+              const float base = p.cap_c1 + nm, k2 = -2.0f * p.cap_c1;
 #pragma unroll
-            for (int r = 0; r < 4; r++) pr[r] = fast_exp2(fmaf(rs[r], p.scale_log2, nm));
+              for (int r = 0; r < 4; r++) {
+                const float e = fast_exp2(rs[r] * p.cap_a);
+                pr[r] = fast_exp2(fmaf(k2, __builtin_amdgcn_rcpf(1.0f + e), base));
+              }
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; r++) pr[r] = fast_exp2(fmaf(rs[r], p.scale_log2, nm));
+            }
             if (!all_valid) {
 #pragma unroll
               for (int r = 0; r < 4; r++)
@@ -695,7 +720,7 @@ smla_attn_kernel(KParams p) {
           }
         } else {
           // end of the pass: 2^64 bounds every p while the reference holds
-          if (!(l_lane[0] <= kRefLimit) || !(l_lane[1] <= kRefLimit)) s_flag = 1;
+          if (!(l_lane[0] <= kRefLimit) || !(l_lane[1] <= kRefLimit) || (seen && m_ref[0] == -INFINITY)) s_flag = 1;
         }
         convert_next();
         lds_barrier();
@@ -710,8 +735,8 @@ smla_attn_kernel(KParams p) {
       float mx_all[2] = {-INFINITY, -INFINITY};
       s_pass(false, mx_all, false);
       wg_max(mx_all);
-      m_ref[0] = mx_all[0];
-      m_ref[1] = mx_all[1];
+      m_ref[0] = cap2(mx_all[0]);
+      m_ref[1] = cap2(mx_all[1]);
       if (threadIdx.x == 0) s_flag = 0;
     }
 
@@ -731,11 +756,23 @@ smla_attn_kernel(KParams p) {
     if (rh == 0 && lg == 0) {
 #pragma unroll
       for (int nbq = 0; nbq < 2; nbq++) {
-        const float lt = s_l[wr * 32 + 16 * nbq + li] + s_l[(wr ^ 2) * 32 + 16 * nbq + li];
+        float lt = s_l[wr * 32 + 16 * nbq + li] + s_l[(wr ^ 2) * 32 + 16 * nbq + li];
         const int hl = 32 * hg + 16 * nbq + li;          // head within the block
-        s_inv[hl] = (lt > 0.0f) ? p.out_mult / lt : 0.0f;
-        const float lse_v = (lt > 0.0f) ? (m_ref[nbq] + log2f(lt)) * 0.69314718055994531f : -INFINITY;
         const int head = hb + hl;
+        float mr = m_ref[nbq], om = p.out_mult;
+        if (p.sinks && head < H) {
+          // the sink joins the denominator: rescale to M = max(m, sink)
+          const float sg = p.sinks[head] * 1.4426950408889634f;
+          const float M = fmaxf(mr, sg);
+          if (M != -INFINITY) {
+            const float a = exp2f(mr - M);                 // 0 for an empty row
+            lt = fmaf(lt, a, exp2f(sg - M));
+            om *= a;
+            mr = M;
+          }
+        }
+        s_inv[hl] = (lt > 0.0f) ? om / lt : 0.0f;
+        const float lse_v = (lt > 0.0f) ? (mr + log2f(lt)) * 0.69314718055994531f : -INFINITY;
         if (head < H) {
           if (p.splits == 1) {
             if (p.lse) p.lse[(int64_t)t * p.lse_st + head] = lse_v;
@@ -898,14 +935,15 @@ smla_attn_kernel(KParams p) {
 }
 
 // Merge partial results by their LSE: lse = ln sum_s exp(lse_s),
-// out = sum_s exp(lse_s - lse) * O_s; (0, -inf) is the identity. Partials are
+// out = sum_s exp(lse_s - lse) * O_s; (0, -inf) is the identity, and a sink
+// enters as one more partial (0, sink). Partials are
 // the normalised O_s in bf16 (the decode splits, or the context-parallel
 // ranks' outputs: the cross-rank merge of the FlashMLA sparse docs).
 __global__ void __launch_bounds__(256)
 smla_combine_kernel(const uint16_t* __restrict__ part_o, int64_t po_rank, int64_t po_tok, int64_t po_head,
                     const float* __restrict__ part_lse, int64_t pl_rank, int64_t pl_tok, int splits,
                     int T, int H, uint16_t* __restrict__ out, int64_t out_st, int64_t out_sh,
-                    float* __restrict__ lse, int64_t lse_st) {
+                    float* __restrict__ lse, int64_t lse_st, const float* __restrict__ sinks) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;   // one thread = 8 channels
   const int64_t total = (int64_t)T * H * (kDLatent / 8);
   if (gid >= total) return;
@@ -915,11 +953,14 @@ smla_combine_kernel(const uint16_t* __restrict__ part_o, int64_t po_rank, int64_
   const int t = (int)(th / H);
   const float* pl = part_lse + (int64_t)t * pl_tok + head;
   const uint16_t* po = part_o + (int64_t)t * po_tok + (int64_t)head * po_head + 8 * c8;
-  float m = -INFINITY;
+  // a sink is one more partial with a zero output and LSE sinks[head]
+  const float sg = sinks ? sinks[head] : -INFINITY;
+  float m = sg;
   for (int s = 0; s < splits; s++) m = fmaxf(m, pl[s * pl_rank]);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float tot = 0.0f;
   if (m != -INFINITY) {
+    if (sg != -INFINITY) tot = expf(sg - m);
     for (int s = 0; s < splits; s++) {
       const float ls = pl[s * pl_rank];
       const float wgt = (ls == -INFINITY) ? 0.0f : expf(ls - m);
@@ -1007,6 +1048,11 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
     kp.scale_log2 *= a.k_scale;
     kp.out_mult = a.k_scale;
   }
+  kp.softcap_on = a.softcap > 0.0f ? 1 : 0;
+  kp.cap_a = kp.softcap_on ? 2.0f * kp.scale_log2 / a.softcap : 0.0f;
+  kp.cap_t = kp.softcap_on ? 2.0f / a.softcap : 0.0f;
+  kp.cap_c1 = a.softcap * 1.4426950408889634f;
+  kp.sinks = splits == 1 ? a.sinks : nullptr;        // with splits the merge adds the sink
   kp.splits = splits;
   kp.longest_first = longest_first ? 1 : 0;
   kp.head_blocks = a.num_heads > 64 ? 2 : 1;
@@ -1048,6 +1094,7 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
   m.num_heads = a.num_heads;
   m.out = a.out; m.out_st = a.out_st; m.out_sh = a.out_sh;
   m.lse = a.lse; m.lse_st = a.lse_st;
+  m.sinks = a.sinks;
   return launch_merge(m, stream);
 }
 
@@ -1056,7 +1103,7 @@ hipError_t launch_merge(const MergeArgs& m, hipStream_t stream) {
   if (total == 0) return hipSuccess;
   smla_combine_kernel<<<(int)((total + 255) / 256), 256, 0, stream>>>(
       m.part_o, m.po_rank, m.po_tok, m.po_head, m.part_lse, m.pl_rank, m.pl_tok, m.parts, m.num_tokens,
-      m.num_heads, m.out, m.out_st, m.out_sh, m.lse, m.lse_st);
+      m.num_heads, m.out, m.out_st, m.out_sh, m.lse, m.lse_st, m.sinks);
   return hipGetLastError();
 }
 

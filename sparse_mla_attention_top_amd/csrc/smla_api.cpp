@@ -89,6 +89,9 @@ int check_attn(const smla_attn_args* a, bool decode) {
     return fail(SMLA_ERR_INVALID_ARG, "k_scale must be finite and > 0");
   if (a->kv_format == SMLA_KV_FP8_E4M3_GROUP128 && ((uintptr_t)a->group_scales & 3))
     return fail(SMLA_ERR_INVALID_ARG, "group_scales must be 4-byte aligned");
+  if (!(std::isfinite(a->softcap) && a->softcap >= 0.0f))
+    return fail(SMLA_ERR_INVALID_ARG, "softcap must be finite and >= 0 (0 = off)");
+  if ((uintptr_t)a->sinks & 3) return fail(SMLA_ERR_INVALID_ARG, "sinks must be 4-byte aligned");
   if (a->kv_format == SMLA_KV_FP8_DS_MLA && a->group_scales)
     return fail(SMLA_ERR_INVALID_ARG, "group_scales must be NULL for the packed FP8 format (its scales are in the row)");
   if (decode && a->num_splits < 0) return fail(SMLA_ERR_INVALID_ARG, "num_splits < 0");
@@ -129,6 +132,8 @@ smla::AttnArgs to_internal(const smla_attn_args* a) {
   r.bt_row_stride = a->bt_row_stride;
   r.block_size = a->block_size;
   r.block_stride_rows = a->block_stride_rows == 0 ? a->block_size : a->block_stride_rows;
+  r.softcap = a->softcap;
+  r.sinks = a->sinks;
   r.ev_start = g_ev_start;
   r.ev_end = g_ev_end;
   return r;
@@ -232,6 +237,7 @@ int smla_merge_partials(const void* part_out, int64_t part_out_stride_part, int6
   m.out_sh = out_stride_head;
   m.lse = lse;
   m.lse_st = lse_stride_tok;
+  m.sinks = nullptr;
   return hip_status(smla::launch_merge(m, (hipStream_t)stream), "merge_partials launch");
 }
 

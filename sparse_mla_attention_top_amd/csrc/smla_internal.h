@@ -45,6 +45,7 @@ struct MergeArgs {
   int64_t out_st, out_sh;
   float* lse;
   int64_t lse_st;
+  const float* sinks;   // [num_heads] extra logits (zero value rows), or nullptr
 };
 
 struct CacheWriteArgs {
@@ -87,6 +88,8 @@ struct AttnArgs {
   int32_t num_reqs, max_blocks;
   int64_t bt_row_stride;
   int32_t block_size, block_stride_rows;
+  float softcap;                 // > 0: logits c tanh(z / c)
+  const float* sinks;            // [num_heads] or nullptr
   hipEvent_t ev_start, ev_end;   // optional, recorded around the main kernel
 };
 

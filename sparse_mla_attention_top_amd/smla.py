@@ -81,6 +81,8 @@ class AttnArgs(ctypes.Structure):
         ("bt_row_stride", ctypes.c_int64),
         ("block_size", ctypes.c_int32),
         ("block_stride_rows", ctypes.c_int32),
+        ("softcap", ctypes.c_float),
+        ("sinks", ctypes.c_void_p),
     ]
 
 
@@ -262,7 +264,7 @@ def _check_kv(kv_cache: torch.Tensor, kv_format: int, width: int, S: int,
 
 def _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk_length, k_scale,
                group_scales, out, lse, num_splits, block_table=None, req_id=None, block_size=64,
-               block_stride_rows=0) -> Tuple[AttnArgs, torch.Tensor, Optional[torch.Tensor]]:
+               block_stride_rows=0, softcap=0.0, sinks=None) -> Tuple[AttnArgs, torch.Tensor, Optional[torch.Tensor]]:
     _need(q_nope.dtype == torch.bfloat16 and q_nope.dim() == 3 and q_nope.shape[2] == 512 and q_nope.stride(2) == 1,
           "q_nope must be bf16 [T, h, 512] with unit channel stride")
     T, H, _ = q_nope.shape
@@ -302,6 +304,11 @@ def _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk
     a.lse = _ptr(lse)
     a.lse_stride_tok = lse.stride(0) if lse is not None else 0
     a.num_splits = int(num_splits)
+    a.softcap = float(softcap)
+    if sinks is not None:
+        _need(sinks.dtype == torch.float32 and sinks.numel() == H and sinks.is_contiguous(),
+              "sinks must be contiguous fp32 [h]")
+        a.sinks = _ptr(sinks)
     if block_table is not None:
         _need(req_id is not None and req_id.dtype == torch.int32 and req_id.numel() == T and req_id.is_contiguous(),
               "req_id must be contiguous int32 [T] with a block table")
@@ -326,16 +333,19 @@ def decode_num_splits(num_tokens: int, num_heads: int, topk: int, num_splits: in
 
 def decode_fwd(q_nope, q_rope, kv_cache, indices, softmax_scale, kv_format=KV_BF16, topk_length=None,
                k_scale=1.0, group_scales=None, out=None, lse=None, return_lse=True, num_splits=0,
-               workspace=None, stream=None, block_table=None, req_id=None, block_size=64, block_stride_rows=0):
+               workspace=None, stream=None, block_table=None, req_id=None, block_size=64, block_stride_rows=0,
+               softcap=0.0, sinks=None):
     """Sparse MLA decode forward. Returns (out [T,h,512] bf16, lse [T,h] fp32 or None).
     With ``block_table`` (and ``req_id``), ``indices`` are request-local and are
-    converted inside the attention kernel."""
+    converted inside the attention kernel. ``softcap`` > 0 caps the scaled
+    logits (c tanh(z / c)); ``sinks`` (fp32 [h]) adds one logit per head with a
+    zero value row to each softmax."""
     T, H = q_nope.shape[:2]
     if lse is None and return_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=q_nope.device)
     a, out, lse = _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk_length,
                              k_scale, group_scales, out, lse, num_splits, block_table, req_id, block_size,
-                             block_stride_rows)
+                             block_stride_rows, softcap, sinks)
     need = decode_workspace_size(T, H, indices.shape[1], num_splits) if T > 0 else 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_nope.device)
@@ -347,15 +357,15 @@ def decode_fwd(q_nope, q_rope, kv_cache, indices, softmax_scale, kv_format=KV_BF
 
 def prefill_fwd(q_nope, q_rope, kv_cache, indices, softmax_scale, kv_format=KV_BF16, topk_length=None,
                 k_scale=1.0, group_scales=None, out=None, lse=None, return_lse=False, stream=None,
-                block_table=None, req_id=None, block_size=64, block_stride_rows=0):
-    """Sparse MLA prefill forward (no split). Returns (out, lse or None). ``block_table``
-    as for decode_fwd."""
+                block_table=None, req_id=None, block_size=64, block_stride_rows=0, softcap=0.0, sinks=None):
+    """Sparse MLA prefill forward (no split). Returns (out, lse or None). ``block_table``,
+    ``softcap`` and ``sinks`` as for decode_fwd."""
     T, H = q_nope.shape[:2]
     if lse is None and return_lse:
         lse = torch.empty((T, H), dtype=torch.float32, device=q_nope.device)
     a, out, lse = _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk_length,
                              k_scale, group_scales, out, lse, 0, block_table, req_id, block_size,
-                             block_stride_rows)
+                             block_stride_rows, softcap, sinks)
     rc = load().smla_prefill_fwd(ctypes.byref(a), _stream(stream))
     _check("smla_prefill_fwd", rc)
     return out, lse

@@ -64,10 +64,11 @@ def compare(out_gpu: torch.Tensor, lse_gpu: Optional[torch.Tensor], ref, what: s
 
 def oracle_for(q: torch.Tensor, cache_bits: np.ndarray, global_idx: np.ndarray, scale: float,
                lengths: Optional[np.ndarray] = None, tokens=None, kv_format: int = O.KV_BF16,
-               k_scale: float = 1.0, group_scales: Optional[np.ndarray] = None):
+               k_scale: float = 1.0, group_scales: Optional[np.ndarray] = None, softcap: float = 0.0,
+               sinks: Optional[np.ndarray] = None):
     sel = np.arange(q.shape[0]) if tokens is None else np.asarray(tokens)
     qf = q_f64(q[torch.as_tensor(sel)])
     idx = global_idx[sel]
     ln = None if lengths is None else np.asarray(lengths)[sel]
     return O.attention_with_magnitude(qf, cache_bits, kv_format, idx, scale, topk_length=ln,
-                                      k_scale=k_scale, group_scales=group_scales)
+                                      k_scale=k_scale, group_scales=group_scales, softcap=softcap, sinks=sinks)

@@ -108,6 +108,19 @@ def test_dcp_filter_and_merge_reject_bad_arguments():
     assert lib.smla_merge_partials(None, 0, 0, 512, None, 0, 1, 2, 0, 1, None, 512, 512, None, 1, None) == 0
 
 
+def test_softcap_and_sinks_reject_bad_arguments():
+    lib = smla.load()
+    base = dict(q_nope=16, q_rope=16, kv_cache=16, indices=16, out=16, num_slots=10, indices_stride=64,
+                out_stride_head=512, kv_row_stride_bytes=1152)
+    for cap in (-1.0, float("nan"), float("inf")):
+        a = _args(softcap=cap, **base)
+        assert lib.smla_prefill_fwd(ctypes.byref(a), None) == -1
+        assert b"softcap" in lib.smla_last_error()
+    a = _args(sinks=18, **base)
+    assert lib.smla_prefill_fwd(ctypes.byref(a), None) == -1
+    assert b"sinks" in lib.smla_last_error()
+
+
 def test_packed_fp8_format_rejects_bad_arguments():
     lib = smla.load()
     base = dict(q_nope=16, q_rope=16, kv_cache=16, indices=16, out=16, num_slots=10, indices_stride=64,

@@ -281,6 +281,21 @@ def test_empty_rows_give_merge_identity():
         assert (out[1:].float() == 0).all() and torch.isneginf(lse[1:]).all()
 
 
+def test_leading_invalid_tiles():
+    """Rows (and decode splits) whose first tiles hold no valid entry, with
+    valid entries after them: the softmax reference cannot come from the
+    first tile, and the LSE must still be that of the valid entries."""
+    say("edge leading invalid tiles")
+    c = I.random_case(T=4, h=64, d_rope=64, topk=256, num_slots=600, seed=13)
+    c.indices[0, :32] = -1                 # tile 0 invalid
+    c.indices[1, :100] = -1                # tiles 0-2 invalid, tile 3 partly
+    c.indices[2, :64] = -1                 # split 2 of 2 starts with two invalid tiles too
+    c.indices[2, 128:192] = -1
+    c.indices[3, 200:] = -1                # an invalid tail only
+    for entry, splits in (("prefill", 0), ("decode", 1), ("decode", 2), ("decode", 4)):
+        _run_case(c, 0.08, entry, topk_length=None, num_splits=splits)
+
+
 def test_large_logit_jump_takes_the_exact_path():
     """A slot whose score exceeds the first tile's maximum by far more than the
     reference headroom: the result must still match the oracle."""
