@@ -47,6 +47,22 @@ What is computed, with the passage each step follows:
 * ``merge_partials`` -- combine partial (out, lse) pairs computed over
   disjoint slices of a row: the identity element is (0, -inf) (FlashMLA
   sparse API docs, ``_forward_fp8_kv_mixed_batch``, the cross-rank LSE merge).
+* ``planned_valid_counts`` -- each query row's valid count from the batch
+  layout alone: a row for the j-th query token of request i sees
+  ctx = seq_len[i] - q_len[i] + j + 1 tokens, and the pooled indexer keeps
+  ctx of them when ctx <= topk, else topk + ctx % kpool (FlashInfer sparse SM90
+  backend, ``_kv_lens_host`` and ``_clamp_work_kv_end``).
+  ``indexer_selection`` simulates the selection that docstring describes (whole
+  context up to topk; else the best topk / kpool complete pools of kpool
+  consecutive positions, expanded, plus the trailing incomplete pool), to pin
+  the count.
+* ``gather_upconvert`` -- the FP8 prefill design of the FlashMLA sparse backend
+  (``forward_mqa``, the ``cp_gather_and_upconvert_fp8_kv_cache`` call): each
+  request's context rows, in position order, are gathered from the packed FP8
+  cache through the block table into a bf16 workspace at workspace_starts[r],
+  and the bf16 kernel then runs over the workspace. The pages do not print
+  the conversion; the reading is value = bf16_rne(fl32(e4m3 * scale)) per latent
+  channel and the rope channels copied.
 * ``cache_write`` -- write [kv_c(512) | k_pe(d_rope)] rows at slot_mapping,
   negative slots skipped; bf16 copy, or E4M3 with a given per-tensor scale,
   or E4M3 with per-token x 128-channel-group scales absmax/448 computed here
@@ -94,6 +110,13 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     b = np.asarray(bits).view(np.uint16).astype(np.uint32) << 16
     return b.view(np.float32)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + 0x7FFF + ((u >> 16) & 1)
+    return (u >> 16).astype(np.uint16)
 
 
 # ---------------------------------------------------------------------------
@@ -266,6 +289,58 @@ def _attention(q, cache, kv_format, indices, softmax_scale, topk_length, k_scale
     if not outs:
         return np.zeros((0, h, d_v)), np.zeros((0, h)), np.zeros((0, h, d_v))
     return np.stack(outs), np.stack(lses), (np.stack(mags) if magnitude else None)
+
+
+def planned_valid_counts(seq_lens: np.ndarray, query_start_loc: np.ndarray, req_id: np.ndarray,
+                         topk: int, kpool: int) -> np.ndarray:
+    """Valid count of every query row t (request r = req_id[t], rows of request
+    r are query_start_loc[r] .. query_start_loc[r+1]-1): with
+    ctx = seq_lens[r] - query_start_loc[r+1] + t + 1, ctx if ctx <= topk,
+    else topk + ctx % kpool. int32 [T]."""
+    seq = np.asarray(seq_lens, dtype=np.int64)
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    req = np.asarray(req_id, dtype=np.int64)
+    rows = np.arange(req.shape[0], dtype=np.int64)
+    ctx = seq[req] - qsl[req + 1] + rows + 1
+    return np.where(ctx <= topk, ctx, topk + ctx % kpool).astype(np.int32)
+
+
+def indexer_selection(ctx: int, topk: int, kpool: int, pool_scores: np.ndarray) -> np.ndarray:
+    """Positions a pooled top-k indexer keeps for a context of ctx tokens:
+    all of them when ctx <= topk; otherwise the topk // kpool complete pools
+    (kpool consecutive positions each) with the highest pool_scores, expanded
+    to their positions, plus every position of the trailing incomplete pool."""
+    if ctx <= topk:
+        return np.arange(ctx)
+    assert topk % kpool == 0
+    full = ctx // kpool
+    best = np.argsort(-np.asarray(pool_scores)[:full], kind="stable")[:topk // kpool]
+    kept = (best[:, None] * kpool + np.arange(kpool)[None, :]).ravel()
+    tail = np.arange(full * kpool, ctx)
+    return np.concatenate([kept, tail])
+
+
+def upconvert_rows(cache: np.ndarray, slots: np.ndarray) -> np.ndarray:
+    """Packed FP8 rows -> bf16 bit patterns [n, 576]: latent channel c is
+    bf16_rne(fl32(e4m3(code) * scale[c // 128])), the rope channels are copied."""
+    codes, sc, rope = unpack_ds_mla(np.asarray(cache)[np.asarray(slots, dtype=np.int64)])
+    lat = (e4m3.decode(codes).astype(np.float32) * np.repeat(sc, GROUP, axis=1)).astype(np.float32)
+    return np.concatenate([f32_to_bf16_bits(lat), rope], axis=1)
+
+
+def gather_upconvert(cache: np.ndarray, block_table: np.ndarray, seq_lens: np.ndarray,
+                     workspace_starts: np.ndarray, block_size: int, workspace: np.ndarray,
+                     block_stride_rows: Optional[int] = None) -> None:
+    """Row workspace_starts[r] + p of ``workspace`` (bf16 bits [W, 576]) gets
+    request r's context position p < seq_lens[r], read from the packed cache at
+    slot block_table[r][p // B] * stride + p % B and upconverted."""
+    stride = block_size if block_stride_rows is None else block_stride_rows
+    bt = np.asarray(block_table, dtype=np.int64)
+    for r in range(bt.shape[0]):
+        n = int(seq_lens[r])
+        p = np.arange(n)
+        slots = bt[r, p // block_size] * stride + p % block_size
+        workspace[int(workspace_starts[r]) + p] = upconvert_rows(cache, slots)
 
 
 def dcp_owner_local(pos: np.ndarray, dcp_size: int, interleave: int):

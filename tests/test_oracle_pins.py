@@ -638,3 +638,71 @@ def test_sink_is_a_merge_with_a_zero_partial():
     zero = np.zeros_like(o0)
     mo, ml = O.merge_partials(np.stack([o0, zero]), np.stack([l0, np.broadcast_to(sinks, l0.shape)]))
     assert np.abs(mo - o1).max() < 1e-12 and np.abs(ml - l1).max() < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# planned valid counts (pooled indexer) and the FP8 prefill upconvert
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("topk,kpool", [(64, 1), (64, 4), (256, 64), (2048, 64)])
+def test_planned_counts_match_a_simulated_pooled_indexer(topk, kpool):
+    """For every query row, the count of positions the simulated indexer keeps
+    (distinct, inside the row's context) equals the planned count."""
+    rng = np.random.default_rng(27 + kpool)
+    q_lens = rng.integers(1, 5, 6)
+    seq = np.array([int(rng.integers(q, q + 3 * topk)) for q in q_lens])
+    seq[0] = q_lens[0]                                   # a request that is all new tokens
+    qsl = np.concatenate([[0], np.cumsum(q_lens)])
+    req = np.repeat(np.arange(6), q_lens)
+    planned = O.planned_valid_counts(seq, qsl, req, topk, kpool)
+    for t in range(req.size):
+        r = req[t]
+        ctx = int(seq[r] - q_lens[r] + (t - qsl[r]) + 1)
+        sel = O.indexer_selection(ctx, topk, kpool, rng.standard_normal(ctx // kpool + 1))
+        assert np.unique(sel).size == sel.size and sel.min() >= 0 and sel.max() < ctx
+        assert sel.size == planned[t], (t, ctx, sel.size, planned[t])
+    if kpool == 1:
+        ctx_all = seq[req] - qsl[req + 1] + np.arange(req.size) + 1
+        assert (planned == np.minimum(ctx_all, topk)).all()
+
+
+def test_upconvert_is_the_bf16_rounding_of_the_decoded_value():
+    """Latent: torch's bf16 rounding of e4m3 * scale (exact in fp64, so the
+    fp32 product rounds the same way); power-of-two scales stay exact; the rope
+    bits are copied."""
+    rng = np.random.default_rng(28)
+    n = 40
+    codes = rng.integers(0, 256, (n, 512)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    scales = rng.uniform(1e-3, 10.0, (n, 4)).astype(np.float32)
+    scales[:5] = np.ldexp(1.0, rng.integers(-8, 8, (5, 4))).astype(np.float32)
+    rope = _rand_bf16(rng, (n, 64))
+    cache = O.pack_ds_mla(codes, scales, rope)
+    slots = rng.permutation(n)
+    got = O.upconvert_rows(cache, slots)
+    exact = O.dequantize_rows(cache, O.KV_FP8_DS_MLA, slots)
+    ref = torch.from_numpy(exact[:, :512]).float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (got[:, :512] == ref).all()
+    assert (got[:, 512:] == rope[slots]).all()
+    p2 = np.isin(slots, np.arange(5))
+    assert (O.bf16_bits_to_f64(got[p2]) == exact[p2]).all()
+
+
+def test_gather_upconvert_places_each_position():
+    """Request r's position p lands in workspace row starts[r] + p, read through
+    the block table; rows outside the requests' ranges stay untouched."""
+    rng = np.random.default_rng(29)
+    B, nblk = 4, 12
+    rows = _rand_bf16(rng, (nblk * B, 576))
+    cache = np.zeros((nblk * B, 656), np.uint8)
+    O.cache_write(rows[:, :512], rows[:, 512:], np.arange(nblk * B), O.KV_FP8_DS_MLA, cache)
+    bt = rng.permutation(nblk).reshape(3, 4).astype(np.int32)
+    seq = np.array([5, 16, 0])
+    starts = np.array([0, 8, 30])
+    ws = np.full((32, 576), 0xABCD, np.uint16)
+    O.gather_upconvert(cache, bt, seq, starts, B, ws)
+    for r in range(3):
+        for pos in range(seq[r]):
+            slot = bt[r, pos // B] * B + pos % B
+            assert (ws[starts[r] + pos] == O.upconvert_rows(cache, [slot])[0]).all()
+    assert (ws[5:8] == 0xABCD).all() and (ws[24:] == 0xABCD).all()
