@@ -37,10 +37,12 @@ WORKLOAD_TEXT = {
     "longctx_ds_mla": "sparse MLA long-context decode, packed 656-byte FP8 rows [65536,64,656] (512 E4M3 latent "
                       "codes, 4 fp32 group scales, 64 bf16 rope channels): 64 requests x 65536 context, 4 query "
                       "tokens each (256), h=128, top-k=2048 all valid, random block table, scale 192^-0.5, out + LSE",
+    "prefill_ds_mla": "sparse MLA prefill on packed 656-byte FP8 rows [64,64,656]: 1 request of 4096 new tokens, "
+                      "h=128, top-k=2048, causal indices (valid = min(2048, pos+1)), scale 192^-0.5",
     "tiny": "tiny sparse MLA: 4 tokens, h=16, top-k=64, cache 256 x 576 bf16",
 }
 ENTRY = {"decode_bf16": "decode", "prefill_bf16": "prefill", "nope_fp8": "decode", "longctx_fp8": "decode",
-         "longctx_ds_mla": "decode", "tiny": "decode"}
+         "longctx_ds_mla": "decode", "prefill_ds_mla": "prefill", "tiny": "decode"}
 KV_STORAGE = ["bf16", "e4m3 per-tensor scale", "e4m3 per-row x 128-group scales",
               "packed 656-byte rows: e4m3 latent + 4 fp32 group scales + bf16 rope"]
 
@@ -191,6 +193,9 @@ def main() -> int:
     ap.add_argument("--dcp-interleave", type=int, default=64, help="positions per run of the context-parallel placement")
     ap.add_argument("--dcp-keep-positions", action="store_true",
                     help="shard filter without compaction (the -1 entries stay where they are)")
+    ap.add_argument("--fp8-prefill", choices=["lds", "upconvert"], default="upconvert",
+                    help="prefill on packed FP8 rows: dequantize in LDS inside the attention kernel, or gather and "
+                         "upconvert each request's context to a bf16 workspace first and run the bf16 kernel on it")
     ap.add_argument("--softcap", type=float, default=0.0, help="logit softcap c (c tanh(z / c)); 0 = off")
     ap.add_argument("--sinks", action="store_true", help="one sink logit per head (drawn N(0,1), seeded)")
     ap.add_argument("--separate-convert", action="store_true",
@@ -232,6 +237,20 @@ def main() -> int:
         sinks = torch.randn(H, generator=torch.Generator().manual_seed(spec.seed + 7)).to(dev)
     opts = dict(softcap=args.softcap, sinks=sinks)
 
+    upconvert = entry == "prefill" and spec.kv_format == I.KV_FP8_DS_MLA and args.fp8_prefill == "upconvert"
+    if upconvert and args.separate_convert:
+        print("--fp8-prefill upconvert converts through the workspace's block table in the attention kernel; "
+              "drop --separate-convert", file=sys.stderr)
+        return 2
+    if upconvert:
+        # the context of every request, block-aligned in a bf16 workspace read through its own block table
+        ws_seq = torch.full((spec.num_requests,), spec.ctx_len, dtype=torch.int32, device=dev)
+        ws_starts = (torch.arange(spec.num_requests, dtype=torch.int32, device=dev) * spec.blocks_per_req
+                     * I.BLOCK_SIZE)
+        ws_rows = torch.empty((spec.num_slots, spec.d), dtype=torch.bfloat16, device=dev)
+        ws_cache = ws_rows.view(spec.num_blocks, I.BLOCK_SIZE, spec.d)
+        ws_bt = torch.arange(spec.num_blocks, dtype=torch.int32, device=dev).view(spec.num_requests, -1)
+
     # the global indices and valid counts, for the byte / FLOP counts and the
     # CPU baseline (the step below converts again, inside the attention kernel)
     smla.convert_indices(req, bt, loc, out=gidx, valid_counts=vcnt)
@@ -244,7 +263,11 @@ def main() -> int:
             idx, conv = gidx, dict(topk_length=vcnt)
         else:                       # request-local indices, converted by the attention kernel
             idx, conv = loc, dict(block_table=bt, req_id=req, block_size=I.BLOCK_SIZE)
-        if entry == "decode":
+        if upconvert:
+            smla.gather_upconvert(caches[c], bt, ws_seq, ws_starts, spec.ctx_len, ws_rows, block_size=I.BLOCK_SIZE)
+            conv = dict(conv, block_table=ws_bt)           # request-local positions -> workspace rows
+            smla.prefill_fwd(qn, qr, ws_cache, idx, spec.softmax_scale, out=out, lse=lse, **conv, **opts)
+        elif entry == "decode":
             smla.decode_fwd(qn, qr, caches[c], idx, spec.softmax_scale, kv_format=spec.kv_format,
                             k_scale=kscales[c], group_scales=gscales[c], out=out, lse=lse, workspace=ws,
                             num_splits=args.splits, **conv, **opts)
@@ -348,6 +371,8 @@ def main() -> int:
                    "kv_storage": KV_STORAGE[spec.kv_format],
                    "index_conversion": "separate kernel" if args.separate_convert else "in the attention kernel",
                    "softcap": args.softcap, "sinks": bool(args.sinks),
+                   "fp8_prefill": (args.fp8_prefill if entry == "prefill" and spec.kv_format == I.KV_FP8_DS_MLA
+                                   else None),
                    "timing": "HIP graph of R steps replayed; cold L2/MALL by cache rotation"},
         "tflops": round(tflops, 2),
         "pct_of_path_roofline": round(100 * roofline_time / (dt / steps), 2),

@@ -251,6 +251,55 @@ int smla_decode_fwd(const smla_attn_args* args, void* workspace, size_t workspac
 int smla_prefill_fwd(const smla_attn_args* args, void* stream);
 
 /*
+ * Planned valid counts (FlashInfer sparse SM90 backend, _kv_lens_host and
+ * _clamp_work_kv_end): the valid count of every query row from the batch
+ * layout alone, with no device-to-host copy. Row t belongs to request
+ * r = req_id_per_token[t]; the rows of request r are query_start_loc[r] ..
+ * query_start_loc[r+1]-1, and row t sees
+ *   ctx = seq_lens[r] - query_start_loc[r+1] + t + 1
+ * tokens. The pooled top-k indexer keeps all of them when ctx <= topk and
+ * otherwise topk pool-expanded tokens plus the trailing incomplete pool:
+ *   valid_counts_out[t] = ctx <= topk ? ctx : topk + ctx % kpool.
+ * A request id outside [0, num_reqs) or ctx <= 0 gives 0. The counts equal the
+ * valid entries of the converted rows when the indexer's selection has that
+ * shape, and serve as topk_length for the attention.
+ *   seq_lens [num_reqs], query_start_loc [num_reqs + 1], req_id_per_token
+ *   [num_tokens], valid_counts_out [num_tokens]: int32 device arrays.
+ * Errors: num_reqs < 1, topk < 1 or kpool < 1, NULL pointers.
+ */
+int smla_planned_valid_counts(const int32_t* seq_lens, const int32_t* query_start_loc,
+                              const int32_t* req_id_per_token, int32_t num_reqs, int32_t num_tokens,
+                              int32_t topk, int32_t kpool, int32_t* valid_counts_out, void* stream);
+
+/*
+ * Gather and upconvert (the FP8 prefill path of the FlashMLA sparse backend,
+ * forward_mqa: cp_gather_and_upconvert_fp8_kv_cache of a chunk's contexts into
+ * a bf16 workspace, then the bf16 kernel over the workspace). For every
+ * request r and position p < min(seq_lens[r], max_blocks * block_size),
+ * workspace row workspace_starts[r] + p gets the packed FP8 row at slot
+ * block_table[r][p / block_size] * block_stride_rows + p % block_size, as bf16:
+ * latent channel c = bf16_rne(fl32(e4m3(code c) * scale[c / 128])) (the pages
+ * name the operation, not its rounding; this is the plain reading), rope
+ * channels copied. A negative table entry or a slot >= num_slots gives a zero
+ * row; rows outside [0, workspace_rows) are not written.
+ *   kv_cache: packed rows (kv_format must be SMLA_KV_FP8_DS_MLA), stride >= 656.
+ *   block_table [num_reqs][bt_row_stride] int32; seq_lens, workspace_starts
+ *   [num_reqs] int32; max_seq_len >= every seq_lens[r] (positions past it are
+ *   not written); block_stride_rows = 0 means block_size.
+ *   workspace: bf16 [workspace_rows][workspace_row_stride] (>= 576 elements, a
+ *   multiple of 8), 16-byte aligned.
+ * The bf16 attention then reads the workspace with indices
+ * workspace_starts[r] + p (or request-local indices through a block table
+ * that maps request r's block b to workspace block starts[r] / B + b).
+ */
+int smla_gather_upconvert(const void* kv_cache, int64_t num_slots, int64_t kv_row_stride_bytes,
+                          int32_t kv_format, const int32_t* block_table, int32_t num_reqs, int32_t max_blocks,
+                          int64_t bt_row_stride, int32_t block_size, int32_t block_stride_rows,
+                          const int32_t* seq_lens, const int32_t* workspace_starts, int32_t max_seq_len,
+                          void* workspace, int64_t workspace_rows, int64_t workspace_row_stride,
+                          void* stream);
+
+/*
  * Cache write (vLLM concat_and_cache_mla as called by do_kv_cache_update):
  * row slot_mapping[t] of the cache gets [kv_c[t][0:512] | k_pe[t][0:d_rope]].
  * slot_mapping < 0 skips the token. Formats:

@@ -296,12 +296,16 @@ def planned_valid_counts(seq_lens: np.ndarray, query_start_loc: np.ndarray, req_
     """Valid count of every query row t (request r = req_id[t], rows of request
     r are query_start_loc[r] .. query_start_loc[r+1]-1): with
     ctx = seq_lens[r] - query_start_loc[r+1] + t + 1, ctx if ctx <= topk,
-    else topk + ctx % kpool. int32 [T]."""
+    else topk + ctx % kpool. A request id outside [0, R) or ctx <= 0 gives 0.
+    int32 [T]."""
     seq = np.asarray(seq_lens, dtype=np.int64)
     qsl = np.asarray(query_start_loc, dtype=np.int64)
     req = np.asarray(req_id, dtype=np.int64)
+    ok = (req >= 0) & (req < seq.shape[0])
+    rq = np.where(ok, req, 0)
     rows = np.arange(req.shape[0], dtype=np.int64)
-    ctx = seq[req] - qsl[req + 1] + rows + 1
+    ctx = np.where(ok, seq[rq] - qsl[rq + 1] + rows + 1, 0)
+    ctx = np.maximum(ctx, 0)
     return np.where(ctx <= topk, ctx, topk + ctx % kpool).astype(np.int32)
 
 
@@ -332,15 +336,25 @@ def gather_upconvert(cache: np.ndarray, block_table: np.ndarray, seq_lens: np.nd
                      workspace_starts: np.ndarray, block_size: int, workspace: np.ndarray,
                      block_stride_rows: Optional[int] = None) -> None:
     """Row workspace_starts[r] + p of ``workspace`` (bf16 bits [W, 576]) gets
-    request r's context position p < seq_lens[r], read from the packed cache at
-    slot block_table[r][p // B] * stride + p % B and upconverted."""
+    request r's context position p < seq_lens[r] (and p < max_blocks * B), read
+    from the packed cache at slot block_table[r][p // B] * stride + p % B and
+    upconverted. A negative table entry or a slot past the cache gives a zero
+    row; rows that fall outside the workspace are not written."""
     stride = block_size if block_stride_rows is None else block_stride_rows
     bt = np.asarray(block_table, dtype=np.int64)
+    S, W = cache.shape[0], workspace.shape[0]
     for r in range(bt.shape[0]):
-        n = int(seq_lens[r])
-        p = np.arange(n)
-        slots = bt[r, p // block_size] * stride + p % block_size
-        workspace[int(workspace_starts[r]) + p] = upconvert_rows(cache, slots)
+        n = min(int(seq_lens[r]), bt.shape[1] * block_size)
+        for pos in range(max(n, 0)):
+            w = int(workspace_starts[r]) + pos
+            if w < 0 or w >= W:
+                continue
+            e = bt[r, pos // block_size]
+            slot = e * stride + pos % block_size
+            if e < 0 or slot >= S:
+                workspace[w] = 0
+            else:
+                workspace[w] = upconvert_rows(cache, [slot])[0]
 
 
 def dcp_owner_local(pos: np.ndarray, dcp_size: int, interleave: int):

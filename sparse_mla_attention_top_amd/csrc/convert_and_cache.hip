@@ -237,6 +237,86 @@ cache_write_kernel(const uint16_t* __restrict__ kv_c, int64_t kv_c_stride,
   }
 }
 
+// Planned valid counts (FlashInfer sparse SM90 backend, _kv_lens_host and
+// _clamp_work_kv_end): row t of request r = req_id[t] sees
+// ctx = seq_lens[r] - query_start_loc[r + 1] + t + 1 tokens, and the pooled
+// indexer keeps ctx of them up to topk, else topk + ctx % kpool. A request id
+// outside [0, num_reqs) or ctx <= 0 gives 0.
+__global__ void __launch_bounds__(256)
+planned_counts_kernel(const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ query_start_loc,
+                      const int32_t* __restrict__ req_id, int32_t num_reqs, int32_t num_tokens, int32_t topk,
+                      int32_t kpool, int32_t* __restrict__ out) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= num_tokens) return;
+  const int r = req_id[t];
+  int64_t ctx = 0;
+  if (r >= 0 && r < num_reqs) ctx = (int64_t)seq_lens[r] - query_start_loc[r + 1] + t + 1;
+  if (ctx < 0) ctx = 0;
+  out[t] = (int32_t)(ctx <= topk ? ctx : topk + ctx % kpool);
+}
+
+// Gather and upconvert of packed FP8 rows into a bf16 workspace (the FP8
+// prefill path of the FlashMLA sparse backend: cp_gather_and_upconvert of a
+// chunk's contexts, then the bf16 kernel over the workspace). Workspace row
+// starts[r] + p gets request r's position p: latent channel c is
+// bf16_rne(fl32(e4m3 * scale[c / 128])), the rope channels are copied. One wave
+// per row: lane c8 converts latent channels 8 c8 .. 8 c8 + 7, lanes 0..7 copy
+// the 8 rope chunks.
+__global__ void __launch_bounds__(256)
+gather_upconvert_kernel(const uint8_t* __restrict__ cache, int64_t num_slots, int64_t row_stride,
+                        const int32_t* __restrict__ block_table, int32_t max_blocks, int64_t bt_row_stride,
+                        int32_t block_size, int32_t block_stride_rows, const int32_t* __restrict__ seq_lens,
+                        const int32_t* __restrict__ starts, uint16_t* __restrict__ ws, int64_t ws_rows,
+                        int64_t ws_stride) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.y;
+  const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int n = min((int64_t)seq_lens[r], (int64_t)max_blocks * block_size);
+  if (p >= n) return;
+  const int64_t w = (int64_t)starts[r] + p;
+  if (w < 0 || w >= ws_rows) return;
+  const int blk = p / block_size;
+  const int e = block_table[(int64_t)r * bt_row_stride + blk];
+  const int64_t slot = (int64_t)e * block_stride_rows + (p - blk * block_size);
+  uint16_t* dst = ws + w * ws_stride;
+  if (e < 0 || slot >= num_slots) {
+    *(u32x4*)(dst + 8 * lane) = (u32x4){0u, 0u, 0u, 0u};
+    if (lane < 8) *(u32x4*)(dst + 512 + 8 * lane) = (u32x4){0u, 0u, 0u, 0u};
+    return;
+  }
+  const uint8_t* row = cache + slot * row_stride;
+  const uint2 codes = *(const uint2*)(row + 8 * lane);
+  const float sc = *(const float*)(row + 512 + 4 * (lane >> 4));
+  u32x4 rope = {};
+  if (lane < 8) rope = *(const u32x4*)(row + 528 + 16 * lane);
+  // channels 8 lane + 2i, 8 lane + 2i + 1 from bytes 2i, 2i+1 of the 8 codes
+  f32x2 v[4] = {__builtin_amdgcn_cvt_pk_f32_fp8((int)codes.x, false), __builtin_amdgcn_cvt_pk_f32_fp8((int)codes.x, true),
+                __builtin_amdgcn_cvt_pk_f32_fp8((int)codes.y, false), __builtin_amdgcn_cvt_pk_f32_fp8((int)codes.y, true)};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) o[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v[i] * sc, bf16x2));
+  *(u32x4*)(dst + 8 * lane) = (u32x4){o[0], o[1], o[2], o[3]};
+  if (lane < 8) *(u32x4*)(dst + 512 + 8 * lane) = rope;
+}
+
+hipError_t launch_planned_counts(const PlannedCountsArgs& a, hipStream_t stream) {
+  if (a.num_tokens == 0) return hipSuccess;
+  planned_counts_kernel<<<(a.num_tokens + 255) / 256, 256, 0, stream>>>(
+      a.seq_lens, a.query_start_loc, a.req_id, a.num_reqs, a.num_tokens, a.topk, a.kpool, a.out);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_upconvert(const UpconvertArgs& a, hipStream_t stream) {
+  if (a.num_reqs == 0 || a.max_seq_len <= 0) return hipSuccess;
+  dim3 grid((a.max_seq_len + 3) / 4, a.num_reqs);
+  gather_upconvert_kernel<<<grid, 256, 0, stream>>>(a.cache, a.num_slots, a.row_stride, a.block_table, a.max_blocks,
+                                                    a.bt_row_stride, a.block_size, a.block_stride_rows, a.seq_lens,
+                                                    a.starts, a.ws, a.ws_rows, a.ws_stride);
+  return hipGetLastError();
+}
+
 hipError_t launch_convert(const ConvertArgs& a, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;
   convert_indices_kernel<<<a.num_tokens, 256, 0, stream>>>(

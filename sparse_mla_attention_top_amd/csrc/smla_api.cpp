@@ -205,6 +205,50 @@ int smla_dcp_filter_convert(const int32_t* req_id, const int32_t* block_table, i
   return hip_status(smla::launch_dcp_filter(a, (hipStream_t)stream), "dcp_filter_convert launch");
 }
 
+int smla_planned_valid_counts(const int32_t* seq_lens, const int32_t* query_start_loc,
+                              const int32_t* req_id_per_token, int32_t num_reqs, int32_t num_tokens, int32_t topk,
+                              int32_t kpool, int32_t* valid_counts_out, void* stream) {
+  if (num_reqs < 1 || num_tokens < 0) return fail(SMLA_ERR_INVALID_ARG, "num_reqs=%d num_tokens=%d", num_reqs, num_tokens);
+  if (topk < 1 || kpool < 1) return fail(SMLA_ERR_INVALID_ARG, "topk=%d kpool=%d must be >= 1", topk, kpool);
+  if (num_tokens == 0) return ok();
+  if (!seq_lens || !query_start_loc || !req_id_per_token || !valid_counts_out)
+    return fail(SMLA_ERR_INVALID_ARG, "NULL pointer argument");
+  smla::PlannedCountsArgs a{seq_lens, query_start_loc, req_id_per_token, num_reqs, num_tokens, topk, kpool,
+                            valid_counts_out};
+  return hip_status(smla::launch_planned_counts(a, (hipStream_t)stream), "planned_valid_counts launch");
+}
+
+int smla_gather_upconvert(const void* kv_cache, int64_t num_slots, int64_t kv_row_stride_bytes, int32_t kv_format,
+                          const int32_t* block_table, int32_t num_reqs, int32_t max_blocks, int64_t bt_row_stride,
+                          int32_t block_size, int32_t block_stride_rows, const int32_t* seq_lens,
+                          const int32_t* workspace_starts, int32_t max_seq_len, void* workspace,
+                          int64_t workspace_rows, int64_t workspace_row_stride, void* stream) {
+  if (kv_format != SMLA_KV_FP8_DS_MLA)
+    return fail(SMLA_ERR_UNSUPPORTED, "gather_upconvert reads the packed FP8 format only (kv_format=%d)", kv_format);
+  if (num_reqs < 0 || max_seq_len < 0) return fail(SMLA_ERR_INVALID_ARG, "num_reqs=%d max_seq_len=%d", num_reqs, max_seq_len);
+  if (num_slots < 1 || num_slots > INT32_MAX)
+    return fail(SMLA_ERR_INVALID_ARG, "num_slots=%lld outside 1..2^31-1", (long long)num_slots);
+  if (kv_row_stride_bytes < 656 || kv_row_stride_bytes % 16 != 0)
+    return fail(SMLA_ERR_INVALID_ARG, "kv_row_stride_bytes=%lld must be >= 656 and a multiple of 16",
+                (long long)kv_row_stride_bytes);
+  if (max_blocks < 1 || bt_row_stride < max_blocks || block_size < 1 || block_stride_rows < 0)
+    return fail(SMLA_ERR_INVALID_ARG, "block table shape invalid (max_blocks=%d stride=%lld block_size=%d)",
+                max_blocks, (long long)bt_row_stride, block_size);
+  if (workspace_rows < 0 || workspace_row_stride < 576 || workspace_row_stride % 8 != 0)
+    return fail(SMLA_ERR_INVALID_ARG, "workspace row stride must be >= 576 and a multiple of 8 elements");
+  if (num_reqs > 65535) return fail(SMLA_ERR_UNSUPPORTED, "num_reqs above 65535");
+  if (num_reqs == 0 || max_seq_len == 0 || workspace_rows == 0) return ok();
+  if (!kv_cache || !block_table || !seq_lens || !workspace_starts || !workspace)
+    return fail(SMLA_ERR_INVALID_ARG, "NULL pointer argument");
+  if (!aligned16(kv_cache) || !aligned16(workspace))
+    return fail(SMLA_ERR_INVALID_ARG, "kv_cache and workspace must be 16-byte aligned");
+  smla::UpconvertArgs a{(const uint8_t*)kv_cache, num_slots, kv_row_stride_bytes, block_table, num_reqs, max_blocks,
+                        bt_row_stride, block_size, block_stride_rows == 0 ? block_size : block_stride_rows,
+                        seq_lens, workspace_starts, max_seq_len, (uint16_t*)workspace, workspace_rows,
+                        workspace_row_stride};
+  return hip_status(smla::launch_gather_upconvert(a, (hipStream_t)stream), "gather_upconvert launch");
+}
+
 int smla_merge_partials(const void* part_out, int64_t part_out_stride_part, int64_t part_out_stride_tok,
                         int64_t part_out_stride_head, const float* part_lse, int64_t part_lse_stride_part,
                         int64_t part_lse_stride_tok, int32_t num_parts, int32_t num_tokens, int32_t num_heads,

@@ -48,6 +48,28 @@ struct MergeArgs {
   const float* sinks;   // [num_heads] extra logits (zero value rows), or nullptr
 };
 
+struct PlannedCountsArgs {
+  const int32_t* seq_lens;
+  const int32_t* query_start_loc;
+  const int32_t* req_id;
+  int32_t num_reqs, num_tokens, topk, kpool;
+  int32_t* out;
+};
+
+struct UpconvertArgs {
+  const uint8_t* cache;
+  int64_t num_slots, row_stride;
+  const int32_t* block_table;
+  int32_t num_reqs, max_blocks;
+  int64_t bt_row_stride;
+  int32_t block_size, block_stride_rows;
+  const int32_t* seq_lens;
+  const int32_t* starts;
+  int32_t max_seq_len;
+  uint16_t* ws;
+  int64_t ws_rows, ws_stride;
+};
+
 struct CacheWriteArgs {
   const uint16_t* kv_c;
   int64_t kv_c_stride;
@@ -104,6 +126,8 @@ hipError_t launch_convert(const ConvertArgs& a, hipStream_t stream);
 hipError_t launch_dcp_filter(const DcpFilterArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream);
+hipError_t launch_planned_counts(const PlannedCountsArgs& a, hipStream_t stream);
+hipError_t launch_gather_upconvert(const UpconvertArgs& a, hipStream_t stream);
 // splits == 1: direct output. splits > 1: partials into workspace + combine.
 hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, bool longest_first,
                             hipStream_t stream);

@@ -104,6 +104,10 @@ SPECS = {
     # FlashMLA sparse backend (heads padded to 64 / 128 there; here h = 128)
     "longctx_ds_mla": WorkloadSpec("longctx_ds_mla", 606, 64, 4, 65532, 65536, 128, 64,
                                    KV_FP8_DS_MLA, 2048, 192 ** -0.5, "min_pos"),
+    # the bf16 prefill shape on packed FP8 rows (the FP8 prefill of the pages'
+    # FlashMLA sparse backend)
+    "prefill_ds_mla": WorkloadSpec("prefill_ds_mla", 707, 1, 4096, 0, 4096, 128, 64, KV_FP8_DS_MLA,
+                                   2048, 192 ** -0.5, "min_pos", identity_blocks=True),
 }
 
 

@@ -37,6 +37,8 @@ EXPORTED = (
     "smla_attn_args_size",
     "smla_dcp_filter_convert",
     "smla_merge_partials",
+    "smla_planned_valid_counts",
+    "smla_gather_upconvert",
 )
 
 
@@ -106,6 +108,11 @@ def load() -> ctypes.CDLL:
     lib.smla_dcp_filter_convert.restype = ctypes.c_int
     lib.smla_merge_partials.argtypes = [vp, i64, i64, i64, vp, i64, i64, i32, i32, i32, vp, i64, i64, vp, i64, vp]
     lib.smla_merge_partials.restype = ctypes.c_int
+    lib.smla_planned_valid_counts.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp]
+    lib.smla_planned_valid_counts.restype = ctypes.c_int
+    lib.smla_gather_upconvert.argtypes = [vp, i64, i64, i32, vp, i32, i32, i64, i32, i32, vp, vp, i32, vp, i64, i64,
+                                          vp]
+    lib.smla_gather_upconvert.restype = ctypes.c_int
     lib.smla_decode_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.smla_decode_workspace_size.restype = sz
     lib.smla_decode_num_splits.argtypes = [i32, i32, i32, i32]
@@ -229,6 +236,44 @@ def merge_partials(part_out: torch.Tensor, part_lse: torch.Tensor, out: Optional
                                     lse.stride(0) if lse is not None else 0, _stream(stream))
     _check("smla_merge_partials", rc)
     return out, lse
+
+
+def planned_valid_counts(seq_lens: torch.Tensor, query_start_loc: torch.Tensor, req_id: torch.Tensor, topk: int,
+                         kpool: int, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Valid count of every query row from the batch layout (int32 [T])."""
+    for name, t in (("seq_lens", seq_lens), ("query_start_loc", query_start_loc), ("req_id", req_id)):
+        _need(t.dtype == torch.int32 and t.dim() == 1 and t.is_contiguous(), f"{name} must be contiguous int32 [n]")
+    R, T = seq_lens.shape[0], req_id.shape[0]
+    _need(query_start_loc.shape[0] == R + 1, "query_start_loc must be int32 [num_reqs + 1]")
+    if out is None:
+        out = torch.empty((T,), dtype=torch.int32, device=req_id.device)
+    _need(out.dtype == torch.int32 and out.numel() == T and out.is_contiguous(), "out must be int32 [T]")
+    rc = load().smla_planned_valid_counts(_ptr(seq_lens), _ptr(query_start_loc), _ptr(req_id), R, T, int(topk),
+                                          int(kpool), _ptr(out), _stream(stream))
+    _check("smla_planned_valid_counts", rc)
+    return out
+
+
+def gather_upconvert(kv_cache: torch.Tensor, block_table: torch.Tensor, seq_lens: torch.Tensor,
+                     workspace_starts: torch.Tensor, max_seq_len: int, workspace: torch.Tensor,
+                     block_size: int = 64, block_stride_rows: int = 0, stream=None) -> torch.Tensor:
+    """Gather each request's context rows from a packed FP8 cache into the bf16
+    workspace [W, 576] at workspace_starts[r] + position."""
+    S, row_stride, width = _kv_geometry(kv_cache)
+    _check_kv(kv_cache, KV_FP8_DS_MLA, width, S, None)
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.stride(1) == 1,
+          "block_table must be int32 [num_reqs, max_blocks]")
+    R = block_table.shape[0]
+    for name, t in (("seq_lens", seq_lens), ("workspace_starts", workspace_starts)):
+        _need(t.dtype == torch.int32 and t.numel() == R and t.is_contiguous(), f"{name} must be contiguous int32 [R]")
+    _need(workspace.dtype == torch.bfloat16 and workspace.dim() == 2 and workspace.shape[1] >= 576
+          and workspace.stride(1) == 1, "workspace must be bf16 [W, >= 576]")
+    rc = load().smla_gather_upconvert(_ptr(kv_cache), S, row_stride, KV_FP8_DS_MLA, _ptr(block_table), R,
+                                      block_table.shape[1], _bt_row_stride(block_table), int(block_size),
+                                      int(block_stride_rows), _ptr(seq_lens), _ptr(workspace_starts), int(max_seq_len),
+                                      _ptr(workspace), workspace.shape[0], workspace.stride(0), _stream(stream))
+    _check("smla_gather_upconvert", rc)
+    return workspace
 
 
 # ---------------------------------------------------------------------------

@@ -135,3 +135,16 @@ def test_packed_fp8_format_rejects_bad_arguments():
     assert b"group_scales" in lib.smla_last_error()
     assert lib.smla_cache_write(16, 512, 16, 64, 16, 2, 64, 3, 1.0, 16, 4, 576, None, None) == -1  # stride < 656
     assert lib.smla_cache_write(16, 512, None, 0, 16, 2, 0, 3, 1.0, 16, 4, 656, None, None) == -2  # no rope
+
+
+def test_planned_counts_and_upconvert_reject_bad_arguments():
+    lib = smla.load()
+    assert lib.smla_planned_valid_counts(16, 16, 16, 0, 4, 64, 1, 16, None) == -1     # no requests
+    assert lib.smla_planned_valid_counts(16, 16, 16, 2, 4, 64, 0, 16, None) == -1     # kpool 0
+    assert lib.smla_planned_valid_counts(None, None, None, 2, 0, 64, 1, None, None) == 0  # no rows: no-op
+    # only the packed format; row stride; workspace stride
+    assert lib.smla_gather_upconvert(16, 10, 656, 2, 16, 1, 4, 4, 64, 0, 16, 16, 8, 16, 8, 576, None) == -2
+    assert lib.smla_gather_upconvert(16, 10, 640, 3, 16, 1, 4, 4, 64, 0, 16, 16, 8, 16, 8, 576, None) == -1
+    assert lib.smla_gather_upconvert(16, 10, 656, 3, 16, 1, 4, 4, 64, 0, 16, 16, 8, 16, 8, 570, None) == -1
+    assert lib.smla_gather_upconvert(16, 10, 656, 3, 16, 1, 4, 2, 64, 0, 16, 16, 8, 16, 8, 576, None) == -1
+    assert lib.smla_last_error()
