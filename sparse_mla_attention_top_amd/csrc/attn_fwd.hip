@@ -654,16 +654,21 @@ smla_attn_kernel(KParams p) {
           convert_tile_s(0);
         }
       }
+      // the index entry of row l & 31 of the next tile is read one tile ahead,
+      // so the row mask needs no LDS round trip at the start of a tile
+      int idx_next = ntiles > 0 ? sidx[l & 31] : -1;
       lds_barrier();                                       // pass start: tile 0 is in LDS
       for (int i = 0; i <= ntiles; i++) {
         const bool have = i < ntiles;
+        const int idx_cur = idx_next;
+        if (i + 1 < ntiles) idx_next = sidx[(i + 1) * kTileRows + (l & 31)];
         if (F8 && i + 2 < ntiles) issue_tile_s(i + 2);
         f32x4 r0 = {}, r1 = {};
         uint32_t vmask = 0;
         float tv[2][4];
         float mx[2] = {-INFINITY, -INFINITY};
         if (have) {
-          vmask = (uint32_t)__ballot((l < 32) ? (sidx[i * kTileRows + l] >= 0) : 0);
+          vmask = (uint32_t)__ballot(l < 32 && idx_cur >= 0);
           seen = seen || vmask != 0;
           scores(i, r0, r1);
           if (!full || i == 0) scaled(r0, r1, vmask, tv, mx);
