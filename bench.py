@@ -97,6 +97,23 @@ def hip_elapsed_ms(a, b) -> float:
     return ms.value
 
 
+def kernel_percentiles(ms_list):
+    """p10, median and p90 of per-launch kernel durations, in microseconds."""
+    import numpy as np
+    v = np.asarray(ms_list, dtype=np.float64) * 1e3
+    return [round(float(x), 3) for x in np.percentile(v, [10, 50, 90])]
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, gidx_np, valid_np, min_seconds: float, k_scale: float, softcap: float = 0.0, sinks=None):
     """The fp64 oracle on the host over a sample of the workload's tokens. FP8
     workloads: the rows the sample reads are quantised by the oracle's own
@@ -141,7 +158,7 @@ def cpu_baseline(w, gidx_np, valid_np, min_seconds: float, k_scale: float, softc
     sample = (f"{len(tokens)} tokens of the same workload (all h={spec.heads} heads, their full top-k rows) "
               f"x {reps} repetitions, numpy fp64")
     return {"value": n_tok / dt, "unit": "query tokens/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "seconds": round(dt, 2)}
+            "sample": sample, "seconds": round(dt, 2), "cpu": cpu_model(), "host_cpus": os.cpu_count()}
 
 
 def build_caches(spec, w, R: int, dev):
@@ -328,7 +345,8 @@ def main() -> int:
         step(k)
     smla.set_timing_events(None, None)
     torch.cuda.synchronize()
-    kern_ms = sum(hip_elapsed_ms(a, b) for a, b in evs) / n_ev
+    kern_all = [hip_elapsed_ms(a, b) for a, b in evs]
+    kern_ms = sum(kern_all) / n_ev
 
     gidx_np, vcnt_np = gidx.cpu().numpy(), vcnt.cpu().numpy()
     row_bytes = I.kv_row_bytes(spec)
@@ -377,6 +395,7 @@ def main() -> int:
         "tflops": round(tflops, 2),
         "pct_of_path_roofline": round(100 * roofline_time / (dt / steps), 2),
         "attn_kernel_us": round(kern_ms * 1e3, 3),
+        "attn_kernel_us_p10_p50_p90": kernel_percentiles(kern_all),
         "alg_bytes_per_step": alg_bytes,
         "alg_flops_per_step": flops,
         "roofline": roof,
@@ -499,7 +518,8 @@ def run_dcp(args) -> int:
         step(k)
     smla.set_timing_events(None, None)
     torch.cuda.synchronize()
-    kern_ms = sum(hip_elapsed_ms(a, b) for a, b in evs) / n_ev
+    kern_all = [hip_elapsed_ms(a, b) for a, b in evs]
+    kern_ms = sum(kern_all) / n_ev
 
     # algorithmic bytes of the rank's attention: its rows, Q, its partial, indices
     loc_np = loc.cpu().numpy()
@@ -536,6 +556,7 @@ def run_dcp(args) -> int:
                    "cache_copies_rotated": R, "merged_vs_unsharded_max_abs": [derr, lerr],
                    "timing": "HIP graph of R steps replayed; the other ranks' partials precomputed"},
         "attn_kernel_us": round(kern_ms * 1e3, 3),
+        "attn_kernel_us_p10_p50_p90": kernel_percentiles(kern_all),
         "alg_bytes_per_step": int(alg_bytes),
         "roofline": roof,
         "cpu_baseline": cpu,
