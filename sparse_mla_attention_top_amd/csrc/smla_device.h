@@ -60,19 +60,22 @@ __device__ __forceinline__ float wave_xor32_max(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 3-bit swizzle of a tile row: reversal of the bits of (r >> 1) & 7.
+// 3-bit swizzle of a tile row: bits 1-2 from (r >> 2) & 3, bit 0 from (r >> 1) & 1.
 __device__ __forceinline__ int swz(int r) {
-  const int a = (r >> 1) & 7;
-  return ((a & 1) << 2) | (a & 2) | ((a >> 2) & 1);
+  return (((r >> 2) & 3) << 1) | ((r >> 1) & 1);
 }
 
 // Staged cache tile layout (32 rows x NC 16-byte chunks, NC = 8 x segments of
 // 128 bytes). Block 4s + g (1 KB) holds segment s of rows 8g..8g+7; inside
 // it row r's chunk 8s + cc sits at ((r & 7) * 8 + (cc ^ swz(r))) * 16. So a
 // 64-lane global->LDS copy fills one block from 8 whole 128-byte lines (lane
-// l: row 8g + l/8), a read of one chunk by 16 consecutive rows hits 16
-// distinct 16-byte bank groups, and the transposing V reads (4 rows x 2
-// chunks per 16 lanes) are conflict-free per 32 lanes.
+// l: row 8g + l/8). LDS on gfx950 serves 512 bytes (128 banks) per cycle, 32
+// lanes of a 16-byte read at a time: the K reads (16 rows x 2 adjacent chunks
+// per 32 lanes) fall in 32 distinct 16-byte groups, because the 4 rows that
+// share (r & 3) -- 128 bytes apart -- get 4 different values of swz >> 1, and
+// the two chunks of a pair differ in bit 0. The transposing V reads (4 rows x
+// 2 chunks per 16 lanes) are conflict-free too. (Bit-reversing (r >> 1) & 7
+// instead left the K reads 2-way conflicted: measured with SQ_LDS_BANK_CONFLICT.)
 __device__ __forceinline__ int tile_pos(int r, int c) {
   return (4 * (c >> 3) + (r >> 3)) * 1024 + ((r & 7) * 8 + ((c & 7) ^ swz(r))) * 16;
 }
