@@ -116,3 +116,51 @@ def test_dcp_sharded_decode_matches_whole(W, I):
     compare(mo, ml, ref, f"dcp merged W={W}", k=2)
     assert (mo.float() - wo.float()).abs().max().item() <= 2 * OUT_TOL
     assert (ml - wl).abs().max().item() <= 2 * LSE_TOL
+
+
+def test_dcp_packed_fp8_ranks_with_sink_merge_to_the_whole():
+    """The pages' context-parallel path runs on the packed FP8 cache: each rank
+    holds its share of the positions as packed rows (written by the oracle),
+    filters and decodes it; the rank partials, merged with the sink given as
+    one more partial (0, sink), equal the whole context's attention with that
+    sink, and the oracle's."""
+    rng = np.random.default_rng(35)
+    W, I, B = 4, 64, 64
+    N, T, h, K, scale = 4096, 5, 64, 700, 192 ** -0.5
+    g = torch.Generator().manual_seed(36)
+    rows = torch.randn((N, 576), generator=g).to(torch.bfloat16)
+    q = torch.randn((T, h, 576), generator=g).to(torch.bfloat16)
+    sinks = torch.linspace(-2.0, 3.0, h)
+    pos = np.stack([rng.permutation(N)[:K] for _ in range(T)]).astype(np.int32)
+    pos[2, 400:] = -1
+    rb = bits(rows)
+    packed = np.zeros((N, 656), np.uint8)
+    O.cache_write(rb[:, :512], rb[:, 512:], np.arange(N), O.KV_FP8_DS_MLA, packed)
+    # rank caches as packed rows, laid out by the placement
+    rank, local = O.dcp_owner_local(np.arange(N), W, I)
+    req = torch.zeros(T, dtype=torch.int32, device=DEV)
+    qd = q.to(DEV)
+    parts_o, parts_l = [], []
+    say("dcp packed fp8 ranks")
+    for r in range(W):
+        own = np.nonzero(rank == r)[0]
+        nb = (own.size + B - 1) // B
+        bt = rng.permutation(nb + 2)[:nb].astype(np.int32)[None]
+        cache = np.zeros(((nb + 2) * B, 656), np.uint8)
+        cache[bt[0, local[own] // B] * B + local[own] % B] = packed[own]
+        loc, _ = smla.dcp_filter_convert(req, torch.from_numpy(bt).to(DEV), torch.from_numpy(pos).to(DEV), W, r, I,
+                                         block_size=B, compact_valid_to_front=True)
+        o, l = smla.decode_fwd(qd[..., :512], qd[..., 512:], torch.from_numpy(cache).to(DEV), loc, scale,
+                               kv_format=smla.KV_FP8_DS_MLA)
+        parts_o.append(o)
+        parts_l.append(l)
+    parts_o.append(torch.zeros_like(parts_o[0]))                 # the sink as a partial (0, sink)
+    parts_l.append(sinks.to(DEV)[None, :].expand(T, h).contiguous())
+    mo, ml = smla.merge_partials(torch.stack(parts_o), torch.stack(parts_l))
+    wo, wl = smla.decode_fwd(qd[..., :512], qd[..., 512:], torch.from_numpy(packed).to(DEV),
+                             torch.from_numpy(pos).to(DEV), scale, kv_format=smla.KV_FP8_DS_MLA,
+                             sinks=sinks.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle_for(q, packed, pos, scale, kv_format=O.KV_FP8_DS_MLA, sinks=sinks.numpy().astype(np.float64))
+    compare(wo, wl, ref, "packed whole with sink", 2)
+    compare(mo, ml, ref, "packed ranks merged with sink", 2)
