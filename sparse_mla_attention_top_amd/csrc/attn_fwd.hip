@@ -641,7 +641,8 @@ smla_attn_kernel(KParams p) {
     // flagging a rerun if a row sum left the range the reference guarantees
     // (some p = 2^(t - m) above 2^64, or not finite), or if tile 0 held no
     // valid entry (no reference) while a later tile did.
-    auto s_pass = [&](const bool full, float (&mx_all)[2], const bool issued) {
+    auto s_pass = [&](auto cap_c, const bool full, float (&mx_all)[2], const bool issued) {
+      constexpr bool CAP = decltype(cap_c)::value;          // softcap on (uniform, hoisted out of the loop)
       l_lane[0] = l_lane[1] = 0.0f;
       bool seen = false;                                   // a valid entry in some tile (uniform)
       if constexpr (F8) {                                  // this wave's share of tile 0
@@ -696,30 +697,33 @@ smla_attn_kernel(KParams p) {
         }
         if (have) {
           lds_char* pb = pbuf + (i & 1) * (4 * 64 * 16);
-          const bool all_valid = vmask == 0xffffffffu;    // uniform
+          float pr[2][4];
 #pragma unroll
           for (int nbq = 0; nbq < 2; nbq++) {
             const float nm = (m_ref[nbq] == -INFINITY) ? 0.0f : -m_ref[nbq];
             const f32x4& rs = nbq ? r1 : r0;
-            float pr[4];
-            if (p.softcap_on) {
+            if constexpr (CAP) {
               const float base = p.cap_c1 + nm, k2 = -2.0f * p.cap_c1;
 #pragma unroll
               for (int r = 0; r < 4; r++) {
                 const float e = fast_exp2(rs[r] * p.cap_a);
-                pr[r] = fast_exp2(fmaf(k2, __builtin_amdgcn_rcpf(1.0f + e), base));
+                pr[nbq][r] = fast_exp2(fmaf(k2, __builtin_amdgcn_rcpf(1.0f + e), base));
               }
             } else {
 #pragma unroll
-              for (int r = 0; r < 4; r++) pr[r] = fast_exp2(fmaf(rs[r], p.scale_log2, nm));
+              for (int r = 0; r < 4; r++) pr[nbq][r] = fast_exp2(fmaf(rs[r], p.scale_log2, nm));
             }
-            if (!all_valid) {
+          }
+          if (vmask != 0xffffffffu) {                      // uniform
 #pragma unroll
-              for (int r = 0; r < 4; r++)
-                if (!((vmask >> (16 * rh + 4 * lg + r)) & 1)) pr[r] = 0.0f;
-            }
-            l_lane[nbq] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-            const uint64_t pk = (uint64_t)pack_bf16x2(pr[0], pr[1]) | ((uint64_t)pack_bf16x2(pr[2], pr[3]) << 32);
+            for (int r = 0; r < 4; r++)
+              if (!((vmask >> (16 * rh + 4 * lg + r)) & 1)) pr[0][r] = pr[1][r] = 0.0f;
+          }
+#pragma unroll
+          for (int nbq = 0; nbq < 2; nbq++) {
+            l_lane[nbq] += (pr[nbq][0] + pr[nbq][1]) + (pr[nbq][2] + pr[nbq][3]);
+            const uint64_t pk = (uint64_t)pack_bf16x2(pr[nbq][0], pr[nbq][1]) |
+                                ((uint64_t)pack_bf16x2(pr[nbq][2], pr[nbq][3]) << 32);
             // A operand of m-block 2hg + nbq, elements 4rh .. 4rh+3
             lds_st64(pb + ((2 * hg + nbq) * 64 + l) * 16 + 8 * rh, pk);
           }
@@ -734,11 +738,12 @@ smla_attn_kernel(KParams p) {
 
     for (int attempt = 0; attempt < 2; attempt++) {
       float unused[2] = {-INFINITY, -INFINITY};
-      s_pass(true, unused, attempt == 0);
+      if (p.softcap_on) s_pass(std::true_type{}, true, unused, attempt == 0);
+      else s_pass(std::false_type{}, true, unused, attempt == 0);
       if (!s_flag) break;                                  // uniform (after the pass's last barrier)
       // exact per-head maximum, then the full pass again
       float mx_all[2] = {-INFINITY, -INFINITY};
-      s_pass(false, mx_all, false);
+      s_pass(std::false_type{}, false, mx_all, false);
       wg_max(mx_all);
       m_ref[0] = cap2(mx_all[0]);
       m_ref[1] = cap2(mx_all[1]);
