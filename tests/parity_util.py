@@ -72,3 +72,23 @@ def oracle_for(q: torch.Tensor, cache_bits: np.ndarray, global_idx: np.ndarray, 
     ln = None if lengths is None else np.asarray(lengths)[sel]
     return O.attention_with_magnitude(qf, cache_bits, kv_format, idx, scale, topk_length=ln,
                                       k_scale=k_scale, group_scales=group_scales, softcap=softcap, sinks=sinks)
+
+
+def cache_for(kv_src: torch.Tensor, kv_format: int, device: str = "cuda"):
+    """The cache of one format built from bf16 rows [S, D]: (the cache as the
+    oracle reads it, the device cache, device group scales or None, k_scale,
+    the bf16 roundings k of each P term for compare)."""
+    from sparse_mla_attention_top_amd import inputs as I
+    rows = bits(kv_src)
+    if kv_format == O.KV_BF16:
+        return rows, kv_src.to(device), None, 1.0, 1
+    if kv_format == O.KV_FP8_PER_TENSOR:
+        ks = I.per_tensor_scale_from_absmax(kv_src)
+        codes = O.quantize_per_tensor(rows, ks)
+        return codes, torch.from_numpy(codes).to(device), None, ks, 1
+    if kv_format == O.KV_FP8_GROUP128:
+        codes, sc = O.quantize_group128(rows)
+        return codes, torch.from_numpy(codes).to(device), torch.from_numpy(sc).to(device), 1.0, 2
+    packed = np.zeros((rows.shape[0], O.DS_MLA_ROW_BYTES), np.uint8)
+    O.cache_write(rows[:, :512], rows[:, 512:], np.arange(rows.shape[0]), O.KV_FP8_DS_MLA, packed)
+    return packed, torch.from_numpy(packed).to(device), None, 1.0, 2

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from oracle import sparse_mla as O
-from parity_util import bits, compare, oracle_for, say
+from parity_util import bits, cache_for, compare, oracle_for, say
 from sparse_mla_attention_top_amd import inputs as I
 from sparse_mla_attention_top_amd import smla
 
@@ -16,39 +16,22 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _cache(c, kv_format):
-    """(cache as the oracle stores it, device cache, device group scales, k_scale, k)."""
-    rows = bits(c.kv_src)
-    if kv_format == O.KV_BF16:
-        return rows, c.kv_src.to(DEV), None, 1.0, 1
-    if kv_format == O.KV_FP8_PER_TENSOR:
-        ks = I.per_tensor_scale_from_absmax(c.kv_src)
-        codes = O.quantize_per_tensor(rows, ks)
-        return codes, torch.from_numpy(codes).to(DEV), None, ks, 1
-    if kv_format == O.KV_FP8_GROUP128:
-        codes, sc = O.quantize_group128(rows)
-        return codes, torch.from_numpy(codes).to(DEV), sc, 1.0, 2
-    packed = np.zeros((rows.shape[0], O.DS_MLA_ROW_BYTES), np.uint8)
-    O.cache_write(rows[:, :512], rows[:, 512:], np.arange(rows.shape[0]), O.KV_FP8_DS_MLA, packed)
-    return packed, torch.from_numpy(packed).to(DEV), None, 1.0, 2
-
-
 def _run(c, kv_format, scale, entry, softcap=0.0, sinks=None, num_splits=0, use_lengths=True):
-    host, kv, sc, ks, k = _cache(c, kv_format)
+    host, kv, sc, ks, k = cache_for(c.kv_src, kv_format, DEV)
     q = c.q.to(DEV)
     d_rope = q.shape[2] - 512
     qn, qr = q[..., :512], (q[..., 512:] if d_rope else None)
     ln = c.lengths.to(DEV) if use_lengths else None
     sk = None if sinks is None else torch.as_tensor(sinks, dtype=torch.float32).to(DEV)
-    kw = dict(kv_format=kv_format, k_scale=ks, group_scales=None if sc is None else torch.from_numpy(sc).to(DEV),
-              topk_length=ln, softcap=softcap, sinks=sk)
+    kw = dict(kv_format=kv_format, k_scale=ks, group_scales=sc, topk_length=ln, softcap=softcap, sinks=sk)
     if entry == "decode":
         out, lse = smla.decode_fwd(qn, qr, kv, c.indices.to(DEV), scale, num_splits=num_splits, **kw)
     else:
         out, lse = smla.prefill_fwd(qn, qr, kv, c.indices.to(DEV), scale, return_lse=True, **kw)
     torch.cuda.synchronize()
     ref = oracle_for(c.q, host, c.indices.numpy(), scale, c.lengths.numpy() if use_lengths else None,
-                     kv_format=kv_format, k_scale=ks, group_scales=sc, softcap=softcap,
+                     kv_format=kv_format, k_scale=ks, group_scales=None if sc is None else sc.cpu().numpy(),
+                     softcap=softcap,
                      sinks=None if sinks is None else np.asarray(sinks, np.float64))
     compare(out, lse, ref, f"fmt={kv_format} {entry} softcap={softcap} sinks={sinks is not None}", k)
     return out, lse

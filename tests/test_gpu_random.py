@@ -1,0 +1,106 @@
+"""Seeded random configurations against the fp64 oracle: cache format, NoPE or
+rope, head count, top-k width, row lengths with scattered invalid entries,
+decode (with a random split count) or prefill, softcap and sinks, drawn
+together so that combinations no targeted test names are exercised too; and
+request-local indices converted inside the kernel through random block
+tables (block size, row stride, bad request ids, entries past the table). Each
+case is small enough for the oracle to check every output; the bar is the one
+of the other parity tests (max-abs 1e-2 plus the bf16 allowance on the output,
+1e-3 on the LSE)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import sparse_mla as O
+from parity_util import bits, cache_for, compare, oracle_for, say
+from sparse_mla_attention_top_amd import inputs as I
+from sparse_mla_attention_top_amd import smla
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+FORMATS = [O.KV_BF16, O.KV_FP8_PER_TENSOR, O.KV_FP8_GROUP128, O.KV_FP8_DS_MLA]
+
+
+def _draw(seed: int) -> dict:
+    r = np.random.default_rng(seed)
+    fmt = FORMATS[r.integers(len(FORMATS))]
+    d_rope = 64 if fmt == O.KV_FP8_DS_MLA else int(r.choice([0, 64]))
+    topk = int(r.choice([1, 2, 31, 32, 33, 64, 95, 128, 200, 257, 480, 700]))
+    T = int(r.integers(1, 6))
+    lengths = [int(r.integers(0, topk + 1)) if r.random() < 0.7 else topk for _ in range(T)]
+    return dict(fmt=fmt, d_rope=d_rope, h=int(r.integers(1, 129)), T=T, topk=topk,
+                num_slots=int(r.integers(topk, 3 * topk + 64)), lengths=lengths,
+                holes=float(r.choice([0.0, 0.0, 0.2, 0.6])), use_lengths=bool(r.random() < 0.7),
+                entry=str(r.choice(["decode", "prefill"])), splits=int(r.integers(0, 7)),
+                softcap=float(r.choice([0.0, 0.0, 0.0, 2.5, 15.0])), sinks=bool(r.random() < 0.3),
+                scale=float(r.uniform(0.03, 0.12)))
+
+
+@pytest.mark.parametrize("seed", range(1000, 1160))
+def test_random_configuration(seed):
+    cfg = _draw(seed)
+    say(f"random seed={seed} {cfg}")
+    c = I.random_case(T=cfg["T"], h=cfg["h"], d_rope=cfg["d_rope"], topk=cfg["topk"],
+                      num_slots=cfg["num_slots"], seed=seed, lengths=cfg["lengths"])
+    if cfg["holes"] > 0:                                   # invalid entries inside the rows
+        g = torch.Generator().manual_seed(seed + 1)
+        c.indices[torch.rand(c.indices.shape, generator=g) < cfg["holes"]] = -1
+    host, kv, gs, ks, k = cache_for(c.kv_src, cfg["fmt"], DEV)
+    q = c.q.to(DEV)
+    qn, qr = q[..., :512], (q[..., 512:] if cfg["d_rope"] else None)
+    ln = c.lengths.to(DEV) if cfg["use_lengths"] else None
+    sinks = None
+    if cfg["sinks"]:
+        sinks = np.random.default_rng(seed + 2).normal(0.0, 2.0, cfg["h"]).astype(np.float32)
+    kw = dict(kv_format=cfg["fmt"], k_scale=ks, group_scales=gs, topk_length=ln, softcap=cfg["softcap"],
+              sinks=None if sinks is None else torch.from_numpy(sinks).to(DEV))
+    if cfg["entry"] == "decode":
+        out, lse = smla.decode_fwd(qn, qr, kv, c.indices.to(DEV), cfg["scale"], num_splits=cfg["splits"], **kw)
+    else:
+        out, lse = smla.prefill_fwd(qn, qr, kv, c.indices.to(DEV), cfg["scale"], return_lse=True, **kw)
+    torch.cuda.synchronize()
+    ref = oracle_for(c.q, host, c.indices.numpy(), cfg["scale"], c.lengths.numpy() if cfg["use_lengths"] else None,
+                     kv_format=cfg["fmt"], k_scale=ks, group_scales=None if gs is None else gs.cpu().numpy(),
+                     softcap=cfg["softcap"], sinks=None if sinks is None else sinks.astype(np.float64))
+    compare(out, lse, ref, f"random seed={seed}", k)
+
+
+@pytest.mark.parametrize("seed", range(2000, 2032))
+def test_random_block_tables_converted_in_kernel(seed):
+    """Request-local indices through a random block table, converted in the
+    kernel: the oracle's conversion rule, then its attention."""
+    r = np.random.default_rng(seed)
+    B = int(r.choice([1, 16, 48, 64, 100]))
+    stride = B + int(r.choice([0, 0, 8]))
+    R, MB = int(r.integers(1, 5)), int(r.integers(1, 12))
+    T, h, K = int(r.integers(1, 6)), int(r.integers(1, 129)), int(r.choice([32, 96, 300, 512]))
+    num_slots = R * MB * stride
+    bt = r.permutation(R * MB).astype(np.int32).reshape(R, MB)
+    req = r.integers(-1, R + 1, T).astype(np.int32)          # -1 and R are bad request ids
+    loc = r.integers(-1, MB * B + B, (T, K)).astype(np.int32)  # past the table for some entries
+    entry = str(r.choice(["decode", "prefill"]))
+    splits = int(r.integers(0, 5))
+    say(f"random block table seed={seed} B={B} stride={stride} R={R} MB={MB} T={T} h={h} K={K} {entry} splits={splits}")
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((T, h, 576), generator=g).to(torch.bfloat16)
+    kv = torch.randn((num_slots, 576), generator=g).to(torch.bfloat16)
+    good = (req >= 0) & (req < R)                            # a bad request id leaves its row empty
+    go, _ = O.convert_indices(np.where(good, req, 0), bt, loc, B, block_stride_rows=stride)
+    qd = q.to(DEV)
+    kvd = kv.to(DEV)
+    kw = dict(block_table=torch.from_numpy(bt).to(DEV), req_id=torch.from_numpy(req).to(DEV), block_size=B,
+              block_stride_rows=stride)
+    if entry == "decode":
+        out, lse = smla.decode_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(loc).to(DEV), 0.07,
+                                   num_splits=splits, **kw)
+    else:
+        out, lse = smla.prefill_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(loc).to(DEV), 0.07,
+                                    return_lse=True, **kw)
+    torch.cuda.synchronize()
+    keep = np.nonzero(good)[0]
+    if keep.size:
+        ref = oracle_for(q[torch.from_numpy(keep)], bits(kv), go[keep], 0.07)
+        kd = torch.from_numpy(keep).to(DEV)
+        compare(out[kd], lse[kd], ref, f"random block table seed={seed}")
+    bad = torch.from_numpy(np.nonzero(~good)[0]).to(DEV)
+    assert (out[bad] == 0).all() and torch.isneginf(lse[bad]).all()
