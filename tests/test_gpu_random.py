@@ -1,12 +1,17 @@
-"""Seeded random configurations against the fp64 oracle: cache format, NoPE or
-rope, head count, top-k width, row lengths with scattered invalid entries,
-decode (with a random split count) or prefill, softcap and sinks, drawn
-together so that combinations no targeted test names are exercised too; and
-request-local indices converted inside the kernel through random block
-tables (block size, row stride, bad request ids, entries past the table). Each
-case is small enough for the oracle to check every output; the bar is the one
-of the other parity tests (max-abs 1e-2 plus the bf16 allowance on the output,
-1e-3 on the LSE)."""
+"""Seeded random configurations.
+
+Attention against the fp64 oracle: cache format, NoPE or rope, head count,
+top-k width, row lengths with scattered invalid entries, decode (with a random
+split count) or prefill, softcap and sinks, drawn together so that
+combinations no targeted test names are exercised too; and request-local
+indices converted inside the kernel through random block tables (block size,
+row stride, bad request ids, entries past the table). Each case is small
+enough for the oracle to check every output; the bar is the one of the other
+parity tests (max-abs 1e-2 plus the bf16 allowance on the output, 1e-3 on the
+LSE).
+
+Index work, bit-exact against the oracle: the context-parallel filter and the
+planned valid counts."""
 import numpy as np
 import pytest
 import torch
@@ -104,3 +109,53 @@ def test_random_block_tables_converted_in_kernel(seed):
         compare(out[kd], lse[kd], ref, f"random block table seed={seed}")
     bad = torch.from_numpy(np.nonzero(~good)[0]).to(DEV)
     assert (out[bad] == 0).all() and torch.isneginf(lse[bad]).all()
+
+
+@pytest.mark.parametrize("seed", range(3000, 3024))
+def test_random_context_parallel_filter(seed):
+    """One rank's filter and conversion of top-k positions, bit-exact: random
+    rank count, rank, interleave, block size, row widths past one pass of the
+    kernel, positions outside every table, -1 table entries, compaction."""
+    r = np.random.default_rng(seed)
+    W = int(r.integers(1, 9))
+    rank = int(r.integers(0, W))
+    IL = int(r.choice([1, 2, 16, 64]))
+    B = int(r.choice([1, 16, 64]))
+    R, MB = int(r.integers(1, 5)), int(r.integers(1, 40))
+    T, K = int(r.integers(1, 20)), int(r.choice([1, 64, 700, 2048, 2500]))
+    compact = bool(r.random() < 0.5)
+    bt = r.permutation(R * MB).astype(np.int32).reshape(R, MB)
+    bt[r.random(bt.shape) < 0.05] = -1
+    req = r.integers(0, R, T).astype(np.int32)
+    pos = r.integers(-2, W * MB * B + 50, (T, K)).astype(np.int32)
+    say(f"random dcp filter seed={seed} W={W} rank={rank} I={IL} B={B} T={T} K={K} compact={compact}")
+    g, v = smla.dcp_filter_convert(torch.from_numpy(req).to(DEV), torch.from_numpy(bt).to(DEV),
+                                   torch.from_numpy(pos).to(DEV), W, rank, IL, block_size=B,
+                                   compact_valid_to_front=compact)
+    torch.cuda.synchronize()
+    go, vo = O.dcp_filter_convert(req, bt, pos, W, rank, IL, B, compact_valid_to_front=compact)
+    assert (g.cpu().numpy() == go).all() and (v.cpu().numpy() == vo).all()
+
+
+@pytest.mark.parametrize("seed", range(4000, 4024))
+def test_random_planned_counts(seed):
+    """Valid counts planned from the batch layout, bit-exact: random request
+    count, query lengths, contexts (some shorter than their queries), top-k,
+    pool size and bad request ids."""
+    r = np.random.default_rng(seed)
+    R = int(r.integers(1, 60))
+    topk = int(r.choice([1, 64, 256, 2048]))
+    kpool = int(r.choice([1, 4, 64]))
+    q_lens = r.integers(0, 9, R)
+    seq = q_lens + r.integers(-2, 3 * topk, R)
+    qsl = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    req = np.repeat(np.arange(R), q_lens).astype(np.int32)
+    if req.size:
+        req[r.random(req.size) < 0.05] = R + 1
+    say(f"random planned counts seed={seed} R={R} topk={topk} kpool={kpool} tokens={req.size}")
+    if req.size == 0:
+        return
+    got = smla.planned_valid_counts(torch.from_numpy(seq.astype(np.int32)).to(DEV), torch.from_numpy(qsl).to(DEV),
+                                    torch.from_numpy(req).to(DEV), topk, kpool)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), O.planned_valid_counts(seq, qsl, req, topk, kpool))
