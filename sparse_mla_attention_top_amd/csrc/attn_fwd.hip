@@ -550,8 +550,7 @@ smla_attn_kernel(KParams p) {
       };
       f32x4 s0 = {}, s1 = {}, s2 = {}, s3 = {};   // even / odd k-steps: 4 independent chains
       f32x4 t0 = {}, t1 = {};
-      const lds_char* rs = rsc_buf(i) + 4 * (16 * rh + 4 * lg);
-      (void)rs;
+      [[maybe_unused]] const lds_char* rs = rsc_buf(i) + 4 * (16 * rh + 4 * lg);   // row scales (group formats)
       constexpr int PF = S::GROUP ? 2 : 6;        // K operand reads kept in flight
       bf16x8 a[PF];
       static_for<PF>([&](auto ks_c) { a[decltype(ks_c)::value] = lds_ld128(kaddr(ks_c)); });
@@ -1020,8 +1019,9 @@ int32_t plan_splits(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t
 }
 
 
-size_t workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t splits) {
-  (void)topk;
+// The partials take the same space whatever the top-k width (topk is part of
+// the signature so that a later plan may size by it).
+size_t workspace_bytes(int32_t num_tokens, int32_t num_heads, [[maybe_unused]] int32_t topk, int32_t splits) {
   if (splits <= 1) return 0;
   const size_t n = (size_t)splits * num_tokens * num_heads;
   return n * kDLatent * sizeof(uint16_t) + n * sizeof(float);
