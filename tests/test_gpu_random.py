@@ -5,7 +5,8 @@ top-k width, row lengths with scattered invalid entries, decode (with a random
 split count) or prefill, softcap and sinks, drawn together so that
 combinations no targeted test names are exercised too; and request-local
 indices converted inside the kernel through random block tables (block size,
-row stride, bad request ids, entries past the table). Each case is small
+row stride, bad request ids, entries past the table); and rows that repeat
+slots (each entry counts). Each case is small
 enough for the oracle to check every output; the bar is the one of the other
 parity tests (max-abs 1e-2 plus the bf16 allowance on the output, 1e-3 on the
 LSE).
@@ -159,3 +160,33 @@ def test_random_planned_counts(seed):
                                     torch.from_numpy(req).to(DEV), topk, kpool)
     torch.cuda.synchronize()
     assert np.array_equal(got.cpu().numpy(), O.planned_valid_counts(seq, qsl, req, topk, kpool))
+
+
+@pytest.mark.parametrize("seed", range(5000, 5008))
+def test_random_rows_with_duplicate_slots(seed):
+    """Rows drawn with replacement from a small pool of slots, so that a slot
+    repeats within a tile, across tiles and across splits: every entry counts
+    (the oracle's reading), in decode with splits and in prefill."""
+    r = np.random.default_rng(seed)
+    T, h, K = int(r.integers(1, 5)), int(r.choice([16, 64, 128])), int(r.choice([64, 300, 1024]))
+    pool = int(r.choice([1, 3, 40]))
+    fmt = FORMATS[r.integers(len(FORMATS))]
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn((T, h, 576), generator=g).to(torch.bfloat16)
+    kv = torch.randn((pool + 5, 576), generator=g).to(torch.bfloat16)
+    idx = r.integers(0, pool, (T, K)).astype(np.int32)
+    idx[r.random((T, K)) < 0.1] = -1
+    say(f"duplicate slots seed={seed} T={T} h={h} K={K} pool={pool} fmt={fmt}")
+    host, kvd, gs, ks, k = cache_for(kv, fmt, DEV)
+    qd = q.to(DEV)
+    kw = dict(kv_format=fmt, k_scale=ks, group_scales=gs)
+    ref = oracle_for(q, host, idx, 0.06, kv_format=fmt, k_scale=ks, group_scales=None if gs is None else gs.cpu().numpy())
+    for splits in (1, 3):
+        out, lse = smla.decode_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(idx).to(DEV), 0.06,
+                                   num_splits=splits, **kw)
+        torch.cuda.synchronize()
+        compare(out, lse, ref, f"duplicates decode splits={splits}", k)
+    out, lse = smla.prefill_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(idx).to(DEV), 0.06,
+                                return_lse=True, **kw)
+    torch.cuda.synchronize()
+    compare(out, lse, ref, "duplicates prefill", k)
