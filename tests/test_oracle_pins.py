@@ -141,6 +141,88 @@ def test_group_quantizer_zero_group_scale_is_one():
     assert (sc == 1.0).all() and (codes == 0).all()
 
 
+def _division_ties(rng, n: int):
+    """(bf16 bits x, fp32 scales s) such that fl32(x / s) is exactly the midpoint
+    of two neighbouring E4M3 values while the exact quotient is not: a quantizer
+    that rounds the exact (fp64) quotient goes to the nearer code, one that
+    divides in fp32 takes the tie to the even code. Built as s = fl32(x / m)
+    for random bf16 x and midpoints m, keeping the pairs with that property."""
+    mids = ((e4m3.DECODE_TABLE[8:0x7D] + e4m3.DECODE_TABLE[9:0x7E]) / 2)
+    xb = _rand_bf16(rng, (20000,))
+    x32 = O.bf16_bits_to_f32(xb)
+    m = rng.choice(mids, 20000) * np.sign(x32)
+    s = (x32 / m.astype(np.float32)).astype(np.float32)
+    ok = (s > 0) & np.isfinite(s)
+    q32 = (x32 / np.where(ok, s, 1)).astype(np.float32)
+    exact = x32.astype(np.float64) / np.where(ok, s, 1).astype(np.float64)
+    ok &= (q32.astype(np.float64) == m) & (exact != m)
+    idx = np.nonzero(ok)[0][:n]
+    assert idx.size == n
+    return xb[idx], s[idx]
+
+
+def _torch_codes(x_bits: np.ndarray, s) -> np.ndarray:
+    """torch: fp32 x / fp32 scale, cast to float8_e4m3fn."""
+    q = torch.from_numpy(O.bf16_bits_to_f32(x_bits)) / torch.as_tensor(np.asarray(s, np.float32))
+    return q.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _nearest_code_f64(v: np.ndarray) -> np.ndarray:
+    """E4M3FN code nearest to each fp64 value (ties to even), no fp32 step."""
+    pos = e4m3.DECODE_TABLE[:0x7F]
+    a = np.minimum(np.abs(v), 448.0)
+    hi = np.clip(np.searchsorted(pos, a), 1, 0x7E)
+    lo = hi - 1
+    dl, dh = a - pos[lo], pos[hi] - a
+    code = np.where((dh < dl) | ((dh == dl) & (hi % 2 == 0)), hi, lo)
+    return (code | (np.signbit(v).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def test_per_tensor_quantizer_matches_torch():
+    """The per-tensor quantizer against torch: (x_fp32 / k_scale) in fp32, then
+    torch's cast to float8_e4m3fn (round to nearest even), for quotients up to
+    464 where torch saturates to 448 as well; beyond that torch gives NaN and
+    the oracle saturates at +-448 (checked apart). Scales of the workloads'
+    absmax / 448 kind and quotients that land exactly on an E4M3 tie in fp32
+    (but not in exact arithmetic) are included, so a quantizer that multiplies
+    by the scale or divides in fp64 fails."""
+    rng = np.random.default_rng(21)
+    x = _rand_bf16(rng, (256, 576))
+    for k_scale in (float(np.float32(np.abs(O.bf16_bits_to_f32(x)).max() / np.float32(448))),
+                    0.0123, 1.0, 3.0e-3):
+        ref = (torch.from_numpy(O.bf16_bits_to_f32(x)) / torch.tensor(k_scale, dtype=torch.float32))
+        inside = ref.abs() <= 464
+        ours = O.quantize_per_tensor(x, k_scale)
+        theirs = ref.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert (ours[inside.numpy()] == theirs[inside.numpy()]).all(), k_scale
+        if (~inside).any():
+            out = ours[~inside.numpy()]
+            assert ((out & 0x7F) == 0x7E).all()
+            assert ((out >> 7) == (ref[~inside].numpy() < 0)).all()
+    xt, st = _division_ties(rng, 64)
+    ours = np.array([O.quantize_per_tensor(np.array([[xb]], np.uint16), float(sc))[0, 0] for xb, sc in zip(xt, st)])
+    assert (ours == _torch_codes(xt, st)).all()
+    assert (ours % 2 == 0).all()                      # every one of them a tie, taken to the even code
+
+
+def test_per_tensor_quantizer_planted_mistakes_are_caught(monkeypatch):
+    """A quantizer that multiplies by the scale, or divides in fp64, disagrees
+    with torch on the pin's inputs."""
+    rng = np.random.default_rng(22)
+    x = _rand_bf16(rng, (64, 512))
+    ks = 0.0123
+    theirs = (torch.from_numpy(O.bf16_bits_to_f32(x)) / torch.tensor(ks, dtype=torch.float32)
+              ).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+    def times_scale(x_bits, k_scale):
+        return e4m3.encode_rne((O.bf16_bits_to_f32(x_bits) * np.float32(k_scale)).astype(np.float32))
+
+    assert not (times_scale(x, ks) == theirs).all()
+    xt, st = _division_ties(rng, 64)
+    fp64 = _nearest_code_f64(O.bf16_bits_to_f64(xt) / st.astype(np.float64))
+    assert (fp64 != _torch_codes(xt, st)).any()
+
+
 def test_cache_write_bf16_roundtrip_and_skip():
     """Cache write then read back equals the written rows, negative slots are
     skipped (branch diff, test_kv_cache_write_read_consistency)."""
