@@ -63,8 +63,9 @@ typedef enum {
   SMLA_KV_BF16 = 0,
   /* row = D OCP E4M3FN bytes; value = e4m3(byte) * k_scale */
   SMLA_KV_FP8_E4M3_PER_TENSOR = 1,
-  /* row = D OCP E4M3FN bytes; value = e4m3(byte) * group_scales[slot][c/128]
-   * with group_scales a separate fp32 [num_slots][ceil(D/128)] array */
+  /* row = D OCP E4M3FN bytes; value = e4m3(byte) * scale g = c/128 of the
+   * slot, from a separate fp32 array with one row of ceil(D/128) scales per
+   * slot (rows group_scales_stride floats apart) */
   SMLA_KV_FP8_E4M3_GROUP128 = 2,
   /* Packed 656-byte row (the FP8 cache of the FlashMLA sparse backend, whose
    * docs give 656 bytes per token but no layout; this layout is the split of
@@ -96,7 +97,9 @@ typedef struct {
   int64_t kv_row_stride_bytes;
   int32_t kv_format;            /* smla_kv_format */
   float k_scale;                /* SMLA_KV_FP8_E4M3_PER_TENSOR */
-  const float* group_scales;    /* SMLA_KV_FP8_E4M3_GROUP128: [num_slots][ceil(D/128)] */
+  const float* group_scales;    /* SMLA_KV_FP8_E4M3_GROUP128: row `slot` holds the scales
+                                 * of groups 0..ceil(D/128)-1 at group_scales[slot *
+                                 * group_scales_stride + g] (group_scales_stride below) */
 
   /* Global slot indices [T][topk] int32 (row stride indices_stride), as
    * produced by smla_convert_indices; negative = invalid. (Request-local
@@ -149,6 +152,12 @@ typedef struct {
    *     ranks merged by smla_merge_partials, give it to one rank only. */
   float softcap;
   const float* sinks;
+
+  /* SMLA_KV_FP8_E4M3_GROUP128: floats between the scale rows of consecutive
+   * slots, >= ceil(D/128); 0 means exactly ceil(D/128). A cache written with
+   * d_rope = 64 (5 scales per row) and read by a NoPE call (d_rope = 0, 4
+   * groups used) passes 5 here. Ignored by the other formats. */
+  int64_t group_scales_stride;
 } smla_attn_args;
 
 /*
@@ -305,9 +314,11 @@ int smla_gather_upconvert(const void* kv_cache, int64_t num_slots, int64_t kv_ro
  * slot_mapping < 0 skips the token. Formats:
  *   SMLA_KV_BF16                 bf16 copy;
  *   SMLA_KV_FP8_E4M3_PER_TENSOR  byte = e4m3_rne(fl32(x / k_scale)), saturated at 448;
- *   SMLA_KV_FP8_E4M3_GROUP128    per row and 128-channel group g:
- *                                scale = fl32(absmax / 448) (1 if the group is all zero),
- *                                written to group_scales[slot][g]; byte as above;
+ *   SMLA_KV_FP8_E4M3_GROUP128    per row and 128-channel group g (g < ceil(D/128),
+ *                                D = 512 + d_rope): scale = fl32(absmax / 448) (1 if the
+ *                                group is all zero), written to group_scales[slot *
+ *                                group_scales_stride + g] (a stride of 0 means
+ *                                ceil(D/128); otherwise it must be >= that); byte as above;
  *   SMLA_KV_FP8_DS_MLA           (d_rope = 64) the 512 latent channels as in the group
  *                                format with the 4 scales written into the row at bytes
  *                                512..527, the rope channels copied as bf16 to 528..655;
@@ -318,7 +329,8 @@ int smla_gather_upconvert(const void* kv_cache, int64_t num_slots, int64_t kv_ro
 int smla_cache_write(const void* kv_c, int64_t kv_c_stride, const void* k_pe, int64_t k_pe_stride,
                      const int64_t* slot_mapping, int32_t num_tokens, int32_t d_rope,
                      int32_t kv_format, float k_scale, void* kv_cache, int64_t num_slots,
-                     int64_t kv_row_stride_bytes, float* group_scales, void* stream);
+                     int64_t kv_row_stride_bytes, float* group_scales, int64_t group_scales_stride,
+                     void* stream);
 
 /*
  * Profiling hook (not part of the computation). When set for the calling

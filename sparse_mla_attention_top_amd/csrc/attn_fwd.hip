@@ -40,7 +40,8 @@ struct KParams {
   int64_t qr_st, qr_sh;
   const uint8_t* kv;
   int64_t kv_row_stride, num_slots;
-  const float* group_scales;   // [num_slots][ceil(D/128)] (group-scaled FP8 only)
+  const float* group_scales;   // group-scaled FP8: scale g of slot s at [s * gs_stride + g]
+  int64_t gs_stride;
   const int32_t* indices;
   int64_t idx_stride;
   int32_t topk;
@@ -86,6 +87,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+// acc + the two bf16 halves of v, in one v_dot2c_f32_bf16 (v . (1, 1) + acc).
+__device__ __forceinline__ float sum_bf16x2(uint32_t v, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, v), __builtin_bit_cast(bf16x2, 0x3f803f80u), acc,
+                                         false);
 }
 
 // Reference maximum policy. O and the running sum are accumulated against a
@@ -180,6 +187,7 @@ smla_attn_kernel(KParams p) {
   // epilogue: row sums and inverse sums in latent buffer 2 (O is staged in 0-1)
   float* s_l = (float*)(s_lat + 2 * kLatBytes);
   float* s_inv = s_l + 4 * 32;
+  float* s_lb = s_inv + 64;
 
   const int w = threadIdx.x >> 6;
   const int l = threadIdx.x & 63;
@@ -330,7 +338,7 @@ smla_attn_kernel(KParams p) {
         s.rope = row + kPackedRopeAt + dcol;
         s.sc = (const float*)(p.kv + (uint64_t)(uint32_t)max(sidx[base + srow], 0) * kv_stride + kPackedScalesAt) + sgrp;
       } else if constexpr (S::GROUP) {
-        s.sc = p.group_scales + ((uint64_t)(uint32_t)max(sidx[base + srow], 0) * S::G + sgrp);
+        s.sc = p.group_scales + ((uint64_t)(uint32_t)max(sidx[base + srow], 0) * (uint64_t)p.gs_stride + sgrp);
       }
     }
     return s;
@@ -611,7 +619,14 @@ smla_attn_kernel(KParams p) {
     };
 
     float m_ref[2] = {-INFINITY, -INFINITY};
-    float l_lane[2] = {0.0f, 0.0f};
+    // Two row sums per head: l_lane of the fp32 p (the LSE and the rerun
+    // test), lb_lane of the bf16-rounded p that P.V multiplies (the output's
+    // normaliser: the output is then a weighted mean of the V rows with the
+    // weights P.V used, so rounding P moves it by sum_j dw_j (v_j - out), not
+    // by sum_j dw_j v_j; a row dominated by a few similar values comes out
+    // nearly exact). Summing the bf16 p for the LSE as well moved the LSE by
+    // up to 2^-9 relative in l, beyond its 1e-3 bar.
+    float l_lane[2] = {0.0f, 0.0f}, lb_lane[2] = {0.0f, 0.0f};
     bool have_ref = false;                                 // workgroup-uniform
     // capped value of a base-2 logit (the cap is increasing, so the capped
     // maximum is the cap of the maximum)
@@ -643,6 +658,7 @@ smla_attn_kernel(KParams p) {
     auto s_pass = [&](auto cap_c, const bool full, float (&mx_all)[2], const bool issued) {
       constexpr bool CAP = decltype(cap_c)::value;          // softcap on (uniform, hoisted out of the loop)
       l_lane[0] = l_lane[1] = 0.0f;
+      lb_lane[0] = lb_lane[1] = 0.0f;
       bool seen = false;                                   // a valid entry in some tile (uniform)
       if constexpr (F8) {                                  // this wave's share of tile 0
         if (!issued) {
@@ -720,9 +736,14 @@ smla_attn_kernel(KParams p) {
           }
 #pragma unroll
           for (int nbq = 0; nbq < 2; nbq++) {
+            // the row sum adds the fp32 p (the LSE stays exact to fp32
+            // rounding; summing the bf16-rounded p instead moved it by up to
+            // 2^-9 relative, beyond the 1e-3 LSE bar)
             l_lane[nbq] += (pr[nbq][0] + pr[nbq][1]) + (pr[nbq][2] + pr[nbq][3]);
-            const uint64_t pk = (uint64_t)pack_bf16x2(pr[nbq][0], pr[nbq][1]) |
-                                ((uint64_t)pack_bf16x2(pr[nbq][2], pr[nbq][3]) << 32);
+            const uint32_t p01 = pack_bf16x2(pr[nbq][0], pr[nbq][1]);
+            const uint32_t p23 = pack_bf16x2(pr[nbq][2], pr[nbq][3]);
+            lb_lane[nbq] = sum_bf16x2(p23, sum_bf16x2(p01, lb_lane[nbq]));
+            const uint64_t pk = (uint64_t)p01 | ((uint64_t)p23 << 32);
             // A operand of m-block 2hg + nbq, elements 4rh .. 4rh+3
             lds_st64(pb + ((2 * hg + nbq) * 64 + l) * 16 + 8 * rh, pk);
           }
@@ -739,7 +760,10 @@ smla_attn_kernel(KParams p) {
       float unused[2] = {-INFINITY, -INFINITY};
       if (p.softcap_on) s_pass(std::true_type{}, true, unused, attempt == 0);
       else s_pass(std::false_type{}, true, unused, attempt == 0);
-      if (!s_flag) break;                                  // uniform (after the pass's last barrier)
+      // uniform (after the pass's last barrier). A pass with the exact maximum
+      // is only flagged by a NaN or infinite score: that result stands (NaN
+      // propagates to the output and LSE)
+      if (!s_flag || attempt == 1) break;
       // exact per-head maximum, then the full pass again
       float mx_all[2] = {-INFINITY, -INFINITY};
       s_pass(std::false_type{}, false, mx_all, false);
@@ -752,20 +776,26 @@ smla_attn_kernel(KParams p) {
     // ---- epilogue (S side): row sums per head, LSE, inverse sums
 #pragma unroll
     for (int nbq = 0; nbq < 2; nbq++) {
-      float v = l_lane[nbq];
+      float v = l_lane[nbq], vb = lb_lane[nbq];
       v += __shfl_xor(v, 16, 64);
       v += __shfl_xor(v, 32, 64);
+      vb += __shfl_xor(vb, 16, 64);
+      vb += __shfl_xor(vb, 32, 64);
       l_lane[nbq] = v;
+      lb_lane[nbq] = vb;
     }
     if (lg == 0) {
       s_l[wr * 32 + li] = l_lane[0];
       s_l[wr * 32 + 16 + li] = l_lane[1];
+      s_lb[wr * 32 + li] = lb_lane[0];
+      s_lb[wr * 32 + 16 + li] = lb_lane[1];
     }
     lds_barrier();                                         // E1
     if (rh == 0 && lg == 0) {
 #pragma unroll
       for (int nbq = 0; nbq < 2; nbq++) {
         float lt = s_l[wr * 32 + 16 * nbq + li] + s_l[(wr ^ 2) * 32 + 16 * nbq + li];
+        float lbt = s_lb[wr * 32 + 16 * nbq + li] + s_lb[(wr ^ 2) * 32 + 16 * nbq + li];
         const int hl = 32 * hg + 16 * nbq + li;          // head within the block
         const int head = hb + hl;
         float mr = m_ref[nbq], om = p.out_mult;
@@ -776,12 +806,14 @@ smla_attn_kernel(KParams p) {
           if (M != -INFINITY) {
             const float a = exp2f(mr - M);                 // 0 for an empty row
             lt = fmaf(lt, a, exp2f(sg - M));
+            lbt = fmaf(lbt, a, exp2f(sg - M));
             om *= a;
             mr = M;
           }
         }
-        s_inv[hl] = (lt > 0.0f) ? om / lt : 0.0f;
-        const float lse_v = (lt > 0.0f) ? (mr + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+        const bool nonempty = !(lt <= 0.0f);              // a NaN sum stays NaN
+        s_inv[hl] = nonempty ? om / lbt : 0.0f;
+        const float lse_v = nonempty ? (mr + log2f(lt)) * 0.69314718055994531f : -INFINITY;
         if (head < H) {
           if (p.splits == 1) {
             if (p.lse) p.lse[(int64_t)t * p.lse_st + head] = lse_v;
@@ -897,7 +929,7 @@ smla_attn_kernel(KParams p) {
     }
     for (int attempt = 0; attempt < 2; attempt++) {
       o_pass(true, !F8 && attempt == 0);
-      if (!s_flag) break;                                  // uniform (after the pass's last barrier)
+      if (!s_flag || attempt == 1) break;                  // uniform (after the pass's last barrier)
       o_pass(false, false);
       lds_barrier();                                       // matches the S-waves' final maximum exchange
     }
@@ -976,7 +1008,13 @@ smla_combine_kernel(const uint16_t* __restrict__ part_o, int64_t po_rank, int64_
   // a sink is one more partial with a zero output and LSE sinks[head]
   const float sg = sinks ? sinks[head] : -INFINITY;
   float m = sg;
-  for (int s = 0; s < splits; s++) m = fmaxf(m, pl[s * pl_rank]);
+  bool nan = false;                                    // a NaN partial makes the result NaN
+  for (int s = 0; s < splits; s++) {
+    const float ls = pl[s * pl_rank];
+    m = fmaxf(m, ls);
+    nan = nan || ls != ls;
+  }
+  if (nan) m = __builtin_nanf("");
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float tot = 0.0f;
   if (m != -INFINITY) {
@@ -1049,6 +1087,7 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
   kp.q_rope = a.d_rope ? a.q_rope : a.q_nope; kp.qr_st = a.qr_st; kp.qr_sh = a.qr_sh;
   kp.kv = a.kv; kp.kv_row_stride = a.kv_row_stride; kp.num_slots = a.num_slots;
   kp.group_scales = a.group_scales;
+  kp.gs_stride = a.gs_stride;
   kp.indices = a.indices; kp.idx_stride = a.idx_stride; kp.topk = a.topk;
   kp.topk_length = a.topk_length;
   kp.req_id = a.req_id;

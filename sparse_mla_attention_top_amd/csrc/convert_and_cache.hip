@@ -185,7 +185,7 @@ cache_write_kernel(const uint16_t* __restrict__ kv_c, int64_t kv_c_stride,
                    const uint16_t* __restrict__ k_pe, int64_t k_pe_stride,
                    const int64_t* __restrict__ slot_mapping, int32_t num_tokens, int32_t d_rope,
                    float k_scale, uint8_t* __restrict__ cache, int64_t num_slots,
-                   int64_t row_stride, float* __restrict__ group_scales) {
+                   int64_t row_stride, float* __restrict__ group_scales, int64_t gs_stride) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= num_tokens) return;
@@ -222,7 +222,7 @@ cache_write_kernel(const uint16_t* __restrict__ kv_c, int64_t kv_c_stride,
       for (int o = 1; o < 16; o <<= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
       sc = (m == 0.0f) ? 1.0f : m / 448.0f;
       int g = c8 / 16;
-      if (FMT == 2 && active && (c8 % 16) == 0 && g < G) group_scales[slot * G + g] = sc;
+      if (FMT == 2 && active && (c8 % 16) == 0 && g < G) group_scales[slot * gs_stride + g] = sc;
       if (FMT == 3 && active && (c8 % 16) == 0) *(float*)(cache + slot * row_stride + 512 + 4 * g) = sc;
     }
     if (active) {
@@ -342,22 +342,22 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t stream) {
     case 0:
       cache_write_kernel<0><<<grid, 256, 0, stream>>>(a.kv_c, a.kv_c_stride, a.k_pe, a.k_pe_stride,
                                                       a.slot_mapping, a.num_tokens, a.d_rope, a.k_scale,
-                                                      a.cache, a.num_slots, a.row_stride, a.group_scales);
+                                                      a.cache, a.num_slots, a.row_stride, a.group_scales, a.gs_stride);
       break;
     case 1:
       cache_write_kernel<1><<<grid, 256, 0, stream>>>(a.kv_c, a.kv_c_stride, a.k_pe, a.k_pe_stride,
                                                       a.slot_mapping, a.num_tokens, a.d_rope, a.k_scale,
-                                                      a.cache, a.num_slots, a.row_stride, a.group_scales);
+                                                      a.cache, a.num_slots, a.row_stride, a.group_scales, a.gs_stride);
       break;
     case 2:
       cache_write_kernel<2><<<grid, 256, 0, stream>>>(a.kv_c, a.kv_c_stride, a.k_pe, a.k_pe_stride,
                                                       a.slot_mapping, a.num_tokens, a.d_rope, a.k_scale,
-                                                      a.cache, a.num_slots, a.row_stride, a.group_scales);
+                                                      a.cache, a.num_slots, a.row_stride, a.group_scales, a.gs_stride);
       break;
     case 3:
       cache_write_kernel<3><<<grid, 256, 0, stream>>>(a.kv_c, a.kv_c_stride, a.k_pe, a.k_pe_stride,
                                                       a.slot_mapping, a.num_tokens, a.d_rope, a.k_scale,
-                                                      a.cache, a.num_slots, a.row_stride, a.group_scales);
+                                                      a.cache, a.num_slots, a.row_stride, a.group_scales, a.gs_stride);
       break;
     default:
       return hipErrorInvalidValue;

@@ -89,6 +89,11 @@ int check_attn(const smla_attn_args* a, bool decode) {
     return fail(SMLA_ERR_INVALID_ARG, "k_scale must be finite and > 0");
   if (a->kv_format == SMLA_KV_FP8_E4M3_GROUP128 && ((uintptr_t)a->group_scales & 3))
     return fail(SMLA_ERR_INVALID_ARG, "group_scales must be 4-byte aligned");
+  if (a->kv_format == SMLA_KV_FP8_E4M3_GROUP128 && a->group_scales_stride != 0 &&
+      a->group_scales_stride < (D + 127) / 128)
+    return fail(SMLA_ERR_INVALID_ARG, "group_scales_stride=%lld below the %d groups of a %d-channel row",
+                (long long)a->group_scales_stride, (D + 127) / 128, D);
+  if (a->group_scales_stride < 0) return fail(SMLA_ERR_INVALID_ARG, "group_scales_stride < 0");
   if (!(std::isfinite(a->softcap) && a->softcap >= 0.0f))
     return fail(SMLA_ERR_INVALID_ARG, "softcap must be finite and >= 0 (0 = off)");
   if ((uintptr_t)a->sinks & 3) return fail(SMLA_ERR_INVALID_ARG, "sinks must be 4-byte aligned");
@@ -115,6 +120,7 @@ smla::AttnArgs to_internal(const smla_attn_args* a) {
   r.kv_format = a->kv_format;
   r.k_scale = a->k_scale;
   r.group_scales = a->group_scales;
+  r.gs_stride = a->group_scales_stride ? a->group_scales_stride : (512 + a->d_rope + 127) / 128;
   r.indices = a->indices;
   r.idx_stride = a->indices_stride;
   r.topk = a->topk;
@@ -319,7 +325,7 @@ int smla_prefill_fwd(const smla_attn_args* args, void* stream) {
 int smla_cache_write(const void* kv_c, int64_t kv_c_stride, const void* k_pe, int64_t k_pe_stride,
                      const int64_t* slot_mapping, int32_t num_tokens, int32_t d_rope, int32_t kv_format,
                      float k_scale, void* kv_cache, int64_t num_slots, int64_t kv_row_stride_bytes,
-                     float* group_scales, void* stream) {
+                     float* group_scales, int64_t group_scales_stride, void* stream) {
   if (num_tokens < 0) return fail(SMLA_ERR_INVALID_ARG, "num_tokens < 0");
   if (d_rope != 0 && d_rope != 64) return fail(SMLA_ERR_UNSUPPORTED, "d_rope=%d (only 0 or 64)", d_rope);
   if (kv_format < SMLA_KV_BF16 || kv_format > SMLA_KV_FP8_DS_MLA)
@@ -341,9 +347,14 @@ int smla_cache_write(const void* kv_c, int64_t kv_c_stride, const void* k_pe, in
     return fail(SMLA_ERR_INVALID_ARG, "k_scale must be finite and > 0");
   if (kv_format == SMLA_KV_FP8_E4M3_GROUP128 && !group_scales)
     return fail(SMLA_ERR_INVALID_ARG, "group_scales is NULL for the group-scaled FP8 format");
+  const int G = (D + 127) / 128;
+  if (group_scales_stride < 0 || (group_scales_stride != 0 && group_scales_stride < G))
+    return fail(SMLA_ERR_INVALID_ARG, "group_scales_stride=%lld: 0 or >= %d", (long long)group_scales_stride, G);
+  if (kv_format == SMLA_KV_FP8_E4M3_GROUP128 && ((uintptr_t)group_scales & 3))
+    return fail(SMLA_ERR_INVALID_ARG, "group_scales must be 4-byte aligned");
   smla::CacheWriteArgs a{(const uint16_t*)kv_c, kv_c_stride, (const uint16_t*)k_pe, k_pe_stride, slot_mapping,
                          num_tokens, d_rope, kv_format, k_scale, (uint8_t*)kv_cache, num_slots,
-                         kv_row_stride_bytes, group_scales};
+                         kv_row_stride_bytes, group_scales, group_scales_stride ? group_scales_stride : G};
   return hip_status(smla::launch_cache_write(a, (hipStream_t)stream), "cache_write launch");
 }
 

@@ -81,6 +81,7 @@ struct CacheWriteArgs {
   uint8_t* cache;
   int64_t num_slots, row_stride;
   float* group_scales;
+  int64_t gs_stride;             // floats between consecutive slots' scale rows
 };
 
 // Attention launch description (validated by the ABI layer).
@@ -95,6 +96,7 @@ struct AttnArgs {
   int32_t kv_format;
   float k_scale;
   const float* group_scales;
+  int64_t gs_stride;             // floats between consecutive slots' scale rows
   const int32_t* indices;
   int64_t idx_stride;
   int32_t topk;

@@ -85,6 +85,7 @@ class AttnArgs(ctypes.Structure):
         ("block_stride_rows", ctypes.c_int32),
         ("softcap", ctypes.c_float),
         ("sinks", ctypes.c_void_p),
+        ("group_scales_stride", ctypes.c_int64),
     ]
 
 
@@ -121,7 +122,7 @@ def load() -> ctypes.CDLL:
     lib.smla_decode_fwd.restype = ctypes.c_int
     lib.smla_prefill_fwd.argtypes = [ctypes.POINTER(AttnArgs), vp]
     lib.smla_prefill_fwd.restype = ctypes.c_int
-    lib.smla_cache_write.argtypes = [vp, i64, vp, i64, vp, i32, i32, i32, f32, vp, i64, i64, vp, vp]
+    lib.smla_cache_write.argtypes = [vp, i64, vp, i64, vp, i32, i32, i32, f32, vp, i64, i64, vp, i64, vp]
     lib.smla_cache_write.restype = ctypes.c_int
     lib.smla_set_timing_events.argtypes = [vp, vp]
     lib.smla_set_timing_events.restype = ctypes.c_int
@@ -291,6 +292,17 @@ def _kv_geometry(kv_cache: torch.Tensor):
     return kv_cache.shape[0], kv_cache.stride(0) * kv_cache.element_size(), kv_cache.shape[1]
 
 
+def _group_scales_stride(group_scales: Optional[torch.Tensor], S: int, d: int) -> int:
+    """Row stride (floats) of a [num_slots, >= ceil(d/128)] fp32 group-scale
+    array whose rows are those of the cache's slots; d = 512 + d_rope, the
+    channels the call reads."""
+    G = (d + 127) // 128
+    _need(group_scales is not None and group_scales.dtype == torch.float32 and group_scales.dim() == 2
+          and group_scales.shape[0] >= S and group_scales.shape[1] >= G and group_scales.stride(1) == 1,
+          f"group_scales must be fp32 [num_slots, >= {G}] with unit column stride")
+    return group_scales.stride(0)
+
+
 def _check_kv(kv_cache: torch.Tensor, kv_format: int, width: int, S: int,
               group_scales: Optional[torch.Tensor]) -> None:
     """Storage type of the cache and the group-scale array for kv_format."""
@@ -299,9 +311,7 @@ def _check_kv(kv_cache: torch.Tensor, kv_format: int, width: int, S: int,
     else:
         _need(kv_cache.dtype == torch.uint8, "an FP8-format cache must be a uint8 tensor of E4M3FN codes")
     if kv_format == KV_FP8_GROUP128:
-        G = (width + 127) // 128
-        _need(group_scales is not None and group_scales.dtype == torch.float32 and group_scales.is_contiguous()
-              and group_scales.numel() >= S * G, f"group_scales must be contiguous fp32 [num_slots, {G}]")
+        _need(group_scales is not None, "group_scales is required for the group-scaled FP8 format")
     if kv_format == KV_FP8_DS_MLA:
         _need(width >= DS_MLA_ROW_BYTES and group_scales is None,
               "a packed FP8 cache is uint8 [..., >= 656] with its scales in the row (no group_scales)")
@@ -339,6 +349,8 @@ def _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk
     a.kv_format = kv_format
     a.k_scale = float(k_scale)
     a.group_scales = _ptr(group_scales)
+    if kv_format == KV_FP8_GROUP128:
+        a.group_scales_stride = _group_scales_stride(group_scales, S, 512 + d_rope)
     a.indices = _ptr(indices)
     a.indices_stride = indices.stride(0)
     a.topk = indices.shape[1]
@@ -432,9 +444,10 @@ def cache_write(kv_c: torch.Tensor, k_pe: Optional[torch.Tensor], slot_mapping: 
         _need(k_pe.dtype == torch.bfloat16 and k_pe.stride(1) == 1, "k_pe must be bf16 [T, d_rope]")
     S, row_stride, width = _kv_geometry(kv_cache)
     _check_kv(kv_cache, kv_format, width, S, group_scales)
+    gs_stride = _group_scales_stride(group_scales, S, 512 + d_rope) if kv_format == KV_FP8_GROUP128 else 0
     rc = load().smla_cache_write(_ptr(kv_c), kv_c.stride(0), _ptr(k_pe), k_pe.stride(0) if k_pe is not None else 0,
                                  _ptr(slot_mapping), kv_c.shape[0], d_rope, kv_format, float(k_scale),
-                                 _ptr(kv_cache), S, row_stride, _ptr(group_scales), _stream(stream))
+                                 _ptr(kv_cache), S, row_stride, _ptr(group_scales), gs_stride, _stream(stream))
     _check("smla_cache_write", rc)
 
 

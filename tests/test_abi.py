@@ -71,16 +71,16 @@ def test_zero_tokens_is_a_no_op():
     assert lib.smla_prefill_fwd(ctypes.byref(a), None) == 0
     assert lib.smla_decode_fwd(ctypes.byref(a), None, 0, None) == 0
     assert lib.smla_convert_indices(None, None, 1, 1, 1, None, 0, 0, 0, 64, 0, None, 0, None, None) == 0
-    assert lib.smla_cache_write(None, 512, None, 0, None, 0, 64, 0, 1.0, None, 1, 1152, None, None) == 0
+    assert lib.smla_cache_write(None, 512, None, 0, None, 0, 64, 0, 1.0, None, 1, 1152, None, 0, None) == 0
 
 
 def test_convert_and_cache_write_reject_bad_args():
     lib = smla.load()
     assert lib.smla_convert_indices(16, 16, 1, 4, 4, 16, 8, 2, 8, 0, 0, 16, 8, None, None) == -1   # block_size 0
     assert lib.smla_convert_indices(16, 16, 1, 4, 2, 16, 8, 2, 8, 64, 0, 16, 8, None, None) == -1  # bt stride
-    assert lib.smla_cache_write(16, 512, 16, 64, 16, 2, 64, 1, 0.0, 16, 4, 576, None, None) == -1  # k_scale 0
-    assert lib.smla_cache_write(16, 512, 16, 64, 16, 2, 64, 2, 1.0, 16, 4, 576, None, None) == -1  # no scales
-    assert lib.smla_cache_write(16, 512, 16, 64, 16, 2, 48, 0, 1.0, 16, 4, 1152, None, None) == -2  # d_rope
+    assert lib.smla_cache_write(16, 512, 16, 64, 16, 2, 64, 1, 0.0, 16, 4, 576, None, 0, None) == -1  # k_scale 0
+    assert lib.smla_cache_write(16, 512, 16, 64, 16, 2, 64, 2, 1.0, 16, 4, 576, None, 0, None) == -1  # no scales
+    assert lib.smla_cache_write(16, 512, 16, 64, 16, 2, 48, 0, 1.0, 16, 4, 1152, None, 0, None) == -2  # d_rope
 
 
 def test_split_plan_is_shape_only():
@@ -133,8 +133,8 @@ def test_packed_fp8_format_rejects_bad_arguments():
     a = _args(kv_row_stride_bytes=656, group_scales=16, **base)
     assert lib.smla_prefill_fwd(ctypes.byref(a), None) == -1          # scales live in the row
     assert b"group_scales" in lib.smla_last_error()
-    assert lib.smla_cache_write(16, 512, 16, 64, 16, 2, 64, 3, 1.0, 16, 4, 576, None, None) == -1  # stride < 656
-    assert lib.smla_cache_write(16, 512, None, 0, 16, 2, 0, 3, 1.0, 16, 4, 656, None, None) == -2  # no rope
+    assert lib.smla_cache_write(16, 512, 16, 64, 16, 2, 64, 3, 1.0, 16, 4, 576, None, 0, None) == -1  # stride < 656
+    assert lib.smla_cache_write(16, 512, None, 0, 16, 2, 0, 3, 1.0, 16, 4, 656, None, 0, None) == -2  # no rope
 
 
 def test_planned_counts_and_upconvert_reject_bad_arguments():
@@ -148,3 +148,4 @@ def test_planned_counts_and_upconvert_reject_bad_arguments():
     assert lib.smla_gather_upconvert(16, 10, 656, 3, 16, 1, 4, 4, 64, 0, 16, 16, 8, 16, 8, 570, None) == -1
     assert lib.smla_gather_upconvert(16, 10, 656, 3, 16, 1, 4, 2, 64, 0, 16, 16, 8, 16, 8, 576, None) == -1
     assert lib.smla_last_error()
+

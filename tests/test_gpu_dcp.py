@@ -7,6 +7,7 @@ import pytest
 import torch
 
 from oracle import sparse_mla as O
+import parity_util as PU
 from parity_util import LSE_TOL, OUT_TOL, bits, compare, oracle_for, say
 from sparse_mla_attention_top_amd import smla
 
@@ -48,7 +49,7 @@ def test_merge_partials_matches_oracle():
     pl[:, 5, 3] = -np.inf
     po[:, 5, 3] = 0
     say("merge partials")
-    out, lse = smla.merge_partials(po.to(DEV), pl.to(DEV))
+    out, lse = PU.merge_partials(po.to(DEV), pl.to(DEV))
     torch.cuda.synchronize()
     ro, rl = O.merge_partials(po.float().numpy().astype(np.float64), pl.numpy().astype(np.float64))
     err = np.abs(out.float().cpu().numpy() - ro)
@@ -100,20 +101,20 @@ def test_dcp_sharded_decode_matches_whole(W, I):
     for r in range(W):
         loc, _ = smla.dcp_filter_convert(req.to(DEV), torch.from_numpy(tables[r]).to(DEV),
                                          torch.from_numpy(pos).to(DEV), W, r, I, block_size=B)
-        o, l = smla.decode_fwd(qd[..., :512], qd[..., 512:], caches[r].to(DEV), loc, scale)
+        o, l = PU.decode_fwd(qd[..., :512], qd[..., 512:], caches[r].to(DEV), loc, scale)
         parts_o.append(o)
         parts_l.append(l)
     torch.cuda.synchronize()
     for r in range(1, W):
         assert (parts_o[r][0] == 0).all() and torch.isneginf(parts_l[r][0]).all()
-    mo, ml = smla.merge_partials(torch.stack(parts_o), torch.stack(parts_l))
+    mo, ml = PU.merge_partials(torch.stack(parts_o), torch.stack(parts_l))
     # the whole context on one rank: position p at slot p
-    wo, wl = smla.decode_fwd(qd[..., :512], qd[..., 512:], rows.to(DEV), torch.from_numpy(pos).to(DEV), scale)
+    wo, wl = PU.decode_fwd(qd[..., :512], qd[..., 512:], rows.to(DEV), torch.from_numpy(pos).to(DEV), scale)
     torch.cuda.synchronize()
     ref = oracle_for(q, bits(rows), pos, scale)
     compare(wo, wl, ref, "dcp whole")
     # the merged result: two bf16 roundings (rank output, then merge) on top of the kernel's
-    compare(mo, ml, ref, f"dcp merged W={W}", k=2)
+    compare(mo, ml, ref, f"dcp merged W={W}")
     assert (mo.float() - wo.float()).abs().max().item() <= 2 * OUT_TOL
     assert (ml - wl).abs().max().item() <= 2 * LSE_TOL
 
@@ -150,16 +151,16 @@ def test_dcp_packed_fp8_ranks_with_sink_merge_to_the_whole():
         cache[bt[0, local[own] // B] * B + local[own] % B] = packed[own]
         loc, _ = smla.dcp_filter_convert(req, torch.from_numpy(bt).to(DEV), torch.from_numpy(pos).to(DEV), W, r, I,
                                          block_size=B, compact_valid_to_front=True)
-        o, l = smla.decode_fwd(qd[..., :512], qd[..., 512:], torch.from_numpy(cache).to(DEV), loc, scale,
-                               kv_format=smla.KV_FP8_DS_MLA)
+        o, l = PU.decode_fwd(qd[..., :512], qd[..., 512:], torch.from_numpy(cache).to(DEV), loc, scale,
+                             kv_format=smla.KV_FP8_DS_MLA)
         parts_o.append(o)
         parts_l.append(l)
     parts_o.append(torch.zeros_like(parts_o[0]))                 # the sink as a partial (0, sink)
     parts_l.append(sinks.to(DEV)[None, :].expand(T, h).contiguous())
-    mo, ml = smla.merge_partials(torch.stack(parts_o), torch.stack(parts_l))
-    wo, wl = smla.decode_fwd(qd[..., :512], qd[..., 512:], torch.from_numpy(packed).to(DEV),
-                             torch.from_numpy(pos).to(DEV), scale, kv_format=smla.KV_FP8_DS_MLA,
-                             sinks=sinks.to(DEV))
+    mo, ml = PU.merge_partials(torch.stack(parts_o), torch.stack(parts_l))
+    wo, wl = PU.decode_fwd(qd[..., :512], qd[..., 512:], torch.from_numpy(packed).to(DEV),
+                           torch.from_numpy(pos).to(DEV), scale, kv_format=smla.KV_FP8_DS_MLA,
+                           sinks=sinks.to(DEV))
     torch.cuda.synchronize()
     ref = oracle_for(q, packed, pos, scale, kv_format=O.KV_FP8_DS_MLA, sinks=sinks.numpy().astype(np.float64))
     compare(wo, wl, ref, "packed whole with sink", 2)

@@ -10,7 +10,7 @@ import pytest
 import torch
 
 from oracle import sparse_mla as O
-from parity_util import bits, compare, oracle_for, say
+from parity_util import bits, compare, nan_fill, oracle_for, say
 from sparse_mla_attention_top_amd import inputs as I
 from sparse_mla_attention_top_amd import smla
 
@@ -20,7 +20,12 @@ DEV = "cuda"
 
 def _check_graph(run, outs, replays=3):
     """run(): enqueue the calls on the current stream, writing into `outs`.
-    Eager reference, capture, then replays interleaved with eager runs."""
+    Eager reference, capture, then replays interleaved with eager runs. The
+    outputs are filled with NaN (all-ones bytes) before the eager reference
+    and before every replay, outside the capture, so an element a call does
+    not write shows up."""
+    for o in outs:
+        o.view(torch.uint8).fill_(0xFF)
     run()
     torch.cuda.synchronize()
     ref = [o.clone() for o in outs]
@@ -35,7 +40,7 @@ def _check_graph(run, outs, replays=3):
     torch.cuda.synchronize()
     for k in range(replays):
         for o in outs:
-            o.zero_()
+            o.view(torch.uint8).fill_(0xFF)
         g.replay()
         torch.cuda.synchronize()
         for o, r in zip(outs, ref):
@@ -55,6 +60,7 @@ def test_graph_decode_fused_conversion_and_merge():
     out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((T, H), dtype=torch.float32, device=DEV)
     ws = torch.empty(smla.decode_workspace_size(T, H, spec.topk, 4), dtype=torch.uint8, device=DEV)
+    nan_fill(ws)
     sinks = torch.linspace(-1.0, 2.0, H, device=DEV)
     say("graph decode bf16")
 
@@ -84,6 +90,7 @@ def test_graph_packed_fp8_decode_and_prefill():
     o2 = torch.empty_like(o1)
     l2 = torch.empty_like(l1)
     ws = torch.empty(smla.decode_workspace_size(5, 128, 700, 3), dtype=torch.uint8, device=DEV)
+    nan_fill(ws)
     say("graph packed fp8")
 
     def run():
@@ -115,6 +122,7 @@ def test_graph_context_parallel_step():
     out = torch.empty((T, h, 512), dtype=torch.bfloat16, device=DEV)
     lse = torch.empty((T, h), dtype=torch.float32, device=DEV)
     ws = torch.empty(max(smla.decode_workspace_size(T, h, K), 16), dtype=torch.uint8, device=DEV)
+    nan_fill(ws)
     posd = torch.from_numpy(pos).to(DEV)
     say("graph context-parallel step")
 

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 from oracle import sparse_mla as O
+import parity_util as PU
 from parity_util import bits, cache_for, compare, oracle_for, say
 from sparse_mla_attention_top_amd import inputs as I
 from sparse_mla_attention_top_amd import smla
@@ -25,9 +26,9 @@ def _run(c, kv_format, scale, entry, softcap=0.0, sinks=None, num_splits=0, use_
     sk = None if sinks is None else torch.as_tensor(sinks, dtype=torch.float32).to(DEV)
     kw = dict(kv_format=kv_format, k_scale=ks, group_scales=sc, topk_length=ln, softcap=softcap, sinks=sk)
     if entry == "decode":
-        out, lse = smla.decode_fwd(qn, qr, kv, c.indices.to(DEV), scale, num_splits=num_splits, **kw)
+        out, lse = PU.decode_fwd(qn, qr, kv, c.indices.to(DEV), scale, num_splits=num_splits, **kw)
     else:
-        out, lse = smla.prefill_fwd(qn, qr, kv, c.indices.to(DEV), scale, return_lse=True, **kw)
+        out, lse = PU.prefill_fwd(qn, qr, kv, c.indices.to(DEV), scale, return_lse=True, **kw)
     torch.cuda.synchronize()
     ref = oracle_for(c.q, host, c.indices.numpy(), scale, c.lengths.numpy() if use_lengths else None,
                      kv_format=kv_format, k_scale=ks, group_scales=None if sc is None else sc.cpu().numpy(),
@@ -119,10 +120,10 @@ def test_options_with_fused_conversion_and_scattered_invalid():
     qd = q.to(DEV)
     kvd = kv.to(DEV).view(R * MB, B, 576)
     args = dict(softcap=5.0, sinks=sinks.to(DEV))
-    o1, l1 = smla.decode_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(go).to(DEV), 0.09, **args)
-    o2, l2 = smla.decode_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(loc).to(DEV), 0.09,
-                             block_table=torch.from_numpy(bt).to(DEV), req_id=torch.from_numpy(req).to(DEV),
-                             block_size=B, **args)
+    o1, l1 = PU.decode_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(go).to(DEV), 0.09, **args)
+    o2, l2 = PU.decode_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(loc).to(DEV), 0.09,
+                           block_table=torch.from_numpy(bt).to(DEV), req_id=torch.from_numpy(req).to(DEV),
+                           block_size=B, **args)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
     ref = oracle_for(q, bits(kv), go, 0.09, softcap=5.0, sinks=sinks.numpy().astype(np.float64))

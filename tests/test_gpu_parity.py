@@ -1,8 +1,9 @@
 """GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
 
-Bit-exact for index conversion; for attention max-abs 1e-2 on the bf16 output
-(plus the bf16 rounding allowance of parity_util, which only matters for
-outputs far larger than the N(0,1) workloads give) and 1e-3 on the LSE."""
+Bit-exact for index conversion; for attention max-abs 1e-2 on the output
+before its own bf16 rounding (1e-2 + half a bf16 ulp at |ref|) and 1e-3 on the
+LSE, every output and LSE buffer filled with NaN before the call. The
+workloads are checked on every token at full size."""
 import json
 import os
 
@@ -11,6 +12,7 @@ import pytest
 import torch
 
 from oracle import sparse_mla as O
+import parity_util as PU
 from parity_util import LSE_TOL, OUT_TOL, bits, compare, oracle_for, q_f64, say
 from sparse_mla_attention_top_amd import inputs as I
 from sparse_mla_attention_top_amd import smla
@@ -97,11 +99,11 @@ def _fused_vs_separate(q, kv, req, bt, loc, scale, entry, block_size, stride=0, 
     conv = dict(block_table=btd, req_id=reqd, block_size=block_size, block_stride_rows=stride)
     # no row lengths on either side: invalid entries need not form a tail here
     if entry == "decode":
-        a = smla.decode_fwd(qn, qr, kvd, gidx, scale, num_splits=num_splits)
-        b = smla.decode_fwd(qn, qr, kvd, locd, scale, num_splits=num_splits, **conv)
+        a = PU.decode_fwd(qn, qr, kvd, gidx, scale, num_splits=num_splits)
+        b = PU.decode_fwd(qn, qr, kvd, locd, scale, num_splits=num_splits, **conv)
     else:
-        a = smla.prefill_fwd(qn, qr, kvd, gidx, scale, return_lse=True)
-        b = smla.prefill_fwd(qn, qr, kvd, locd, scale, return_lse=True, **conv)
+        a = PU.prefill_fwd(qn, qr, kvd, gidx, scale, return_lse=True)
+        b = PU.prefill_fwd(qn, qr, kvd, locd, scale, return_lse=True, **conv)
     torch.cuda.synchronize()
     return a, b, gidx, vcnt
 
@@ -159,7 +161,10 @@ def test_fused_conversion_invalid_corners(block_size, stride):
 # attention on the workload specs
 # ---------------------------------------------------------------------------
 
-def _run_workload(w, entry, tokens=None, num_splits=0, scale=None):
+def _run_workload(w, entry, tokens=None, num_splits=0, scale=None, chunk=512):
+    """The workload through convert + attention on the GPU, checked against the
+    oracle on ``tokens`` (default every token), ``chunk`` tokens at a time.
+    Returns the worst output and LSE errors."""
     spec = w.spec
     scale = spec.softmax_scale if scale is None else scale
     q = w.q.to(DEV)
@@ -167,16 +172,23 @@ def _run_workload(w, entry, tokens=None, num_splits=0, scale=None):
     gidx, vcnt = smla.convert_indices(w.req_id.to(DEV), w.block_table.to(DEV), w.topk_local.to(DEV))
     qn, qr = q[..., :512], (q[..., 512:] if spec.d_rope else None)
     if entry == "decode":
-        out, lse = smla.decode_fwd(qn, qr, kv, gidx, scale, topk_length=vcnt, num_splits=num_splits)
+        out, lse = PU.decode_fwd(qn, qr, kv, gidx, scale, topk_length=vcnt, num_splits=num_splits)
     else:
-        out, lse = smla.prefill_fwd(qn, qr, kv, gidx, scale, topk_length=vcnt, return_lse=True)
+        out, lse = PU.prefill_fwd(qn, qr, kv, gidx, scale, topk_length=vcnt, return_lse=True)
     torch.cuda.synchronize()
     go, vo = O.convert_indices(w.req_id.cpu().numpy(), w.block_table.cpu().numpy(), w.topk_local.cpu().numpy(), 64)
+    assert (gidx.cpu().numpy() == go).all() and (vcnt.cpu().numpy() == vo).all()
     sel = np.arange(spec.num_tokens) if tokens is None else np.asarray(tokens)
-    # the oracle gathers only the rows it needs
-    ref = oracle_for(w.q.cpu(), bits(w.kv_src), go, scale, vo, tokens=sel)
-    return compare(out[torch.as_tensor(sel, device=DEV)], lse[torch.as_tensor(sel, device=DEV)], ref,
-                   f"{spec.name}/{entry}")
+    q_cpu, cache_bits = w.q.cpu(), bits(w.kv_src)
+    err = lerr = 0.0
+    for c0 in range(0, len(sel), chunk):
+        part = sel[c0:c0 + chunk]
+        # the oracle gathers only the rows it needs
+        ref = oracle_for(q_cpu, cache_bits, go, scale, vo, tokens=part)
+        st = torch.as_tensor(part, device=DEV)
+        e, le = compare(out[st], lse[st], ref, f"{spec.name}/{entry} tokens {part[0]}..{part[-1]}")
+        err, lerr = max(err, e), max(lerr, le)
+    return err, lerr
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_late"])
@@ -206,23 +218,23 @@ def test_decode_splits(splits):
     _run_workload(w, "decode", num_splits=splits)
 
 
-def test_prefill_bf16_full_size_sampled():
+def test_prefill_bf16_full_size():
     """The bf16 prefill workload (4096 tokens, h=128, top-k 2048, causal
-    indices) at full size; the oracle checks a sample of tokens covering
-    short rows, the 2048 boundary and the longest rows."""
+    indices, valid = min(2048, pos + 1)) at full size, every token against the
+    oracle (FA3 kernel test file, test_fa3_mla_prefill_short_sequence: every
+    output of a causal prefill checked)."""
     spec = I.SPECS["prefill_bf16"]
-    say("attention prefill_bf16 full (sampled)")
+    say("attention prefill_bf16 full, every token")
     w = I.generate(spec, kv_device=DEV)
-    toks = [0, 1, 2, 31, 32, 33, 100, 1023, 2046, 2047, 2048, 2049, 3000, 4094, 4095]
-    err, lerr = _run_workload(w, "prefill", tokens=toks)
-    print(f"prefill_bf16 full sampled: out err {err:.2e} lse err {lerr:.2e}")
+    err, lerr = _run_workload(w, "prefill")
+    print(f"prefill_bf16 full: out err {err:.2e} lse err {lerr:.2e}")
 
 
 # ---------------------------------------------------------------------------
 # edge shapes with global indices
 # ---------------------------------------------------------------------------
 
-def _run_case(c, scale, entry="prefill", topk_length="lengths", num_splits=0, slots_view=None):
+def _run_case(c, scale, entry="prefill", topk_length="lengths", num_splits=0, slots_view=None, stress=False):
     q = c.q.to(DEV)
     d_rope = q.shape[2] - 512
     kv = c.kv_src.to(DEV)
@@ -230,12 +242,13 @@ def _run_case(c, scale, entry="prefill", topk_length="lengths", num_splits=0, sl
     ln = c.lengths.to(DEV) if topk_length == "lengths" else None
     qn, qr = q[..., :512], (q[..., 512:] if d_rope else None)
     if entry == "decode":
-        out, lse = smla.decode_fwd(qn, qr, kv, idx, scale, topk_length=ln, num_splits=num_splits)
+        out, lse = PU.decode_fwd(qn, qr, kv, idx, scale, topk_length=ln, num_splits=num_splits)
     else:
-        out, lse = smla.prefill_fwd(qn, qr, kv, idx, scale, topk_length=ln, return_lse=True)
+        out, lse = PU.prefill_fwd(qn, qr, kv, idx, scale, topk_length=ln, return_lse=True)
     torch.cuda.synchronize()
-    ref = oracle_for(c.q, bits(c.kv_src), c.indices.numpy(), scale, None if ln is None else c.lengths.numpy())
-    return out, lse, compare(out, lse, ref, "edge")
+    ref = oracle_for(c.q, bits(c.kv_src), c.indices.numpy(), scale, None if ln is None else c.lengths.numpy(),
+                     magnitude=stress)
+    return out, lse, compare(out, lse, ref, "edge", stress=stress)
 
 
 @pytest.mark.parametrize("h", [1, 16, 33, 64, 100, 128])
@@ -305,16 +318,16 @@ def test_large_logit_jump_takes_the_exact_path():
     for t in range(2):
         s = int(c.indices[t, 100])
         c.kv_src[s] = (c.q[t, 0].float() * 4.0).to(torch.bfloat16)
-    for entry in ("prefill", "decode"):
-        _run_case(c, 0.1, entry)
+    for entry in ("prefill", "decode"):       # a row of 4 q (values to ~16): the stress allowance
+        _run_case(c, 0.1, entry, stress=True)
 
 
 def test_deterministic_bitwise():
     say("determinism")
     c = I.random_case(T=8, h=128, d_rope=64, topk=512, num_slots=2048, seed=12)
     q, kv, idx = c.q.to(DEV), c.kv_src.to(DEV), c.indices.to(DEV)
-    a, la = smla.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, num_splits=4)
-    b, lb = smla.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, num_splits=4)
+    a, la = PU.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, num_splits=4)
+    b, lb = PU.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, num_splits=4)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
 
@@ -328,7 +341,7 @@ def test_splits_share_the_valid_prefix(splits):
     c = I.random_case(T=6, h=64, d_rope=64, topk=2048, num_slots=4096, seed=40 + splits,
                       lengths=[2048, 700, 100, 33, 1, 0])
     q, kv, idx = c.q.to(DEV), c.kv_src.to(DEV), c.indices.to(DEV)
-    o, l = smla.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, num_splits=splits)
+    o, l = PU.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, num_splits=splits)
     torch.cuda.synchronize()
     compare(o, l, oracle_for(c.q, bits(c.kv_src), c.indices.numpy(), 0.07), f"prefix splits={splits}")
 
@@ -346,8 +359,8 @@ def test_split_workspace_reused_across_shapes():
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
     for c, splits in ((ca, 4), (cb, 64), (ca, 4)):
         q, kv, idx, ln = c.q.to(DEV), c.kv_src.to(DEV), c.indices.to(DEV), c.lengths.to(DEV)
-        o, l = smla.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, topk_length=ln,
-                               num_splits=splits, workspace=ws)
+        o, l = PU.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, topk_length=ln,
+                             num_splits=splits, workspace=ws)
         torch.cuda.synchronize()
         compare(o, l, oracle_for(c.q, bits(c.kv_src), c.indices.numpy(), 0.07, c.lengths.numpy()),
                 f"ws splits={splits}")
@@ -361,8 +374,8 @@ def test_strided_query_and_output_views():
     q = c.q.to(DEV)
     big = torch.zeros((5, 20, 640), dtype=torch.bfloat16, device=DEV)
     out = big[:, :, :512]
-    o, l = smla.prefill_fwd(q[..., :512], q[..., 512:], c.kv_src.to(DEV), c.indices.to(DEV), 0.05,
-                            out=out, return_lse=True)
+    o, l = PU.prefill_fwd(q[..., :512], q[..., 512:], c.kv_src.to(DEV), c.indices.to(DEV), 0.05,
+                          out=out, return_lse=True)
     torch.cuda.synchronize()
     ref = oracle_for(c.q, bits(c.kv_src), c.indices.numpy(), 0.05)
     compare(out, l, ref, "strided")
@@ -373,8 +386,8 @@ def test_decode_matches_prefill():
     say("decode vs prefill")
     c = I.random_case(T=6, h=128, d_rope=64, topk=1024, num_slots=3000, seed=14, lengths=[1024, 900, 513, 64, 33, 1])
     q, kv, idx, ln = c.q.to(DEV), c.kv_src.to(DEV), c.indices.to(DEV), c.lengths.to(DEV)
-    a, la = smla.prefill_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, topk_length=ln, return_lse=True)
-    b, lb = smla.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, topk_length=ln, num_splits=4)
+    a, la = PU.prefill_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, topk_length=ln, return_lse=True)
+    b, lb = PU.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, topk_length=ln, num_splits=4)
     torch.cuda.synchronize()
     assert (a.float() - b.float()).abs().max().item() <= 2 * OUT_TOL
     assert (la - lb).abs().max().item() <= 2 * LSE_TOL

@@ -8,6 +8,7 @@ import pytest
 import torch
 
 from oracle import sparse_mla as O
+import parity_util as PU
 from parity_util import bits, compare, oracle_for, say
 from sparse_mla_attention_top_amd import inputs as I
 from sparse_mla_attention_top_amd import smla
@@ -66,8 +67,8 @@ def test_planned_counts_match_conversion_on_indexer_shaped_rows():
     S = R * mb * B
     kv = torch.randn((S, 576), generator=g).to(torch.bfloat16).to(DEV)
     q = torch.randn((T, h, 576), generator=g).to(torch.bfloat16).to(DEV)
-    o1, l1 = smla.decode_fwd(q[..., :512], q[..., 512:], kv, gidx, 0.07, topk_length=planned)
-    o2, l2 = smla.decode_fwd(q[..., :512], q[..., 512:], kv, gidx, 0.07, topk_length=vcnt)
+    o1, l1 = PU.decode_fwd(q[..., :512], q[..., 512:], kv, gidx, 0.07, topk_length=planned)
+    o2, l2 = PU.decode_fwd(q[..., :512], q[..., 512:], kv, gidx, 0.07, topk_length=vcnt)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
     go, vo = O.convert_indices(req, bt, loc, B)
@@ -128,8 +129,8 @@ def test_fp8_prefill_by_upconvert_full_size_sampled():
     qn, qr = q[..., :512], q[..., 512:]
     req, bt, loc = w.req_id.to(DEV), w.block_table.to(DEV), w.topk_local.to(DEV)
     say("fp8 prefill, in-LDS dequant")
-    o1, l1 = smla.prefill_fwd(qn, qr, kv, loc, spec.softmax_scale, kv_format=smla.KV_FP8_DS_MLA, return_lse=True,
-                              block_table=bt, req_id=req, block_size=I.BLOCK_SIZE)
+    o1, l1 = PU.prefill_fwd(qn, qr, kv, loc, spec.softmax_scale, kv_format=smla.KV_FP8_DS_MLA, return_lse=True,
+                            block_table=bt, req_id=req, block_size=I.BLOCK_SIZE)
     # the workspace: request r's context at starts[r] (block-aligned), read through a workspace block table
     seq = torch.full((spec.num_requests,), spec.ctx_len, dtype=torch.int32, device=DEV)
     starts = torch.zeros((spec.num_requests,), dtype=torch.int32, device=DEV)
@@ -137,8 +138,8 @@ def test_fp8_prefill_by_upconvert_full_size_sampled():
     ws_bt = torch.arange(spec.num_blocks, dtype=torch.int32, device=DEV).view(spec.num_requests, -1)
     say("fp8 prefill, gather-upconvert + bf16")
     smla.gather_upconvert(kv, bt, seq, starts, spec.ctx_len, ws, block_size=I.BLOCK_SIZE)
-    o2, l2 = smla.prefill_fwd(qn, qr, ws.view(spec.num_blocks, I.BLOCK_SIZE, 576), loc, spec.softmax_scale,
-                              return_lse=True, block_table=ws_bt, req_id=req, block_size=I.BLOCK_SIZE)
+    o2, l2 = PU.prefill_fwd(qn, qr, ws.view(spec.num_blocks, I.BLOCK_SIZE, 576), loc, spec.softmax_scale,
+                            return_lse=True, block_table=ws_bt, req_id=req, block_size=I.BLOCK_SIZE)
     torch.cuda.synchronize()
     ws_ref = np.zeros((spec.num_slots, 576), np.uint16)
     O.gather_upconvert(cache, w.block_table.numpy(), seq.cpu().numpy(), starts.cpu().numpy(), I.BLOCK_SIZE, ws_ref)

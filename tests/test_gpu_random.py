@@ -18,6 +18,7 @@ import pytest
 import torch
 
 from oracle import sparse_mla as O
+import parity_util as PU
 from parity_util import bits, cache_for, compare, oracle_for, say
 from sparse_mla_attention_top_amd import inputs as I
 from sparse_mla_attention_top_amd import smla
@@ -61,9 +62,9 @@ def test_random_configuration(seed):
     kw = dict(kv_format=cfg["fmt"], k_scale=ks, group_scales=gs, topk_length=ln, softcap=cfg["softcap"],
               sinks=None if sinks is None else torch.from_numpy(sinks).to(DEV))
     if cfg["entry"] == "decode":
-        out, lse = smla.decode_fwd(qn, qr, kv, c.indices.to(DEV), cfg["scale"], num_splits=cfg["splits"], **kw)
+        out, lse = PU.decode_fwd(qn, qr, kv, c.indices.to(DEV), cfg["scale"], num_splits=cfg["splits"], **kw)
     else:
-        out, lse = smla.prefill_fwd(qn, qr, kv, c.indices.to(DEV), cfg["scale"], return_lse=True, **kw)
+        out, lse = PU.prefill_fwd(qn, qr, kv, c.indices.to(DEV), cfg["scale"], return_lse=True, **kw)
     torch.cuda.synchronize()
     ref = oracle_for(c.q, host, c.indices.numpy(), cfg["scale"], c.lengths.numpy() if cfg["use_lengths"] else None,
                      kv_format=cfg["fmt"], k_scale=ks, group_scales=None if gs is None else gs.cpu().numpy(),
@@ -97,11 +98,11 @@ def test_random_block_tables_converted_in_kernel(seed):
     kw = dict(block_table=torch.from_numpy(bt).to(DEV), req_id=torch.from_numpy(req).to(DEV), block_size=B,
               block_stride_rows=stride)
     if entry == "decode":
-        out, lse = smla.decode_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(loc).to(DEV), 0.07,
-                                   num_splits=splits, **kw)
+        out, lse = PU.decode_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(loc).to(DEV), 0.07,
+                                 num_splits=splits, **kw)
     else:
-        out, lse = smla.prefill_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(loc).to(DEV), 0.07,
-                                    return_lse=True, **kw)
+        out, lse = PU.prefill_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(loc).to(DEV), 0.07,
+                                  return_lse=True, **kw)
     torch.cuda.synchronize()
     keep = np.nonzero(good)[0]
     if keep.size:
@@ -182,11 +183,11 @@ def test_random_rows_with_duplicate_slots(seed):
     kw = dict(kv_format=fmt, k_scale=ks, group_scales=gs)
     ref = oracle_for(q, host, idx, 0.06, kv_format=fmt, k_scale=ks, group_scales=None if gs is None else gs.cpu().numpy())
     for splits in (1, 3):
-        out, lse = smla.decode_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(idx).to(DEV), 0.06,
-                                   num_splits=splits, **kw)
+        out, lse = PU.decode_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(idx).to(DEV), 0.06,
+                                 num_splits=splits, **kw)
         torch.cuda.synchronize()
         compare(out, lse, ref, f"duplicates decode splits={splits}", k)
-    out, lse = smla.prefill_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(idx).to(DEV), 0.06,
-                                return_lse=True, **kw)
+    out, lse = PU.prefill_fwd(qd[..., :512], qd[..., 512:], kvd, torch.from_numpy(idx).to(DEV), 0.06,
+                              return_lse=True, **kw)
     torch.cuda.synchronize()
     compare(out, lse, ref, "duplicates prefill", k)
