@@ -2,12 +2,16 @@
 """Benchmark of the sparse MLA hot path on one MI355X.
 
 One step = one pass of the whole path over one batch of synthetic input:
-request-local -> global index conversion, then the sparse attention (decode:
-split top-k + LSE combine; prefill: one workgroup per token). Prints one JSON
-line with the throughput, the roofline position of the attention kernel and
-the fp64 CPU oracle timed on the host.
+request-local -> global index conversion (inside the attention kernel), then
+the sparse attention (decode: split top-k + LSE combine; prefill: one
+workgroup per token and head block). By default the three workloads of the
+metric (h=128, top-k 2048) run in one invocation: the bf16 decode gives the
+headline fields of the one JSON line (throughput, the attention kernel's
+roofline position, the fp64 CPU oracle timed on the host), and the bf16
+prefill and the long-context FP8 decode are reported beside it under
+"workloads". Exactly --steps steps are timed per workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode_bf16]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config targets|<workload>]
 """
 from __future__ import annotations
 
@@ -194,14 +198,21 @@ def build_caches(spec, w, R: int, dev):
     return caches, gscales, kscales
 
 
-def main() -> int:
+# the workloads the metric names (h=128, top-k 2048): the bf16 decode (the
+# headline line), the bf16 prefill and the long-context FP8 decode
+TARGETS = ["decode_bf16", "prefill_bf16", "longctx_fp8"]
+
+
+def parse_args(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=300)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="decode_bf16", choices=sorted(ENTRY))
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="targets", choices=["targets"] + sorted(ENTRY),
+                    help="'targets' (default): the bf16 decode as the headline line plus the bf16 prefill and "
+                         "the long-context FP8 decode in the same run; or one workload")
     ap.add_argument("--rotate", type=int, default=6, help="independent cache copies cycled through (cold L2/MALL)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="decode top-k splits (0 = the library's plan)")
     ap.add_argument("--dcp", type=int, default=1,
@@ -217,26 +228,77 @@ def main() -> int:
     ap.add_argument("--sinks", action="store_true", help="one sink logit per head (drawn N(0,1), seeded)")
     ap.add_argument("--separate-convert", action="store_true",
                     help="run smla_convert_indices as its own kernel in the step instead of in the attention kernel")
-    args = ap.parse_args()
+    return ap.parse_args(argv)
 
+
+def main() -> int:
+    args = parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the design notes describe how it would shard); run with --gpus 1", file=sys.stderr)
         return 2
+    if args.steps < 1:
+        print("--steps must be >= 1", file=sys.stderr)
+        return 2
 
+    import torch
+
+    if args.dcp > 1:
+        return run_dcp(args)
+    names = TARGETS if args.config == "targets" else [args.config]
+    results = {}
+    for name in names:
+        results[name] = measure(name, args)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    head = results[names[0]]
+    line = {
+        "metric": "sparse-MLA query tokens/s and TFLOP/s (h=128, top-k=2048) + % of roofline",
+        "value": head["tokens_per_s"],
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": head["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": head["config"],
+        "tflops": head["tflops"],
+        "attn_kernel_us": head["attn_kernel_us"],
+        "attn_kernel_us_p10_p50_p90": head["attn_kernel_us_p10_p50_p90"],
+        "step_us_events": head["step_us_events"],
+        "alg_bytes_per_step": head["alg_bytes_per_step"],
+        "alg_flops_per_step": head["alg_flops_per_step"],
+        "roofline": head["roofline"],
+        "step_roofline_frac": head["step_roofline_frac"],
+        "cpu_baseline": head["cpu_baseline"],
+    }
+    if len(names) > 1:
+        line["workloads"] = {n: {k: v for k, v in r.items() if k != "config"} | {"workload": r["config"]["workload"]}
+                             for n, r in results.items()}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def measure(name: str, args) -> dict:
+    """One workload: HIP graph replays of exactly args.steps steps (whole-job
+    throughput), then per-step and attention-kernel durations from HIP events
+    over eager steps queued behind a spin kernel, the roofline position and
+    the oracle on the host."""
     import numpy as np
     import torch
 
     from sparse_mla_attention_top_amd import inputs as I
     from sparse_mla_attention_top_amd import smla
 
-    if args.dcp > 1:
-        return run_dcp(args)
     dev = "cuda"
-    spec = I.SPECS[args.config]
-    entry = ENTRY[args.config]
+    spec = I.SPECS[name]
+    entry = ENTRY[name]
     w = I.generate(spec, kv_device=dev)
-    R = max(1, args.rotate)
+    R = max(1, min(args.rotate, args.steps))
     caches, gscales, kscales = build_caches(spec, w, R, dev)
     q = w.q.to(dev)
     qn, qr = q[..., :512], (q[..., 512:] if spec.d_rope else None)
@@ -256,9 +318,8 @@ def main() -> int:
 
     upconvert = entry == "prefill" and spec.kv_format == I.KV_FP8_DS_MLA and args.fp8_prefill == "upconvert"
     if upconvert and args.separate_convert:
-        print("--fp8-prefill upconvert converts through the workspace's block table in the attention kernel; "
-              "drop --separate-convert", file=sys.stderr)
-        return 2
+        raise SystemExit("--fp8-prefill upconvert converts through the workspace's block table in the attention "
+                         "kernel; drop --separate-convert")
     if upconvert:
         # the context of every request, block-aligned in a bf16 workspace read through its own block table
         ws_seq = torch.full((spec.num_requests,), spec.ctx_len, dtype=torch.int32, device=dev)
@@ -299,54 +360,70 @@ def main() -> int:
     torch.cuda.synchronize()
     ref_out, ref_lse = out.clone(), lse.clone()
 
-    # one graph = R consecutive steps (one per cache copy)
+    # graphs: R consecutive steps (one per cache copy), and the remainder, so
+    # that exactly args.steps steps are timed
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
-    g = torch.cuda.CUDAGraph()
+    replays, rem = divmod(args.steps, R)
+    g_full, g_rem = torch.cuda.CUDAGraph(), (torch.cuda.CUDAGraph() if rem else None)
     with torch.cuda.stream(stream):
         step(0)
         torch.cuda.current_stream().synchronize()
-        with torch.cuda.graph(g, stream=stream):
+        with torch.cuda.graph(g_full, stream=stream):
             for k in range(R):
                 step(k)
+        if g_rem is not None:
+            with torch.cuda.graph(g_rem, stream=stream):
+                for k in range(rem):
+                    step(k)
     torch.cuda.synchronize()
-    replays = max(1, (args.steps + R - 1) // R)
-    steps = replays * R
     # every replay must reproduce the eager result (replays interleaved with eager work)
-    for _ in range(2):
+    for g in [g_full] + ([g_rem] if g_rem is not None else []):
         g.replay()
         torch.cuda.synchronize()
         step(0)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)) and torch.equal(lse, ref_lse)
-    g.replay()
+    g_full.replay()
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
     for _ in range(replays):
-        g.replay()
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    dt = t1 - t0
+    dt = time.perf_counter() - t0
+    steps = replays * R + rem
     ms_per_step = dt / steps * 1e3
     tokens_per_s = T * steps / dt
 
-    # attention kernel duration: HIP events that the library hands to hipExtLaunchKernel, which
-    # sets them from the kernel's own start and end timestamps (queue backed up first)
+    # eager steps queued behind a spin kernel: per step, HIP events recorded
+    # before and after it on its stream (the step's duration, with the gaps
+    # between its kernels), and the attention kernel's own start and end
+    # timestamps (hipExtLaunchKernel sets the events the library is given)
     n_ev = min(steps, 120)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
-    for a, b in evs:          # torch creates the HIP events on first record
+    mk = lambda: torch.cuda.Event(enable_timing=True)    # noqa: E731
+    kev = [(mk(), mk()) for _ in range(n_ev)]
+    sev = [(mk(), mk()) for _ in range(n_ev)]
+    for a, b in kev + sev:    # torch creates the HIP events on first record
         a.record()
         b.record()
     torch.cuda.synchronize()
     torch.cuda._sleep(50_000_000)
     for k in range(n_ev):
-        smla.set_timing_events(*evs[k])
+        smla.set_timing_events(*kev[k])
+        sev[k][0].record()
         step(k)
+        sev[k][1].record()
     smla.set_timing_events(None, None)
     torch.cuda.synchronize()
-    kern_all = [hip_elapsed_ms(a, b) for a, b in evs]
+    kern_all = [hip_elapsed_ms(a, b) for a, b in kev]
+    step_all = [a.elapsed_time(b) for a, b in sev]
     kern_ms = sum(kern_all) / n_ev
+    step_ev_ms = sum(step_all) / n_ev
+    assert kern_ms <= step_ev_ms, (f"{name}: attention kernel {kern_ms * 1e3:.2f} us above the step "
+                                   f"{step_ev_ms * 1e3:.2f} us that contains it")
 
     gidx_np, vcnt_np = gidx.cpu().numpy(), vcnt.cpu().numpy()
     row_bytes = I.kv_row_bytes(spec)
@@ -363,7 +440,12 @@ def main() -> int:
         achieved = flops / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof["traffic"] = traffic_from_profiles(args.config)
+    traffic = traffic_from_profiles(name)
+    roof["traffic"] = traffic
+    roof["traffic_source"] = (f"profiles/attn_traffic_{name}.json: rocprofv3 FETCH_SIZE and WRITE_SIZE of this "
+                              f"kernel source ({source_hash()}), scaled by a plain copy's counters"
+                              if traffic is not None else
+                              "none: no counter summary taken on this kernel source")
     roofline_time = max(alg_bytes / (HBM_PEAK_GBS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
 
     cpu = None
@@ -371,38 +453,32 @@ def main() -> int:
         cpu = cpu_baseline(w, gidx_np, vcnt_np, args.cpu_seconds, kscales[0], args.softcap,
                            None if sinks is None else sinks.cpu().numpy().astype("float64"))
 
-    line = {
-        "metric": "sparse-MLA query tokens/s and TFLOP/s (h=128, top-k=2048) + % of roofline",
-        "value": round(tokens_per_s, 1),
-        "unit": "query tokens/s",
-        "n_gpus": 1,
+    config = {"workload": WORKLOAD_TEXT[name], "name": name, "num_tokens": T, "heads": H,
+              "topk": K, "entry": f"smla_{entry}_fwd", "splits": splits, "cache_copies_rotated": R,
+              "kv_storage": KV_STORAGE[spec.kv_format],
+              "index_conversion": "separate kernel" if args.separate_convert else "in the attention kernel",
+              "softcap": args.softcap, "sinks": bool(args.sinks),
+              "fp8_prefill": (args.fp8_prefill if entry == "prefill" and spec.kv_format == I.KV_FP8_DS_MLA
+                              else None),
+              "timing": "HIP graphs of exactly `steps` steps replayed; cold L2/MALL by cache rotation"}
+    res = {
+        "config": config,
+        "tokens_per_s": round(tokens_per_s, 1),
         "steps": steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.config], "name": args.config, "num_tokens": T, "heads": H,
-                   "topk": K, "entry": f"smla_{entry}_fwd", "splits": splits, "cache_copies_rotated": R,
-                   "kv_storage": KV_STORAGE[spec.kv_format],
-                   "index_conversion": "separate kernel" if args.separate_convert else "in the attention kernel",
-                   "softcap": args.softcap, "sinks": bool(args.sinks),
-                   "fp8_prefill": (args.fp8_prefill if entry == "prefill" and spec.kv_format == I.KV_FP8_DS_MLA
-                                   else None),
-                   "timing": "HIP graph of R steps replayed; cold L2/MALL by cache rotation"},
         "tflops": round(tflops, 2),
-        "pct_of_path_roofline": round(100 * roofline_time / (dt / steps), 2),
         "attn_kernel_us": round(kern_ms * 1e3, 3),
         "attn_kernel_us_p10_p50_p90": kernel_percentiles(kern_all),
+        "step_us_events": round(step_ev_ms * 1e3, 3),
         "alg_bytes_per_step": alg_bytes,
         "alg_flops_per_step": flops,
         "roofline": roof,
+        # the same roofline against the whole step (for decode: attention + split combine)
+        "step_roofline_frac": round(roofline_time / (dt / steps), 4),
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
-    return 0
+    del caches, gscales, w, q
+    return res
 
 
 def run_dcp(args) -> int:
@@ -483,25 +559,33 @@ def run_dcp(args) -> int:
 
     stream = torch.cuda.Stream()
     stream.wait_stream(torch.cuda.current_stream())
-    g = torch.cuda.CUDAGraph()
+    R = min(R, args.steps)
+    replays, rem = divmod(args.steps, R)
+    g, g_rem = torch.cuda.CUDAGraph(), (torch.cuda.CUDAGraph() if rem else None)
     with torch.cuda.stream(stream):
         step(0)
         torch.cuda.current_stream().synchronize()
         with torch.cuda.graph(g, stream=stream):
             for k in range(R):
                 step(k)
+        if g_rem is not None:
+            with torch.cuda.graph(g_rem, stream=stream):
+                for k in range(rem):
+                    step(k)
     torch.cuda.synchronize()
     ref_o, ref_l = out.clone(), lse.clone()
-    g.replay()
-    torch.cuda.synchronize()
-    step(0)
-    torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)) and torch.equal(lse, ref_l)
-    replays = max(1, (args.steps + R - 1) // R)
-    steps = replays * R
+    for gg in [g] + ([g_rem] if g_rem is not None else []):
+        gg.replay()
+        torch.cuda.synchronize()
+        step(0)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)) and torch.equal(lse, ref_l)
+    steps = args.steps
     t0 = time.perf_counter()
     for _ in range(replays):
         g.replay()
+    if g_rem is not None:
+        g_rem.replay()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
 
