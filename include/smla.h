@@ -255,6 +255,24 @@ int32_t smla_decode_num_splits(int32_t num_tokens, int32_t num_heads, int32_t to
 int smla_decode_fwd(const smla_attn_args* args, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/*
+ * Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): smla_decode_fwd with the split partials kept in a static device
+ * scratch of the library instead of a caller workspace. The scratch is one
+ * file-scope device array of 32 MiB per GPU, held until the process ends; its
+ * address is looked up once per device on the first call there (with that
+ * device current). No call allocates. Every call on a GPU shares that GPU's
+ * scratch: calls that overlap in time on one GPU (two streams, two threads)
+ * race and give wrong results; serialise them. The partials are fully written
+ * before they are read, so nothing in the scratch needs clearing. A plan
+ * whose partials exceed 32 MiB (num_splits x num_tokens x num_heads x 1028
+ * bytes; the automatic plan stays below 17 MB) returns
+ * SMLA_ERR_WORKSPACE_TOO_SMALL without launching. Arguments and results as
+ * for smla_decode_fwd; the stream must belong to the current device.
+ */
+int smla_decode_fwd_noalloc(const smla_attn_args* args, void* stream);
+
 /* Prefill forward: the same function without splitting (one workgroup per
  * token); args->num_splits is ignored. */
 int smla_prefill_fwd(const smla_attn_args* args, void* stream);

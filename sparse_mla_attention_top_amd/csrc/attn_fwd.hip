@@ -31,6 +31,8 @@
 #include <hip/hip_ext.h>
 #include <math.h>
 
+#include <mutex>
+
 namespace smla {
 
 struct KParams {
@@ -1165,6 +1167,33 @@ hipError_t launch_merge(const MergeArgs& m, hipStream_t stream) {
       m.part_o, m.po_rank, m.po_tok, m.po_head, m.part_lse, m.pl_rank, m.pl_tok, m.parts, m.num_tokens,
       m.num_heads, m.out, m.out_st, m.out_sh, m.lse, m.lse_st, m.sinks);
   return hipGetLastError();
+}
+
+// Split partials of the allocation-free decode entry point: a file-scope
+// device array, one copy per GPU for the life of the process. Host code never
+// uses the array's name as an address: the device address of each GPU's copy
+// comes from hipGetSymbolAddress, taken once per device with that device
+// current, and is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_buffer(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
 }
 
 }  // namespace smla

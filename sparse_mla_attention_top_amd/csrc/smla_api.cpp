@@ -314,6 +314,26 @@ int smla_decode_fwd(const smla_attn_args* args, void* workspace, size_t workspac
                     "decode launch");
 }
 
+int smla_decode_fwd_noalloc(const smla_attn_args* args, void* stream) {
+  int rc = check_attn(args, true);
+  if (rc != SMLA_OK) return rc;
+  if (args->num_tokens == 0) return ok();
+  const int32_t s = smla::plan_splits(args->num_tokens, args->num_heads, args->topk, args->num_splits);
+  const size_t need = smla::workspace_bytes(args->num_tokens, args->num_heads, args->topk, s);
+  if (need > smla::kScratchBytes)
+    return fail(SMLA_ERR_WORKSPACE_TOO_SMALL,
+                "%d splits x %d tokens x %d heads need %zu bytes of split partials, above the %zu-byte static "
+                "scratch of the allocation-free decode (use smla_decode_fwd with a workspace, or fewer splits)",
+                s, args->num_tokens, args->num_heads, need, smla::kScratchBytes);
+  void* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t e = smla::scratch_buffer(&scratch);
+    if (e != hipSuccess) return hip_status(e, "static scratch address");
+  }
+  return hip_status(smla::launch_attention(to_internal(args), s, scratch, false, (hipStream_t)stream),
+                    "decode launch");
+}
+
 int smla_prefill_fwd(const smla_attn_args* args, void* stream) {
   int rc = check_attn(args, false);
   if (rc != SMLA_OK) return rc;

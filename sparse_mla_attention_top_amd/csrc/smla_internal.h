@@ -120,6 +120,13 @@ struct AttnArgs {
 constexpr int kTileRows = 32;
 constexpr int kMaxTopk = 2048;
 
+// Size of the static device scratch of the allocation-free decode (the split
+// partials; the automatic plan needs at most 256 workgroups x 64 heads x
+// (1024 + 4) bytes = 16.8 MB).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+// Device address of the current GPU's copy of that scratch (looked up once per device).
+hipError_t scratch_buffer(void** out);
+
 // Split plan from shapes only.
 int32_t plan_splits(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t requested);
 size_t workspace_bytes(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t splits);

@@ -39,6 +39,7 @@ EXPORTED = (
     "smla_merge_partials",
     "smla_planned_valid_counts",
     "smla_gather_upconvert",
+    "smla_decode_fwd_noalloc",
 )
 
 
@@ -120,6 +121,8 @@ def load() -> ctypes.CDLL:
     lib.smla_decode_num_splits.restype = i32
     lib.smla_decode_fwd.argtypes = [ctypes.POINTER(AttnArgs), vp, sz, vp]
     lib.smla_decode_fwd.restype = ctypes.c_int
+    lib.smla_decode_fwd_noalloc.argtypes = [ctypes.POINTER(AttnArgs), vp]
+    lib.smla_decode_fwd_noalloc.restype = ctypes.c_int
     lib.smla_prefill_fwd.argtypes = [ctypes.POINTER(AttnArgs), vp]
     lib.smla_prefill_fwd.restype = ctypes.c_int
     lib.smla_cache_write.argtypes = [vp, i64, vp, i64, vp, i32, i32, i32, f32, vp, i64, i64, vp, i64, vp]
@@ -409,6 +412,21 @@ def decode_fwd(q_nope, q_rope, kv_cache, indices, softmax_scale, kv_format=KV_BF
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = load().smla_decode_fwd(ctypes.byref(a), _ptr(workspace), ws_bytes, _stream(stream))
     _check("smla_decode_fwd", rc)
+    return out, lse
+
+
+def decode_fwd_noalloc(q_nope, q_rope, kv_cache, indices, softmax_scale, out, lse=None, kv_format=KV_BF16,
+                       topk_length=None, k_scale=1.0, group_scales=None, num_splits=0, stream=None,
+                       block_table=None, req_id=None, block_size=64, block_stride_rows=0, softcap=0.0, sinks=None):
+    """decode_fwd without a workspace: the split partials live in the library's
+    static device scratch (smla_decode_fwd_noalloc), and the caller passes the
+    output (and LSE, or None) buffers, so nothing is allocated."""
+    _need(out is not None, "decode_fwd_noalloc writes into a caller-owned out buffer (bf16 [T, h, 512])")
+    a, out, lse = _attn_args(q_nope, q_rope, kv_cache, kv_format, indices, softmax_scale, topk_length,
+                             k_scale, group_scales, out, lse, num_splits, block_table, req_id, block_size,
+                             block_stride_rows, softcap, sinks)
+    rc = load().smla_decode_fwd_noalloc(ctypes.byref(a), _stream(stream))
+    _check("smla_decode_fwd_noalloc", rc)
     return out, lse
 
 

@@ -149,3 +149,16 @@ def test_planned_counts_and_upconvert_reject_bad_arguments():
     assert lib.smla_gather_upconvert(16, 10, 656, 3, 16, 1, 4, 2, 64, 0, 16, 16, 8, 16, 8, 576, None) == -1
     assert lib.smla_last_error()
 
+
+def test_noalloc_decode_rejects_partials_beyond_its_scratch():
+    """A split plan whose partials exceed the 32 MiB static scratch is refused
+    before anything is launched (host-side check, no GPU call)."""
+    lib = smla.load()
+    a = _args(q_nope=16, q_rope=16, kv_cache=16, indices=16, out=16, num_slots=10, kv_row_stride_bytes=1152,
+              indices_stride=2048, out_stride_tok=128 * 512, out_stride_head=512, num_tokens=256, num_heads=128,
+              topk=2048, num_splits=64, q_nope_stride_tok=128 * 576, q_nope_stride_head=576,
+              q_rope_stride_tok=128 * 576, q_rope_stride_head=576)
+    assert lib.smla_decode_fwd_noalloc(ctypes.byref(a), None) == -3
+    assert b"scratch" in lib.smla_last_error()
+    a.num_tokens = 0
+    assert lib.smla_decode_fwd_noalloc(ctypes.byref(a), None) == 0
