@@ -27,6 +27,7 @@
 // the block table when one is given) and the S-waves load Q.
 #include "smla_device.h"
 #include "smla_internal.h"
+#include "smla_lookup.h"
 
 #include <hip/hip_ext.h>
 #include <math.h>
@@ -48,13 +49,9 @@ struct KParams {
   int64_t idx_stride;
   int32_t topk;
   const int32_t* topk_length;
-  // fused index conversion (block_table != nullptr: indices are request-local)
+  // fused index conversion (bt.table != nullptr: indices are request-local)
   const int32_t* req_id;
-  const int32_t* block_table;
-  int32_t num_reqs, max_blocks;
-  int64_t bt_stride;
-  int32_t block_size, block_shift;   // block_shift = log2(block_size) if a power of two, else -1
-  int32_t block_stride_rows;
+  BlockTable bt;
   int32_t num_tokens, num_heads;
   float scale_log2;   // softmax scale * log2(e)
   float out_mult;
@@ -234,7 +231,7 @@ smla_attn_kernel(KParams p) {
   const int32_t* irow = p.indices + (int64_t)t * p.idx_stride;
   constexpr int kIdxPerThread = kMaxTopk / 512;
   int gi[kIdxPerThread];
-  const bool convert = p.block_table != nullptr;
+  const bool convert = p.bt.table != nullptr;
   const int rq = convert ? p.req_id[t] : 0;                // loaded with the indices
 #pragma unroll
   for (int k = 0; k < kIdxPerThread; k++) {
@@ -242,33 +239,14 @@ smla_attn_kernel(KParams p) {
     gi[k] = (j < p.topk) ? irow[j] : -1;
   }
   if (convert) {
-    // request-local index lc -> block_table[req][lc / B] * stride + lc % B
-    // (the rule of smla_convert_indices; anything it maps to -1 stays -1)
-    const bool req_ok = rq >= 0 && rq < p.num_reqs;
-    const int32_t* bt = p.block_table + (int64_t)(req_ok ? rq : 0) * p.bt_stride;
-    int blk[kIdxPerThread], off[kIdxPerThread], e[kIdxPerThread];
+    // request-local index -> global slot by the rule of smla_convert_indices
+    // (anything it maps to -1 stays -1); the table reads of the row are all
+    // issued before their results are used
+    int64_t g[kIdxPerThread];
 #pragma unroll
-    for (int k = 0; k < kIdxPerThread; k++) {
-      const int lc = gi[k];
-      blk[k] = p.max_blocks;
-      off[k] = 0;
-      if (lc >= 0) {
-        if (p.block_shift >= 0) {
-          blk[k] = lc >> p.block_shift;
-          off[k] = lc & (p.block_size - 1);
-        } else {
-          blk[k] = lc / p.block_size;
-          off[k] = lc - blk[k] * p.block_size;
-        }
-      }
-      e[k] = -1;
-      if (req_ok && blk[k] < p.max_blocks) e[k] = bt[blk[k]];
-    }
+    for (int k = 0; k < kIdxPerThread; k++) g[k] = local_slot(p.bt, rq, gi[k]);
 #pragma unroll
-    for (int k = 0; k < kIdxPerThread; k++) {
-      const int64_t g = (int64_t)e[k] * p.block_stride_rows + off[k];
-      gi[k] = (e[k] >= 0 && g < p.num_slots) ? (int)g : -1;
-    }
+    for (int k = 0; k < kIdxPerThread; k++) gi[k] = (g[k] >= 0 && g[k] < p.num_slots) ? (int)g[k] : -1;
   }
   int len = p.topk;
   if (p.topk_length) len = min(max(p.topk_length[t], 0), p.topk);
@@ -1043,30 +1021,6 @@ smla_combine_kernel(const uint16_t* __restrict__ part_o, int64_t po_rank, int64_
   if (c8 == 0 && lse) lse[(int64_t)t * lse_st + head] = (m == -INFINITY) ? -INFINITY : m + logf(tot);
 }
 
-int32_t plan_splits(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t requested) {
-  const int32_t max_splits = max(1, (topk + kTileRows - 1) / kTileRows);
-  if (requested > 0) return min(requested, max_splits);
-  if (num_tokens <= 0) return 1;
-  // One workgroup per CU (the LDS use allows one): the most splits that keep
-  // tokens x head blocks x splits within one round of 256 workgroups, since a
-  // second partial round costs a whole workgroup time.
-  const int32_t head_blocks = num_heads > 64 ? 2 : 1;
-  const int32_t target_wgs = 256;
-  int32_t s = target_wgs / (num_tokens * head_blocks);
-  const int32_t min_rows = 256;                // keep >= 8 tiles per split
-  s = min(s, max(1, topk / min_rows));
-  return max(1, min(s, max_splits));
-}
-
-
-// The partials take the same space whatever the top-k width (topk is part of
-// the signature so that a later plan may size by it).
-size_t workspace_bytes(int32_t num_tokens, int32_t num_heads, [[maybe_unused]] int32_t topk, int32_t splits) {
-  if (splits <= 1) return 0;
-  const size_t n = (size_t)splits * num_tokens * num_heads;
-  return n * kDLatent * sizeof(uint16_t) + n * sizeof(float);
-}
-
 // With timing events the launch goes through hipExtLaunchKernel, which sets
 // the events from the kernel's own start and end timestamps.
 template <int D, int FMT>
@@ -1093,15 +1047,8 @@ hipError_t launch_attention(const AttnArgs& a, int32_t splits, void* workspace, 
   kp.indices = a.indices; kp.idx_stride = a.idx_stride; kp.topk = a.topk;
   kp.topk_length = a.topk_length;
   kp.req_id = a.req_id;
-  kp.block_table = a.block_table;
-  kp.num_reqs = a.num_reqs;
-  kp.max_blocks = a.max_blocks;
-  kp.bt_stride = a.bt_row_stride;
-  kp.block_size = a.block_size;
-  kp.block_shift = -1;
-  if (a.block_table && a.block_size > 0 && (a.block_size & (a.block_size - 1)) == 0)
-    kp.block_shift = __builtin_ctz((unsigned)a.block_size);
-  kp.block_stride_rows = a.block_stride_rows;
+  kp.bt = BlockTable{a.block_table, a.num_reqs, a.max_blocks, a.bt_row_stride, a.block_size,
+                     block_shift_of(a.block_size), a.block_stride_rows};
   kp.num_tokens = a.num_tokens; kp.num_heads = a.num_heads;
   kp.scale_log2 = a.softmax_scale * 1.4426950408889634f;
   kp.out_mult = 1.0f;

@@ -10,24 +10,21 @@
 // FlashMLA sparse backend (layout: the reading of its size given with FMT 3).
 #include "smla_device.h"
 #include "smla_internal.h"
+#include "smla_lookup.h"
 
 namespace smla {
 
 // One workgroup per token row; entries are independent, the count is a
 // workgroup reduction (deterministic, no atomics).
 __global__ void __launch_bounds__(256)
-convert_indices_kernel(const int32_t* __restrict__ req_id, const int32_t* __restrict__ block_table,
-                       int32_t num_reqs, int32_t max_blocks, int64_t bt_row_stride,
+convert_indices_kernel(const int32_t* __restrict__ req_id, BlockTable bt,
                        const int32_t* __restrict__ topk_local, int64_t loc_stride, int32_t topk,
-                       int32_t block_size, int32_t block_stride_rows,
                        int32_t* __restrict__ global_out, int64_t out_stride,
                        int32_t* __restrict__ valid_counts) {
   const int t = blockIdx.x;
   const int32_t* src = topk_local + (int64_t)t * loc_stride;
   int32_t* dst = global_out + (int64_t)t * out_stride;
   const int r = req_id[t];
-  const bool req_ok = (r >= 0) && (r < num_reqs);
-  const int32_t* bt = block_table + (int64_t)(req_ok ? r : 0) * bt_row_stride;
   int cnt = 0;
   // 2048 entries per pass, 8 per thread: all local-index loads of a pass are
   // in flight together, then all block-table lookups, then the stores.
@@ -39,19 +36,14 @@ convert_indices_kernel(const int32_t* __restrict__ req_id, const int32_t* __rest
       const int j = base + threadIdx.x + 256 * k;
       l[k] = (j < topk) ? src[j] : -1;
     }
-    int e[PER];
+    int64_t g[PER];
 #pragma unroll
-    for (int k = 0; k < PER; k++) {
-      const int blk = l[k] >= 0 ? l[k] / block_size : max_blocks;
-      e[k] = (req_ok && blk < max_blocks) ? bt[blk] : -1;
-    }
+    for (int k = 0; k < PER; k++) g[k] = local_slot(bt, r, l[k]);
 #pragma unroll
     for (int k = 0; k < PER; k++) {
       const int j = base + threadIdx.x + 256 * k;
-      int g = -1;
-      if (e[k] >= 0) g = e[k] * block_stride_rows + (l[k] - (l[k] / block_size) * block_size);
-      if (j < topk) dst[j] = g;
-      cnt += (g >= 0);
+      if (j < topk) dst[j] = g[k] >= 0 ? (int32_t)g[k] : -1;
+      cnt += (g[k] >= 0);
     }
   }
   if (valid_counts) {
@@ -76,11 +68,9 @@ convert_indices_kernel(const int32_t* __restrict__ req_id, const int32_t* __rest
 // One workgroup per row, 8 consecutive entries per thread; the compaction
 // offsets come from a workgroup prefix sum of the per-thread counts.
 __global__ void __launch_bounds__(256)
-dcp_filter_kernel(const int32_t* __restrict__ req_id, const int32_t* __restrict__ block_table,
-                  int32_t num_reqs, int32_t max_blocks, int64_t bt_row_stride,
+dcp_filter_kernel(const int32_t* __restrict__ req_id, BlockTable bt,
                   const int32_t* __restrict__ topk_tokens, int64_t in_stride, int32_t topk,
-                  int32_t dcp_size, int32_t dcp_rank, int32_t interleave,
-                  int32_t block_size, int32_t block_stride_rows, int32_t compact,
+                  int32_t dcp_size, int32_t dcp_rank, int32_t interleave, int32_t compact,
                   int32_t* __restrict__ out, int64_t out_stride, int32_t* __restrict__ valid_counts) {
   __shared__ int s_wave[4];
   const int t = blockIdx.x;
@@ -88,8 +78,6 @@ dcp_filter_kernel(const int32_t* __restrict__ req_id, const int32_t* __restrict_
   const int32_t* src = topk_tokens + (int64_t)t * in_stride;
   int32_t* dst = out + (int64_t)t * out_stride;
   const int r = req_id[t];
-  const bool req_ok = (r >= 0) && (r < num_reqs);
-  const int32_t* bt = block_table + (int64_t)(req_ok ? r : 0) * bt_row_stride;
   constexpr int PER = 8;
   int running = 0;                                      // valid entries in earlier passes (uniform)
   for (int base = 0; base < topk; base += 256 * PER) {
@@ -104,11 +92,8 @@ dcp_filter_kernel(const int32_t* __restrict__ req_id, const int32_t* __restrict_
         const int run = pos / interleave;
         if (run % dcp_size == dcp_rank) {
           const int local = (run / dcp_size) * interleave + (pos - run * interleave);
-          const int blk = local / block_size;
-          if (req_ok && blk < max_blocks) {
-            const int e = bt[blk];
-            if (e >= 0) v = e * block_stride_rows + (local - blk * block_size);
-          }
+          const int64_t g = local_slot(bt, r, local);
+          if (g >= 0) v = (int32_t)g;
         }
       }
       g[k] = v;
@@ -264,8 +249,7 @@ planned_counts_kernel(const int32_t* __restrict__ seq_lens, const int32_t* __res
 // the 8 rope chunks.
 __global__ void __launch_bounds__(256)
 gather_upconvert_kernel(const uint8_t* __restrict__ cache, int64_t num_slots, int64_t row_stride,
-                        const int32_t* __restrict__ block_table, int32_t max_blocks, int64_t bt_row_stride,
-                        int32_t block_size, int32_t block_stride_rows, const int32_t* __restrict__ seq_lens,
+                        BlockTable bt, const int32_t* __restrict__ seq_lens,
                         const int32_t* __restrict__ starts, uint16_t* __restrict__ ws, int64_t ws_rows,
                         int64_t ws_stride) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -273,15 +257,13 @@ gather_upconvert_kernel(const uint8_t* __restrict__ cache, int64_t num_slots, in
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.y;
   const int p = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int n = min((int64_t)seq_lens[r], (int64_t)max_blocks * block_size);
+  const int n = min((int64_t)seq_lens[r], (int64_t)bt.max_blocks * bt.block_size);
   if (p >= n) return;
   const int64_t w = (int64_t)starts[r] + p;
   if (w < 0 || w >= ws_rows) return;
-  const int blk = p / block_size;
-  const int e = block_table[(int64_t)r * bt_row_stride + blk];
-  const int64_t slot = (int64_t)e * block_stride_rows + (p - blk * block_size);
+  const int64_t slot = local_slot(bt, r, p);
   uint16_t* dst = ws + w * ws_stride;
-  if (e < 0 || slot >= num_slots) {
+  if (slot < 0 || slot >= num_slots) {
     *(u32x4*)(dst + 8 * lane) = (u32x4){0u, 0u, 0u, 0u};
     if (lane < 8) *(u32x4*)(dst + 512 + 8 * lane) = (u32x4){0u, 0u, 0u, 0u};
     return;
@@ -311,27 +293,29 @@ hipError_t launch_planned_counts(const PlannedCountsArgs& a, hipStream_t stream)
 hipError_t launch_gather_upconvert(const UpconvertArgs& a, hipStream_t stream) {
   if (a.num_reqs == 0 || a.max_seq_len <= 0) return hipSuccess;
   dim3 grid((a.max_seq_len + 3) / 4, a.num_reqs);
-  gather_upconvert_kernel<<<grid, 256, 0, stream>>>(a.cache, a.num_slots, a.row_stride, a.block_table, a.max_blocks,
-                                                    a.bt_row_stride, a.block_size, a.block_stride_rows, a.seq_lens,
+  const BlockTable bt{a.block_table, a.num_reqs, a.max_blocks, a.bt_row_stride, a.block_size,
+                      block_shift_of(a.block_size), a.block_stride_rows};
+  gather_upconvert_kernel<<<grid, 256, 0, stream>>>(a.cache, a.num_slots, a.row_stride, bt, a.seq_lens,
                                                     a.starts, a.ws, a.ws_rows, a.ws_stride);
   return hipGetLastError();
 }
 
 hipError_t launch_convert(const ConvertArgs& a, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;
-  convert_indices_kernel<<<a.num_tokens, 256, 0, stream>>>(
-      a.req_id, a.block_table, a.num_reqs, a.max_blocks, a.bt_row_stride, a.topk_local,
-      a.topk_local_stride, a.topk, a.block_size, a.block_stride_rows, a.global_out,
-      a.global_stride, a.valid_counts);
+  const BlockTable bt{a.block_table, a.num_reqs, a.max_blocks, a.bt_row_stride, a.block_size,
+                      block_shift_of(a.block_size), a.block_stride_rows};
+  convert_indices_kernel<<<a.num_tokens, 256, 0, stream>>>(a.req_id, bt, a.topk_local, a.topk_local_stride, a.topk,
+                                                           a.global_out, a.global_stride, a.valid_counts);
   return hipGetLastError();
 }
 
 hipError_t launch_dcp_filter(const DcpFilterArgs& a, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;
-  dcp_filter_kernel<<<a.num_tokens, 256, 0, stream>>>(
-      a.req_id, a.block_table, a.num_reqs, a.max_blocks, a.bt_row_stride, a.topk_tokens, a.in_stride, a.topk,
-      a.dcp_size, a.dcp_rank, a.interleave, a.block_size, a.block_stride_rows, a.compact ? 1 : 0, a.out,
-      a.out_stride, a.valid_counts);
+  const BlockTable bt{a.block_table, a.num_reqs, a.max_blocks, a.bt_row_stride, a.block_size,
+                      block_shift_of(a.block_size), a.block_stride_rows};
+  dcp_filter_kernel<<<a.num_tokens, 256, 0, stream>>>(a.req_id, bt, a.topk_tokens, a.in_stride, a.topk, a.dcp_size,
+                                                      a.dcp_rank, a.interleave, a.compact ? 1 : 0, a.out,
+                                                      a.out_stride, a.valid_counts);
   return hipGetLastError();
 }
 

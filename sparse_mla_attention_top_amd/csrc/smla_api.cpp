@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -146,6 +147,35 @@ smla::AttnArgs to_internal(const smla_attn_args* a) {
 }
 
 }  // namespace
+
+namespace smla {
+
+int32_t plan_splits(int32_t num_tokens, int32_t num_heads, int32_t topk, int32_t requested) {
+  // 64-bit throughout: the sizing entry points take any int32 arguments
+  const int64_t max_splits = std::max<int64_t>(1, ((int64_t)topk + kTileRows - 1) / kTileRows);
+  if (requested > 0) return (int32_t)std::min<int64_t>(requested, max_splits);
+  if (num_tokens <= 0) return 1;
+  // One workgroup per CU (the LDS use allows one): the most splits that keep
+  // tokens x head blocks x splits within one round of 256 workgroups, since a
+  // second partial round costs a whole workgroup time.
+  const int64_t head_blocks = num_heads > 64 ? 2 : 1;
+  const int64_t target_wgs = 256;
+  int64_t s = target_wgs / ((int64_t)num_tokens * head_blocks);
+  const int64_t min_rows = 256;                // keep >= 8 tiles per split
+  s = std::min<int64_t>(s, std::max<int64_t>(1, (int64_t)topk / min_rows));
+  return (int32_t)std::max<int64_t>(1, std::min<int64_t>(s, max_splits));
+}
+
+
+// The partials take the same space whatever the top-k width (topk is part of
+// the signature so that a later plan may size by it).
+size_t workspace_bytes(int32_t num_tokens, int32_t num_heads, [[maybe_unused]] int32_t topk, int32_t splits) {
+  if (splits <= 1) return 0;
+  const size_t n = (size_t)splits * num_tokens * num_heads;
+  return n * 512 * sizeof(uint16_t) + n * sizeof(float);   // bf16 [splits][T][H][512] + fp32 LSE
+}
+
+}  // namespace smla
 
 extern "C" {
 
