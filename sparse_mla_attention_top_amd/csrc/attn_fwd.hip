@@ -18,9 +18,11 @@
 //     64 heads x latent channels 128w..128w+127 in accumulator registers,
 //     A = P from LDS, B = V read with ds_read_b64_tr_b16 from the same tile
 //     (V is the first 512 channels of the gathered row, no second gather).
-//   FP8 caches: rows land in a stage as E4M3 bytes and each wave converts the
-//     rows it copied into the bf16 tile; the latent segments are shared
-//     between the roles (Shape::SEG_O).
+//   FP8 caches: the tile stays in LDS as E4M3 codes (half the bytes of a
+//     bf16 tile) and every MFMA operand is converted to bf16 as it is read:
+//     K with ds_read_b128 (16 codes, two k-steps), V with the 8-bit transposing
+//     read ds_read_b64_tr_b8 (8 codes, one n-block). The FlashMLA-style design
+//     of dequantising into a bf16 tile first costs an LDS round trip per tile.
 // So on every SIMD one wave's softmax / conversion work overlaps the other's
 // MFMAs, and one barrier per tile orders both roles. Before the loop all
 // threads stage the row's indices (converting request-local indices through
@@ -105,51 +107,47 @@ constexpr int kLatKS = kDLatent / 32;                  // k-steps over the 512 l
 constexpr int kLatBytes = kTileRows * kDLatent * 2;    // bf16 latent part of a tile (32 KB)
 constexpr int kRopeBytes = kTileRows * 64 * 2;         // bf16 rope part of a tile (4 KB)
 
-// Buffers of one workgroup. A bf16 tile is its latent part (chunks 0..63 of
-// every row, tile_pos layout, 32 KB) plus, for D = 576, its rope part (chunks
-// 64..71, 4 KB) in a separate ring: the latent part is read one tile longer
-// (by P.V).
-//   bf16 cache: 4 latent + 3 rope buffers; tile i+2 is copied during tile i.
-//   FP8 cache : 3 latent + 2 rope bf16 buffers and 2 FP8 stages; tile i+2 is
-//               copied and tile i+1 converted during tile i.
-// FP8 stage of one tile, as copied from HBM (E4M3 bytes). O-wave w copies and
-// later converts its own rows 8w .. 8w+7:
-//   latent : segment u (bytes 128u .. 128u+127 of the row, u < 4) of the 8
-//            rows in block 4u + w (1 KB, lane l = 8 (row & 7) + chunk);
-//   rope   : (D = 576) bytes 512 .. 575 of the 8 rows, 512 B per wave
-//            (lane l < 32 = 4 (row & 7) + chunk);
-//   scales : (group formats) the G fp32 group scales of the 8 rows, 8G
-//            dwords per wave (lane l < 8G = G (row & 7) + group).
-// Packed rows (FMT 3: 512 E4M3 codes, 4 fp32 scales, 64 bf16 rope channels in
-// 656 bytes) stage only the codes and the scales; their bf16 rope part is
-// copied straight into a rope buffer (3 buffers, as for a bf16 cache).
+// Buffers of one workgroup.
+//   bf16 cache: a tile is its latent part (chunks 0..63 of every row,
+//     tile_pos layout, 32 KB) plus, for D = 576, its rope part (chunks 64..71,
+//     4 KB) in a separate ring, since the latent part is read one tile longer
+//     (by P.V): 4 latent + 3 rope buffers; tile i+2 is copied during tile i.
+//   FP8 cache: a tile stays in LDS as it was copied, and each MFMA operand is
+//     converted to bf16 as it is read. One buffer holds the tile's latent
+//     codes (tile_pos8 layout, 16 KB), its rope part (D = 576: 64 E4M3 codes
+//     per row, 2 KB; packed rows: 64 bf16 channels per row, 4 KB) and, in the
+//     group formats, its scales ([group][row] fp32). 5 buffers; tile i+3 is
+//     copied during tile i.
+// The epilogue stages O (64 heads x 512 channels, bf16) in the first 64 KB of
+// the latent ring and the row sums after it.
 template <int D, int FMT>
 struct Shape {
   static constexpr bool F8 = FMT != 0;
   static constexpr bool ROPE = D > kDLatent;
   static constexpr bool PACKED = FMT == 3;
   static constexpr bool GROUP = FMT == 2 || FMT == 3;
-  static constexpr bool ROPE8 = F8 && ROPE && !PACKED; // rope part staged as E4M3 bytes
+  static constexpr bool ROPE8 = F8 && ROPE && !PACKED; // rope part as E4M3 codes
   static constexpr int QKS = D / 32;                   // k-steps of the QK contraction
-  static constexpr int NLAT = F8 ? 3 : 4;
-  static constexpr int NROPE = ROPE ? (ROPE8 ? 2 : 3) : 0;
   static constexpr int G = PACKED ? 4 : (D + 127) / 128;   // scale groups (packed: the latent's)
-  static constexpr int ST_ROPE = 16 * 1024;
-  static constexpr int ST_SC = ST_ROPE + (ROPE8 ? 4 * 512 : 0);
-  static constexpr int ST_BYTES = ST_SC + (GROUP ? 4 * 256 : 0);
-  static constexpr int NSTAGE = F8 ? 2 : 0;
-  static constexpr int NRSC = GROUP ? 3 : 0;           // row-scale sets (tiles i-1, i, i+1)
-  // copy instructions per wave per tile. FP8: latent segments 0-1, the rope
-  // part and the scales are copied (and converted) by the O-waves, latent
-  // segments 2-3 by the S-waves; bf16: all by the O-waves.
-  // FP8: latent segments [0, SEG_O) are copied and converted by the O-waves,
-  // [SEG_O, 4) by the S-waves (moving more to either side measured slower)
-  static constexpr int SEG_O = 2;
-  static constexpr int NDMA_O = F8 ? SEG_O + (ROPE ? 1 : 0) + (GROUP ? 1 : 0) : D / 64;
-  static constexpr int NDMA_S = F8 ? 4 - SEG_O : 0;
+  // bf16 ring
+  static constexpr int NLAT = F8 ? 0 : 4;
+  static constexpr int NROPE = (!F8 && ROPE) ? 3 : 0;
+  // FP8 ring: byte offsets inside a tile buffer
+  static constexpr int ROPE_AT = 16 * 1024;
+  static constexpr int SC_AT = ROPE_AT + (ROPE8 ? 2048 : (PACKED ? 4096 : 0));
+  static constexpr int TB = SC_AT + (GROUP ? (G * kTileRows * 4 + 255) / 256 * 256 : 0);
+  // tiles copied ahead (FP8: 3; 4 and 5 measured no faster on the decode shapes)
+  static constexpr int PD = F8 ? 3 : 2;
+  static constexpr int NBUF = PD + 2;
+  static constexpr int NSC = GROUP ? (G + 1) / 2 : 0;  // scale copies per tile, by O-waves 0 .. NSC-1
+  // copy instructions per O-wave per tile (FP8: besides the scale copy)
+  static constexpr int NDMA = F8 ? 4 + (ROPE ? 1 : 0) : D / 64;
+  static constexpr int RING = F8 ? NBUF * TB : NLAT * kLatBytes;
   static_assert(D == kDLatent || D == kDLatent + 64, "rope part must be 64 channels");
-  static_assert(8 * G <= 64, "scales of 8 rows fit one instruction");
   static_assert(!PACKED || ROPE, "packed rows carry the rope part");
+  static_assert(G * kTileRows * 4 <= 1024, "the scales of a tile fit 1 KB");
+  static_assert(RING >= 64 * 1024 + 2048, "the epilogue stages O and the row sums in the ring");
+  static_assert(!F8 || NBUF >= PD + 2, "tile i+PD must land in a buffer that no role still reads");
 };
 
 // Byte offsets inside a packed row.
@@ -164,27 +162,22 @@ __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))
 smla_attn_kernel(KParams p) {
   using S = Shape<D, FMT>;
   constexpr bool F8 = S::F8;
-  constexpr int QKS = S::QKS, NLAT = S::NLAT, NROPE = S::NROPE;
+  constexpr int QKS = S::QKS, NLAT = S::NLAT, NROPE = S::NROPE, PD = S::PD;
 
-  __shared__ __attribute__((aligned(16))) char s_lat[NLAT * kLatBytes];
+  __shared__ __attribute__((aligned(16))) char s_lat[S::RING];
   __shared__ __attribute__((aligned(16))) char s_rope[(NROPE ? NROPE * kRopeBytes : 16)];
-  __shared__ __attribute__((aligned(16))) char s_stage[F8 ? S::NSTAGE * S::ST_BYTES : 16];
   __shared__ __attribute__((aligned(16))) char s_p[2 * 4 * 64 * 16];   // P(i) in block i & 1, [mblock][lane]
   __shared__ int s_idx[kMaxTopk];
-  __shared__ __attribute__((aligned(16))) float s_rsc[S::GROUP ? S::NRSC * S::G * kTileRows : 4];
   __shared__ int s_flag;
   __shared__ int s_last[8];
-  static_assert(NLAT >= 3, "the epilogue stages O in latent buffers 0-1 and row sums in buffer 2");
 
   lds_char* lat = (lds_char*)s_lat;
   lds_char* rope = (lds_char*)s_rope;
-  lds_char* stage = (lds_char*)s_stage;
   lds_char* pbuf = (lds_char*)s_p;
-  lds_char* rsc = (lds_char*)s_rsc;
   // per-head maxima exchanged by the S-waves (only while P block 1 is unused)
   float* s_m = (float*)(s_p + 4 * 64 * 16);
-  // epilogue: row sums and inverse sums in latent buffer 2 (O is staged in 0-1)
-  float* s_l = (float*)(s_lat + 2 * kLatBytes);
+  // epilogue: row sums and inverse sums after the staged O block
+  float* s_l = (float*)(s_lat + 64 * 1024);
   float* s_inv = s_l + 4 * 32;
   float* s_lb = s_inv + 64;
 
@@ -277,174 +270,93 @@ smla_attn_kernel(KParams p) {
   const int ntiles = (row1 - row0 + kTileRows - 1) / kTileRows;
   const int32_t* sidx = s_idx + row0;                      // entries of tile i: sidx[32 i ..]
 
-  // address of chunk c (16 bytes of a bf16 row) of tile row r in bf16 tile i
-  auto lat_buf = [&](int i) -> lds_char* { return lat + (i % NLAT) * kLatBytes; };
+  // bf16: latent and rope buffers of tile i; FP8: the buffer of tile i
+  auto lat_buf = [&](int i) -> lds_char* { return lat + (NLAT ? (i % (NLAT ? NLAT : 1)) * kLatBytes : 0); };
   auto rope_buf = [&](int i) -> lds_char* { return rope + (NROPE ? (i % (NROPE ? NROPE : 1)) * kRopeBytes : 0); };
-  auto rsc_buf = [&](int i) -> lds_char* { return rsc + (S::GROUP ? (i % (S::NRSC ? S::NRSC : 1)) * S::G * kTileRows * 4 : 0); };
+  auto tile8 = [&](int i) -> lds_char* { return lat + (i % S::NBUF) * S::TB; };
 
-  // ---- tile copies (and FP8 conversion), shared by both roles
+  // ---- tile copies, issued by the O-waves. Lane l copies into row 8w + l/8
+  //      of the tile (w: the O-wave's index) the logical chunk (l & 7) ^ swz
+  //      of 128-byte segment u, for every u: the same row and column, so one
+  //      address per tile serves all copies through the immediate offset 128u.
   const int wu = __builtin_amdgcn_readfirstlane(wr);
   const uint32_t kv_stride = (uint32_t)p.kv_row_stride;
   const uint32_t lat_addr = (uint32_t)(uintptr_t)lat;
   const uint32_t rope_addr = (uint32_t)(uintptr_t)rope;
-  const uint32_t stage_addr = (uint32_t)(uintptr_t)stage;
-  // bf16 cache: copy u of O-wave w fills block 4u + w of the tile (segment u,
-  // bytes 128u .. 128u+127, of rows 8w .. 8w+7; segment 8 is the rope part).
-  // Lane l loads row 8w + l/8, logical chunk (l & 7) ^ swz(row): the same row
-  // and column for every u, so one address per tile serves all copies
-  // through the immediate offset 128u.
   const int drow = 8 * wu + (l >> 3);
-  const uint32_t dcol = (uint32_t)(16 * ((l & 7) ^ swz(drow)));
-  // FP8 cache: latent chunk l & 7 of row 8w + l/8 (segment u at offset 128u);
-  // rope chunk l & 3 of row 8w + l/4; scale l % G of row 8w + l/G.
-  const int srow = min(l / S::G, 7), sgrp = l % S::G;
-  struct Src {
-    const uint8_t* lat;
-    const uint8_t* rope;
-    const float* sc;
-  };
-  auto sources = [&](int i) -> Src {
-    Src s;
-    const int base = i * kTileRows + 8 * wu;
-    if constexpr (!F8) {
-      s.lat = p.kv + ((uint64_t)(uint32_t)max(sidx[base + (l >> 3)], 0) * kv_stride + dcol);
-    } else {
-      const uint8_t* row = p.kv + (uint64_t)(uint32_t)max(sidx[base + (l >> 3)], 0) * kv_stride;
-      s.lat = row + 16 * (l & 7);
-      if constexpr (S::ROPE8)
-        s.rope = p.kv + ((uint64_t)(uint32_t)max(sidx[base + ((l >> 2) & 7)], 0) * kv_stride + kDLatent + 16 * (l & 3));
-      if constexpr (S::PACKED) {
-        // bf16 rope chunk of the same row, at its swizzled place in the rope buffer
-        s.rope = row + kPackedRopeAt + dcol;
-        s.sc = (const float*)(p.kv + (uint64_t)(uint32_t)max(sidx[base + srow], 0) * kv_stride + kPackedScalesAt) + sgrp;
-      } else if constexpr (S::GROUP) {
-        s.sc = p.group_scales + ((uint64_t)(uint32_t)max(sidx[base + srow], 0) * (uint64_t)p.gs_stride + sgrp);
-      }
-    }
-    return s;
-  };
-  // FP8 latent segment u of this wave's rows of tile i -> stage
-  auto issue_seg = [&](const Src& s, int i, auto u_c) {
-    constexpr int u = decltype(u_c)::value;
-    const uint32_t sb = stage_addr + (i % (S::NSTAGE ? S::NSTAGE : 1)) * S::ST_BYTES;
-    dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(sb + (4 * u + wu) * 1024));
-  };
-  // O-wave copies of tile i
+  const uint32_t dcol = (uint32_t)(16 * ((l & 7) ^ swz(drow)));      // bf16 rows, packed bf16 rope
+  const uint32_t dcol8 = (uint32_t)(16 * ((l & 7) ^ swz8(drow)));    // E4M3 latent codes
+  // E4M3 rope codes (D = 576): lanes 0..31 copy chunk (l & 3) ^ sr of row
+  // 8w + l/4 (sr = 2 for rows 8..15 and 24..31), at ((r & 7) * 4 + chunk) * 16
+  // in the wave's 512 bytes
+  const int rrow = 8 * wu + ((l >> 2) & 7);
+  const uint32_t rcol8 = (uint32_t)(kDLatent + 16 * ((l & 3) ^ (((rrow >> 3) & 1) << 1)));
+  // scales: copy c (c < NSC, by O-wave c) carries groups 2c and 2c+1 of all 32
+  // rows, lane l: row l & 31, group 2c + l/32, at 4 * (group * 32 + row)
+  const int sc_g = 2 * wu + (l >> 5);
+  auto slot_of = [&](int e) -> uint64_t { return (uint64_t)(uint32_t)max(sidx[e], 0); };
+  // O-wave copies of tile i (bf16: segment u of rows 8w .. 8w+7 into block
+  // 4u + w, segment 8 is the rope part)
   auto issue_tile_o = [&](int i) {
-    const Src s = sources(i);
+    const int base = i * kTileRows;
     if constexpr (!F8) {
-      static_for<S::NDMA_O>([&](auto u_c) {
+      const uint8_t* src = p.kv + slot_of(base + drow) * kv_stride + dcol;
+      static_for<S::NDMA>([&](auto u_c) {
         constexpr int u = decltype(u_c)::value;
         if constexpr (u < 8)
-          dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(lat_addr + (i % NLAT) * kLatBytes + (4 * u + wu) * 1024));
+          dma_16b<128 * u>(src, __builtin_amdgcn_readfirstlane(lat_addr + (i % (NLAT ? NLAT : 1)) * kLatBytes + (4 * u + wu) * 1024));
         else
-          dma_16b<128 * u>(s.lat, __builtin_amdgcn_readfirstlane(rope_addr + (i % (NROPE ? NROPE : 1)) * kRopeBytes + wu * 1024));
+          dma_16b<128 * u>(src, __builtin_amdgcn_readfirstlane(rope_addr + (i % (NROPE ? NROPE : 1)) * kRopeBytes + wu * 1024));
       });
     } else {
-      static_for<S::SEG_O>([&](auto u_c) { issue_seg(s, i, u_c); });
-      const uint32_t sb = stage_addr + (i % (S::NSTAGE ? S::NSTAGE : 1)) * S::ST_BYTES;
+      const uint32_t tb = lat_addr + (i % S::NBUF) * S::TB;
+      const uint8_t* row = p.kv + slot_of(base + drow) * kv_stride;
+      const uint8_t* src = row + dcol8;
+      static_for<4>([&](auto u_c) {
+        constexpr int u = decltype(u_c)::value;
+        dma_16b<128 * u>(src, __builtin_amdgcn_readfirstlane(tb + (4 * u + wu) * 1024));
+      });
       if constexpr (S::ROPE8) {
-        if (l < 32) dma_16b<0>(s.rope, __builtin_amdgcn_readfirstlane(sb + S::ST_ROPE + wu * 512));
+        const uint8_t* rsrc = p.kv + slot_of(base + rrow) * kv_stride + rcol8;
+        if (l < 32) dma_16b<0>(rsrc, __builtin_amdgcn_readfirstlane(tb + S::ROPE_AT + wu * 512));
       }
       if constexpr (S::PACKED)
-        dma_16b<0>(s.rope, __builtin_amdgcn_readfirstlane(rope_addr + (i % (NROPE ? NROPE : 1)) * kRopeBytes + wu * 1024));
+        dma_16b<0>(row + kPackedRopeAt + dcol, __builtin_amdgcn_readfirstlane(tb + S::ROPE_AT + wu * 1024));
       if constexpr (S::GROUP) {
-        if (l < 8 * S::G) dma_4b(s.sc, __builtin_amdgcn_readfirstlane(sb + S::ST_SC + wu * 256));
-      }
-    }
-  };
-  // S-wave copies of tile i (FP8: latent segments 2-3)
-  auto issue_tile_s = [&](int i) {
-    if constexpr (F8) {
-      const Src s = sources(i);
-      static_for<4 - S::SEG_O>([&](auto u_c) {
-        issue_seg(s, i, std::integral_constant<int, S::SEG_O + decltype(u_c)::value>{});
-      });
-    }
-  };
-  // FP8 conversion of this wave's rows of tile i into bf16 tile i (exact
-  // E4M3 values). A wave first issues every stage read of its share, then
-  // converts and writes: one LDS round trip instead of one per piece.
-  auto stage_of = [&](int i) -> const lds_char* { return stage + (i % (S::NSTAGE ? S::NSTAGE : 1)) * S::ST_BYTES; };
-  // latent segment u (bytes 128u .. 128u+127 of the row): read, then write
-  auto seg_read = [&](int i, auto u_c) -> u32x4 {
-    constexpr int u = decltype(u_c)::value;
-    return *(const __attribute__((address_space(3))) u32x4*)(stage_of(i) + (4 * u + wr) * 1024 + 16 * l);
-  };
-  auto seg_write = [&](int i, auto u_c, const u32x4 raw) {
-    constexpr int u = decltype(u_c)::value;
-    lds_char* lb = lat_buf(i);
-    const int r = 8 * wr + (l >> 3);
-    u32x4 lo, hi;
-    e4m3x16_to_bf16<false>(raw, 1.0f, lo, hi);
-    const int k = 8 * u + (l & 7);
-    *(__attribute__((address_space(3))) u32x4*)(lb + tile_pos(r, 2 * k)) = lo;
-    *(__attribute__((address_space(3))) u32x4*)(lb + tile_pos(r, 2 * k + 1)) = hi;
-  };
-  // O-wave share: segments [0, SEG_O), the rope part, and (group format) all
-  // the rows' scales -> row-scale set i ([group][row])
-  auto convert_tile_o = [&](int i) {
-    if constexpr (F8) {
-      const lds_char* st = stage_of(i);
-      u32x4 raw[S::SEG_O];
-      static_for<S::SEG_O>([&](auto u_c) { raw[decltype(u_c)::value] = seg_read(i, u_c); });
-      float sc[4] = {}, rsc = 0.0f;
-      u32x4 rraw = {};
-      const int r2 = 8 * wr + (min(l, 31) >> 2);           // rope: lanes 0..31 hold 8 rows x 4 chunks
-      if constexpr (S::GROUP)
-        static_for<4>([&](auto u_c) {
-          constexpr int u = decltype(u_c)::value;
-          sc[u] = *(const __attribute__((address_space(3))) float*)(st + S::ST_SC + wr * 256 + 4 * ((l >> 3) * S::G + u));
-        });
-      if constexpr (S::ROPE8) {
-        rraw = *(const __attribute__((address_space(3))) u32x4*)(st + S::ST_ROPE + wr * 512 + 16 * min(l, 31));
-        if constexpr (S::GROUP)
-          rsc = *(const __attribute__((address_space(3))) float*)(st + S::ST_SC + wr * 256 + 4 * ((r2 - 8 * wr) * S::G + 4));
-      }
-      static_for<S::SEG_O>([&](auto u_c) { seg_write(i, u_c, raw[decltype(u_c)::value]); });
-      if constexpr (S::GROUP) {
-        const int r = 8 * wr + (l >> 3);
-        static_for<4>([&](auto u_c) {
-          constexpr int u = decltype(u_c)::value;
-          *(__attribute__((address_space(3))) float*)(rsc_buf(i) + 4 * (u * kTileRows + r)) = sc[u];
-        });
-      }
-      if constexpr (S::ROPE8) {
-        if (l < 32) {
-          if constexpr (S::GROUP) *(__attribute__((address_space(3))) float*)(rsc_buf(i) + 4 * (4 * kTileRows + r2)) = rsc;
-          u32x4 lo, hi;
-          e4m3x16_to_bf16<false>(rraw, 1.0f, lo, hi);
-          const int k = (l & 3);                            // chunks 64 + 2k, 65 + 2k: rope buffer
-          lds_char* rb = rope_buf(i);
-          *(__attribute__((address_space(3))) u32x4*)(rb + tile_pos(r2, 64 + 2 * k) - kLatBytes) = lo;
-          *(__attribute__((address_space(3))) u32x4*)(rb + tile_pos(r2, 65 + 2 * k) - kLatBytes) = hi;
+        if (wu < S::NSC) {
+          const uint64_t slot = slot_of(base + (l & 31));
+          const float* ssrc = S::PACKED ? (const float*)(p.kv + slot * kv_stride + kPackedScalesAt) + sc_g
+                                        : p.group_scales + (slot * (uint64_t)p.gs_stride + sc_g);
+          if (sc_g < S::G) dma_4b(ssrc, __builtin_amdgcn_readfirstlane(tb + S::SC_AT + wu * 256));
         }
       }
     }
   };
-  // S-wave share: segments [SEG_O, 4)
-  auto convert_tile_s = [&](int i) {
-    if constexpr (F8) {
-      constexpr int NS = 4 - S::SEG_O;
-      u32x4 raw[NS];
-      static_for<NS>([&](auto u_c) {
-        raw[decltype(u_c)::value] = seg_read(i, std::integral_constant<int, S::SEG_O + decltype(u_c)::value>{});
-      });
-      static_for<NS>([&](auto u_c) {
-        seg_write(i, std::integral_constant<int, S::SEG_O + decltype(u_c)::value>{}, raw[decltype(u_c)::value]);
-      });
-    }
+  // this wave's copies of tile k have landed (the copies of the tiles after k
+  // that are already issued, up to k + PD - 1, may stay in flight)
+  auto wait_tile = [&](int k) {
+    const int later = min(ntiles - 1, k + PD - 1) - k;
+    const bool sc = S::GROUP && wu < S::NSC;              // this wave copies scales too
+    static_for<PD>([&](auto n_c) {
+      constexpr int n = decltype(n_c)::value;
+      if (later == n) {
+        if (sc) wait_vmcnt<n * (S::NDMA + 1)>();
+        else wait_vmcnt<n * S::NDMA>();
+      }
+    });
   };
 
   if (is_s) {
     // ======================================================================
     // S-waves: QK^T, softmax, P
     // ======================================================================
-    // Q^T as the B operand of 16x16x32: lane holds head hb + 32hg + 16nbq + li,
-    // channels 32ks + 8lg .. +8 (ks < 16 latent, ks >= 16 rope). Heads past h are zero.
-    // FP8: this wave's copies of tiles 0 and 1 go out before Q
-    if (ntiles > 0) issue_tile_s(0);
-    if (ntiles > 1) issue_tile_s(1);
+    // Q^T as the B operand of 16x16x32: lane holds head hb + 32hg + 16nbq + li
+    // and 8 channels of k-step ks. bf16 cache: channels 32ks + 8lg .. +8.
+    // FP8 cache: the K operand of k-steps 2j and 2j+1 comes from one 16-byte
+    // read of codes 64j + 16lg .. +16, so lane lg holds channels 64j + 16lg .. +8
+    // in k-step 2j and the next 8 in 2j+1 (the contraction sums over the same
+    // channels in another order); the packed rows' bf16 rope part keeps the
+    // bf16 order. Heads past h are zero.
     bf16x8 q[2][QKS];
     if constexpr (!F8) {
       // bf16 cache: the two row halves need the same Q. Each loads half of
@@ -498,13 +410,21 @@ smla_attn_kernel(KParams p) {
         const int head = hb + 32 * hg + 16 * nbq + li;
         const bool valid = head < H;
         const int hq = valid ? head : 0;
-        const uint16_t* qn = p.q_nope + t * p.qn_st + hq * p.qn_sh + 8 * lg;
-#pragma unroll
-        for (int ks = 0; ks < kLatKS; ks++) q[nbq][ks] = *(const bf16x8*)(qn + 32 * ks);
-        if (QKS > kLatKS) {
+        const uint16_t* qn = p.q_nope + t * p.qn_st + hq * p.qn_sh + 16 * lg;
+        static_for<kLatKS / 2>([&](auto j_c) {
+          constexpr int j = decltype(j_c)::value;
+          q[nbq][2 * j] = *(const bf16x8*)(qn + 64 * j);
+          q[nbq][2 * j + 1] = *(const bf16x8*)(qn + 64 * j + 8);
+        });
+        if constexpr (S::ROPE8) {
+          const uint16_t* qr = p.q_rope + t * p.qr_st + hq * p.qr_sh + 16 * lg;
+          q[nbq][kLatKS] = *(const bf16x8*)qr;
+          q[nbq][kLatKS + 1] = *(const bf16x8*)(qr + 8);
+        }
+        if constexpr (S::PACKED) {
           const uint16_t* qr = p.q_rope + t * p.qr_st + hq * p.qr_sh + 8 * lg;
-#pragma unroll
-          for (int ks = kLatKS; ks < QKS; ks++) q[nbq][ks] = *(const bf16x8*)(qr + 32 * (ks - kLatKS));
+          q[nbq][kLatKS] = *(const bf16x8*)qr;
+          q[nbq][kLatKS + 1] = *(const bf16x8*)(qr + 32);
         }
         if (!valid) {
 #pragma unroll
@@ -515,12 +435,20 @@ smla_attn_kernel(KParams p) {
     // complete here, so that the compiler puts no wait on the Q registers inside the loop
     wait_vmcnt<0>();
 
-    // K reads (A operand of 16x16x32): row 16rh + li, chunk 4ks + lg; k-steps
-    // 0..15 in the latent buffer at kbase[ks & 1] + 4096 (ks >> 1), 16..17 in
-    // the rope buffer at kbase[ks & 1] + 4096 (ks >> 1) - 32768.
-    int kbase[2];
+    // K reads (A operand of 16x16x32): row 16rh + li. bf16: chunk 4ks + lg;
+    // k-steps 0..15 in the latent buffer at kbase[ks & 1] + 4096 (ks >> 1),
+    // 16..17 in the rope buffer at kbase[ks & 1] + 4096 (ks >> 1) - 32768
+    // (packed rows' bf16 rope: kbase[ks - 16] in the tile's rope part).
+    // FP8: codes of k-pair j < 8 (chunk 4j + lg) at kb8[j & 1] + 4096 (j >> 1),
+    // the E4M3 rope part (chunk lg) at kr8.
+    int kbase[2], kb8[2];
 #pragma unroll
-    for (int j = 0; j < 2; j++) kbase[j] = tile_pos(16 * rh + li, 4 * j + lg);
+    for (int j = 0; j < 2; j++) {
+      kbase[j] = tile_pos(16 * rh + li, 4 * j + lg);
+      kb8[j] = tile_pos8(16 * rh + li, 4 * j + lg);
+    }
+    const int kr = 16 * rh + li;
+    const int kr8 = S::ROPE_AT + (kr >> 3) * 512 + ((kr & 7) * 4 + (lg ^ (((kr >> 3) & 1) << 1))) * 16;
 
     // S^T[16 rows x 32 heads] of the wave for tile i (unscaled sums). Lane holds
     // rows 16rh + 4lg + r (r = 0..3) of heads 32hg + 16nbq + li. Group
@@ -536,48 +464,122 @@ smla_attn_kernel(KParams p) {
         if constexpr (ks < kLatKS) return lb + kbase[ks & 1] + 4096 * (ks >> 1);
         else return rb + kbase[ks & 1] + 4096 * (ks >> 1) - kLatBytes;
       };
-      f32x4 s0 = {}, s1 = {}, s2 = {}, s3 = {};   // even / odd k-steps: 4 independent chains
-      f32x4 t0 = {}, t1 = {};
-      [[maybe_unused]] const lds_char* rs = rsc_buf(i) + 4 * (16 * rh + 4 * lg);   // row scales (group formats)
-      constexpr int PF = S::GROUP ? 2 : 6;        // K operand reads kept in flight
+      // 4 independent accumulator chains (k-step ks into chain ks & 1 of each
+      // head block). A dependent 16x16x32 MFMA waits about 7 MFMA slots for its
+      // accumulator, so alone one wave reaches ~60% of the matrix core with
+      // them, but the O-wave's P.V fills the gaps: 8 chains measured the same.
+      f32x4 acc[2][2] = {};
+      constexpr int PF = 6;                       // K operand reads kept in flight
       bf16x8 a[PF];
       static_for<PF>([&](auto ks_c) { a[decltype(ks_c)::value] = lds_ld128(kaddr(ks_c)); });
       static_for<QKS>([&](auto ks_c) {
         constexpr int ks = decltype(ks_c)::value;
         const bf16x8 cur = a[ks % PF];
         if constexpr (ks + PF < QKS) a[ks % PF] = lds_ld128(kaddr(std::integral_constant<int, ks + PF>{}));
-        if constexpr (S::GROUP && (ks & 3) == 0 && ks > 0) {
-          // group ks/4 - 1 is complete: scale and add it, start afresh
-          const f32x4 gsc = *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * (ks / 4 - 1));
-          t0 += gsc * (s0 + s2);
-          t1 += gsc * (s1 + s3);
-          s0 = (f32x4){}; s1 = (f32x4){}; s2 = (f32x4){}; s3 = (f32x4){};
-        }
         __builtin_amdgcn_sched_barrier(0);          // keep the read-ahead ahead of the MFMAs
-        const bf16x8 b0 = q[0][ks], b1 = q[1][ks];
-        if constexpr ((ks & 1) == 0 || S::GROUP) {        // group format: two chains (registers)
-          s0 = mfma16x16x32(cur, b0, s0);
-          s1 = mfma16x16x32(cur, b1, s1);
-        } else {
-          s2 = mfma16x16x32(cur, b0, s2);
-          s3 = mfma16x16x32(cur, b1, s3);
-        }
+        acc[ks & 1][0] = mfma16x16x32(cur, q[0][ks], acc[ks & 1][0]);
+        acc[ks & 1][1] = mfma16x16x32(cur, q[1][ks], acc[ks & 1][1]);
         __builtin_amdgcn_sched_barrier(0);
       });
-      if constexpr (S::PACKED) {                        // the rope group is bf16: unscaled
-        s0 = t0 + (s0 + s2);
-        s1 = t1 + (s1 + s3);
-      } else if constexpr (S::GROUP) {
-        constexpr int gl = (QKS - 1) / 4;               // last group
-        const f32x4 lsc = *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * gl);
-        s0 = t0 + lsc * (s0 + s2);
-        s1 = t1 + lsc * (s1 + s3);
-      } else {
-        s0 += s2;
-        s1 += s3;
+      r0 = acc[0][0] + acc[1][0];
+      r1 = acc[0][1] + acc[1][1];
+    };
+    // FP8: per k-pair j one 16-byte read of 16 codes per lane, converted to the
+    // A operands of k-steps 2j (codes 0..7) and 2j+1 (codes 8..15) one pair
+    // ahead of their MFMAs. Accumulator chains acc[set][head block]:
+    //   per-tensor: pair j into sets 0 (k-step 2j) and 1 (k-step 2j+1), 4
+    //     chains (8 measured the same: the O-wave's P.V fills the gaps);
+    //   group formats: group g (pairs 2g, 2g+1) into sets 2 (g & 1) and
+    //     2 (g & 1) + 1. Group g-1's sums are scaled by the rows' group scales
+    //     and folded into t0 / t1 at the end of group g, just before group g+1
+    //     reuses their sets, so that the fold's VALU reads wait as little as
+    //     possible for MFMA results. These reads are still the group formats'
+    //     main cost: with the folds left out (timing only) the QK^T of the
+    //     long-context tile took half as long. The scales of group g are read
+    //     at its first pair and used a group later (LDS reads return in order:
+    //     waiting for them does not wait for the code reads issued after them).
+    auto scores8 = [&](int i, f32x4& r0, f32x4& r1) {
+      const lds_char* tb = tile8(i);
+      constexpr int NP = kLatKS / 2 + (S::ROPE8 ? 1 : 0);  // k-pairs held as codes
+      auto kaddr = [&](auto j_c) -> const lds_char* {
+        constexpr int j = decltype(j_c)::value;
+        if constexpr (j < kLatKS / 2) return tb + kb8[j & 1] + 4096 * (j >> 1);
+        else return tb + kr8;
+      };
+      f32x4 acc[4][2] = {};
+      f32x4 t0 = {}, t1 = {};
+      [[maybe_unused]] const lds_char* rs = tb + S::SC_AT + 4 * (16 * rh + 4 * lg);   // [group][row] scales
+      [[maybe_unused]] f32x4 gs[2];
+      auto read_scales = [&](int g) -> f32x4 { return *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * g); };
+      // fold the sums of group g (sets 2 (g & 1), +1) into t0 / t1 and clear them
+      auto fold = [&](auto g_c) {
+        constexpr int g = decltype(g_c)::value, c = 2 * (g & 1);
+        const f32x4 gsc = gs[g & 1];
+        t0 += gsc * (acc[c][0] + acc[c + 1][0]);
+        t1 += gsc * (acc[c][1] + acc[c + 1][1]);
+        acc[c][0] = acc[c][1] = acc[c + 1][0] = acc[c + 1][1] = (f32x4){};
+      };
+      constexpr int PF = S::GROUP ? 2 : 3;        // code reads kept in flight
+      u32x4 a[PF];
+      if constexpr (S::GROUP) gs[0] = read_scales(0);
+      [[maybe_unused]] bf16x8 k0, k1;
+      if constexpr (S::PACKED) {                   // the bf16 rope part's two k-steps
+        k0 = lds_ld128(tb + S::ROPE_AT + kbase[0]);
+        k1 = lds_ld128(tb + S::ROPE_AT + kbase[1]);
       }
-      r0 = s0;
-      r1 = s1;
+      static_for<PF>([&](auto j_c) {
+        a[decltype(j_c)::value] = *(const __attribute__((address_space(3))) u32x4*)kaddr(j_c);
+      });
+      if constexpr (S::PACKED) {                   // unscaled, straight into t0 / t1
+        t0 = mfma16x16x32(k0, q[0][kLatKS], t0);
+        t1 = mfma16x16x32(k0, q[1][kLatKS], t1);
+        t0 = mfma16x16x32(k1, q[0][kLatKS + 1], t0);
+        t1 = mfma16x16x32(k1, q[1][kLatKS + 1], t1);
+      }
+      // per-tensor: pair j+1 is converted during pair j; group formats (8 more
+      // live registers for the deferred folds): each pair at its own start
+      constexpr bool AHEAD = !S::GROUP;
+      bf16x8 clo, chi;
+      if constexpr (AHEAD) {
+        clo = e4m3x8_to_bf16x8(a[0][0], a[0][1]);
+        chi = e4m3x8_to_bf16x8(a[0][2], a[0][3]);
+      }
+      static_for<NP>([&](auto j_c) {
+        constexpr int j = decltype(j_c)::value;
+        constexpr int c = S::GROUP ? 2 * ((j / 2) & 1) : 0;
+        if constexpr (!AHEAD) {
+          const u32x4 cu = a[j % PF];
+          clo = e4m3x8_to_bf16x8(cu[0], cu[1]);
+          chi = e4m3x8_to_bf16x8(cu[2], cu[3]);
+        }
+        const bf16x8 lo = clo, hi = chi;
+        if constexpr (S::GROUP && (j & 1) == 0 && j > 0) gs[(j / 2) & 1] = read_scales(j / 2);
+        if constexpr (j + PF < NP)
+          a[j % PF] = *(const __attribute__((address_space(3))) u32x4*)kaddr(std::integral_constant<int, j + PF>{});
+        if constexpr (AHEAD && j + 1 < NP) {
+          const u32x4 nx = a[(j + 1) % PF];
+          clo = e4m3x8_to_bf16x8(nx[0], nx[1]);
+          chi = e4m3x8_to_bf16x8(nx[2], nx[3]);
+        }
+        acc[c][0] = mfma16x16x32(lo, q[0][2 * j], acc[c][0]);
+        acc[c][1] = mfma16x16x32(lo, q[1][2 * j], acc[c][1]);
+        acc[c + 1][0] = mfma16x16x32(hi, q[0][2 * j + 1], acc[c + 1][0]);
+        acc[c + 1][1] = mfma16x16x32(hi, q[1][2 * j + 1], acc[c + 1][1]);
+        if constexpr (S::GROUP && (j & 1) == 1 && j >= 3) fold(std::integral_constant<int, (j - 3) / 2>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if constexpr (S::GROUP) {
+        // the groups not folded in the loop, up to the last one (packed rows:
+        // latent group 3, the rope part is bf16)
+        constexpr int GL = S::PACKED ? 3 : (QKS - 1) / 4;
+        constexpr int G0 = NP >= 3 ? (NP - 3) / 2 + ((NP - 3) % 2 ? 1 : 0) : 0;   // first group without an in-loop fold
+        static_for<GL - G0 + 1>([&](auto k_c) { fold(std::integral_constant<int, G0 + decltype(k_c)::value>{}); });
+        r0 = t0;
+        r1 = t1;
+      } else {
+        r0 = acc[0][0] + acc[1][0];
+        r1 = acc[0][1] + acc[1][1];
+      }
     };
     // maximum over the workgroup's 32 rows (both row halves), per head; one
     // barrier, which the O-waves match
@@ -635,21 +637,11 @@ smla_attn_kernel(KParams p) {
     // flagging a rerun if a row sum left the range the reference guarantees
     // (some p = 2^(t - m) above 2^64, or not finite), or if tile 0 held no
     // valid entry (no reference) while a later tile did.
-    auto s_pass = [&](auto cap_c, const bool full, float (&mx_all)[2], const bool issued) {
+    auto s_pass = [&](auto cap_c, const bool full, float (&mx_all)[2]) {
       constexpr bool CAP = decltype(cap_c)::value;          // softcap on (uniform, hoisted out of the loop)
       l_lane[0] = l_lane[1] = 0.0f;
       lb_lane[0] = lb_lane[1] = 0.0f;
       bool seen = false;                                   // a valid entry in some tile (uniform)
-      if constexpr (F8) {                                  // this wave's share of tile 0
-        if (!issued) {
-          if (ntiles > 0) issue_tile_s(0);
-          if (ntiles > 1) issue_tile_s(1);
-        }
-        if (ntiles > 0) {
-          if (ntiles > 1) wait_vmcnt<S::NDMA_S>(); else wait_vmcnt<0>();
-          convert_tile_s(0);
-        }
-      }
       // the index entry of row l & 31 of the next tile is read one tile ahead,
       // so the row mask needs no LDS round trip at the start of a tile
       int idx_next = ntiles > 0 ? sidx[l & 31] : -1;
@@ -658,7 +650,6 @@ smla_attn_kernel(KParams p) {
         const bool have = i < ntiles;
         const int idx_cur = idx_next;
         if (i + 1 < ntiles) idx_next = sidx[(i + 1) * kTileRows + (l & 31)];
-        if (F8 && i + 2 < ntiles) issue_tile_s(i + 2);
         f32x4 r0 = {}, r1 = {};
         uint32_t vmask = 0;
         float tv[2][4];
@@ -666,19 +657,13 @@ smla_attn_kernel(KParams p) {
         if (have) {
           vmask = (uint32_t)__ballot(l < 32 && idx_cur >= 0);
           seen = seen || vmask != 0;
-          scores(i, r0, r1);
+          if constexpr (F8) scores8(i, r0, r1);
+          else scores(i, r0, r1);
           if (!full || i == 0) scaled(r0, r1, vmask, tv, mx);
         }
-        auto convert_next = [&]() {                        // this wave's share of tile i+1
-          if (F8 && i + 1 < ntiles) {
-            if (i + 2 < ntiles) wait_vmcnt<S::NDMA_S>(); else wait_vmcnt<0>();
-            convert_tile_s(i + 1);
-          }
-        };
         if (!full) {
           mx_all[0] = fmaxf(mx_all[0], mx[0]);
           mx_all[1] = fmaxf(mx_all[1], mx[1]);
-          convert_next();
           lds_barrier();
           continue;
         }
@@ -731,22 +716,21 @@ smla_attn_kernel(KParams p) {
           // end of the pass: 2^64 bounds every p while the reference holds
           if (!(l_lane[0] <= kRefLimit) || !(l_lane[1] <= kRefLimit) || (seen && m_ref[0] == -INFINITY)) s_flag = 1;
         }
-        convert_next();
         lds_barrier();
       }
     };
 
     for (int attempt = 0; attempt < 2; attempt++) {
       float unused[2] = {-INFINITY, -INFINITY};
-      if (p.softcap_on) s_pass(std::true_type{}, true, unused, attempt == 0);
-      else s_pass(std::false_type{}, true, unused, attempt == 0);
+      if (p.softcap_on) s_pass(std::true_type{}, true, unused);
+      else s_pass(std::false_type{}, true, unused);
       // uniform (after the pass's last barrier). A pass with the exact maximum
       // is only flagged by a NaN or infinite score: that result stands (NaN
       // propagates to the output and LSE)
       if (!s_flag || attempt == 1) break;
       // exact per-head maximum, then the full pass again
       float mx_all[2] = {-INFINITY, -INFINITY};
-      s_pass(std::false_type{}, false, mx_all, false);
+      s_pass(std::false_type{}, false, mx_all);
       wg_max(mx_all);
       m_ref[0] = cap2(mx_all[0]);
       m_ref[1] = cap2(mx_all[1]);
@@ -807,12 +791,16 @@ smla_attn_kernel(KParams p) {
     lds_barrier();                                         // E3: O staged
   } else {
     // ======================================================================
-    // O-waves: tile copies (and FP8 conversion), P.V
+    // O-waves: tile copies, P.V
     // ======================================================================
-    // V transposing reads (B operand of P.V): in 16-lane group lg, lane li = 4e + q
-    // reads row 4lg + e (then 16 + 4lg + e), channels 128w + 16nb + 4q .. +3,
-    // at vbase[half][nb & 3] + 4096 (nb >> 2).
-    int vbase[2][4];
+    // bf16 V transposing reads (B operand of P.V): in 16-lane group lg, lane
+    // li = 4e + q reads row 4lg + e (then 16 + 4lg + e), channels 128w + 16nb +
+    // 4q .. +3, at vbase[half][nb & 3] + 4096 (nb >> 2).
+    // FP8 V transposing reads: lane li = 2e + q reads row 4lg + e (e < 4) or
+    // 12 + 4lg + e (e >= 4), codes 128w + 16nb + 8q .. +7, at vb8[nb]; lane li
+    // then holds channel 128w + 16nb + li of the 8 rows, in the P operand's
+    // row order.
+    int vbase[2][4], vb8[8];
     {
       const int e = li >> 2, q4 = li & 3;
 #pragma unroll
@@ -820,6 +808,10 @@ smla_attn_kernel(KParams p) {
 #pragma unroll
         for (int j = 0; j < 4; j++)
           vbase[half][j] = tile_pos(16 * half + 4 * lg + e, 16 * wr + 2 * j + (q4 >> 1)) + 8 * (q4 & 1);
+      const int e8 = li >> 1, q2 = li & 1;
+      const int vr8 = e8 < 4 ? 4 * lg + e8 : 12 + 4 * lg + e8;
+#pragma unroll
+      for (int nb = 0; nb < 8; nb++) vb8[nb] = tile_pos8(vr8, 8 * wr + nb) + 8 * q2;
     }
 
     f32x4 O[4][8];
@@ -837,15 +829,6 @@ smla_attn_kernel(KParams p) {
       bf16x8 pa[4];
 #pragma unroll
       for (int mb = 0; mb < 4; mb++) pa[mb] = lds_ld128(pb + (mb * 64 + l) * 16);
-      if constexpr (S::GROUP) {
-        // wave w's channels are group w: P[h][j] * scale[j][w] (elements 0..3 of
-        // the operand are rows 4lg .. 4lg+3, elements 4..7 rows 16+4lg .. 16+4lg+3)
-        const lds_char* rw = rsc_buf(i) + 4 * (wr * kTileRows + 4 * lg);
-        const f32x4 sa = *(const __attribute__((address_space(3))) f32x4*)rw;
-        const f32x4 sb = *(const __attribute__((address_space(3))) f32x4*)(rw + 64);
-#pragma unroll
-        for (int mb = 0; mb < 4; mb++) pa[mb] = scale_bf16x8(pa[mb], sa, sb);
-      }
 #pragma unroll
       for (int nb = 0; nb < 8; nb++) {
         const s16x4 v0 = vr[nb % (VPF + 1)][0];
@@ -862,53 +845,73 @@ smla_attn_kernel(KParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     };
+    // FP8: 8 codes per lane per n-block, converted one n-block ahead of its MFMAs
+    auto pv8 = [&](int i) {
+      const lds_char* tb = tile8(i);
+      const lds_char* pb = pbuf + (i & 1) * (4 * 64 * 16);
+      constexpr int VPF = 3;                                // V reads kept in flight (n-blocks)
+      // the scales and P are read before the V read-ahead, so that scaling P
+      // waits only for them (LDS reads return in order)
+      [[maybe_unused]] f32x4 sa, sb;
+      if constexpr (S::GROUP) {
+        const lds_char* rw = tb + S::SC_AT + 4 * (wr * kTileRows + 4 * lg);
+        sa = *(const __attribute__((address_space(3))) f32x4*)rw;
+        sb = *(const __attribute__((address_space(3))) f32x4*)(rw + 64);
+      }
+      bf16x8 pa[4];
+#pragma unroll
+      for (int mb = 0; mb < 4; mb++) pa[mb] = lds_ld128(pb + (mb * 64 + l) * 16);
+      i32x2 vr[VPF];
+#pragma unroll
+      for (int nb = 0; nb < VPF; nb++) vr[nb] = lds_read_tr8(tb + vb8[nb]);
+      if constexpr (S::GROUP) {
+        // wave w's channels are group w: P[h][j] * scale[j][w] (elements 0..3 of
+        // the operand are rows 4lg .. 4lg+3, elements 4..7 rows 16+4lg .. 16+4lg+3)
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) pa[mb] = scale_bf16x8(pa[mb], sa, sb);
+      }
+      bf16x8 cv = e4m3x8_to_bf16x8((uint32_t)vr[0][0], (uint32_t)vr[0][1]);
+#pragma unroll
+      for (int nb = 0; nb < 8; nb++) {
+        const bf16x8 bv = cv;
+        if (nb + VPF < 8) vr[nb % VPF] = lds_read_tr8(tb + vb8[nb + VPF]);
+        if (nb + 1 < 8) cv = e4m3x8_to_bf16x8((uint32_t)vr[(nb + 1) % VPF][0], (uint32_t)vr[(nb + 1) % VPF][1]);
+#pragma unroll
+        for (int mb = 0; mb < 4; mb++) O[mb][nb] = mfma16x16x32(pa[mb], bv, O[mb][nb]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
 
-    // one pass over the tiles, the same barriers as s_pass. Tiles 0 and 1 are
-    // copied (and tile 0 converted) before the pass's first barrier.
+    // one pass over the tiles, the same barriers as s_pass. Tiles 0 .. PD-1
+    // are copied before the pass (in the prologue for the first pass).
     auto o_pass = [&](const bool full, const bool issued) {
 #pragma unroll
       for (int mb = 0; mb < 4; mb++)
 #pragma unroll
         for (int nb = 0; nb < 8; nb++) O[mb][nb] = (f32x4){};
       if (!issued) {
-        if (ntiles > 0) issue_tile_o(0);
-        if (ntiles > 1) issue_tile_o(1);
+        for (int k = 0; k < PD; k++)
+          if (k < ntiles) issue_tile_o(k);
       }
-      if (ntiles > 0) {
-        if (ntiles > 1) wait_vmcnt<S::NDMA_O>(); else wait_vmcnt<0>();   // tile 0 has landed
-        convert_tile_o(0);
-      }
+      if (ntiles > 0) wait_tile(0);
       lds_barrier();                                       // pass start
       for (int i = 0; i <= ntiles; i++) {
-        if (i + 2 < ntiles) issue_tile_o(i + 2);
+        if (i + PD < ntiles) issue_tile_o(i + PD);
         if (full && i == 0) lds_barrier();                 // matches the S-waves' reference exchange
-        auto convert_next = [&]() {
-          if (i + 1 < ntiles) {
-            if (i + 2 < ntiles) wait_vmcnt<S::NDMA_O>(); else wait_vmcnt<0>();   // tile i+1 has landed
-            convert_tile_o(i + 1);
-          }
-        };
-        if constexpr (F8 && !S::GROUP) {
-          // per-tensor FP8: convert first (VALU while the S-waves' QK^T holds the
-          // matrix core), then P.V beside their softmax: -3.5% on the NoPE decode;
-          // with group scales (more VALU in P.V) the other order is faster
-          convert_next();
-          if (full && i >= 1) pv(i - 1);
-        } else {
-          if (full && i >= 1) pv(i - 1);
-          convert_next();
+        if (full && i >= 1) {
+          if constexpr (F8) pv8(i - 1);
+          else pv(i - 1);
         }
+        if (i + 1 < ntiles) wait_tile(i + 1);              // tile i+1 has landed
         lds_barrier();
       }
     };
 
-    if constexpr (!F8) {
-      if (ntiles > 0) issue_tile_o(0);
-      if (ntiles > 1) issue_tile_o(1);
-      lds_barrier();                                       // matches the S-waves' Q exchange
-    }
+    for (int k = 0; k < PD; k++)
+      if (k < ntiles) issue_tile_o(k);
+    if constexpr (!F8) lds_barrier();                      // matches the S-waves' Q exchange
     for (int attempt = 0; attempt < 2; attempt++) {
-      o_pass(true, !F8 && attempt == 0);
+      o_pass(true, attempt == 0);
       if (!s_flag || attempt == 1) break;                  // uniform (after the pass's last barrier)
       o_pass(false, false);
       lds_barrier();                                       // matches the S-waves' final maximum exchange
@@ -917,12 +920,13 @@ smla_attn_kernel(KParams p) {
     // ---- epilogue (O side)
     lds_barrier();                                         // E1: row sums written
     lds_barrier();                                         // E2: inverse sums written
-    // Stage the normalised O block [64 heads][512 ch] as bf16 in latent buffers
-    // 0-1 (idle now), then all waves write whole 16-byte chunks. O lane layout:
-    // m-block mb, n-block nb: head 16mb + 4lg + r, channel 128w + 16nb + li. Two
-    // heads of one channel are rounded together (v_cvt_pk_bf16_f32). Staged row
-    // h, byte b sits at h*1024 + (b ^ (((h >> 2) & 3) << 5)): the 4 head groups
-    // of one store instruction fall in different banks.
+    // Stage the normalised O block [64 heads][512 ch] as bf16 in the first
+    // 64 KB of the latent ring (idle now), then all waves write whole 16-byte
+    // chunks. O lane layout: m-block mb, n-block nb: head 16mb + 4lg + r,
+    // channel 128w + 16nb + li. Two heads of one channel are rounded together
+    // (v_cvt_pk_bf16_f32). Staged row h, byte b sits at h*1024 + (b ^ (((h >>
+    // 2) & 3) << 5)): the 4 head groups of one store instruction fall in
+    // different banks.
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 #pragma unroll

@@ -80,6 +80,44 @@ __device__ __forceinline__ int tile_pos(int r, int c) {
   return (4 * (c >> 3) + (r >> 3)) * 1024 + ((r & 7) * 8 + ((c & 7) ^ swz(r))) * 16;
 }
 
+// FP8 tile layout (32 rows x 32 chunks of 16 E4M3 codes, 16 KB): block
+// 4s + g (1 KB) holds segment s (chunks 8s..8s+7) of rows 8g..8g+7, and row
+// r's chunk 8s + cc sits at ((r & 7) * 8 + (cc ^ swz8(r))) * 16 inside it, so
+// one 64-lane global->LDS copy fills a block from 8 whole 128-byte lines.
+// swz8 takes bits 1-2 from (r >> 2) & 3, as swz does, and bit 0 from
+// (r >> 4) & 1. In the 512-byte LDS model above, the K reads of QK^T
+// (ds_read_b128, 16 rows x 2 adjacent chunks per 32 lanes) fall in 32 distinct
+// 16-byte groups: the 4 rows of the 16 that share r & 3 differ in bits 1-2,
+// and the two chunks of a pair differ in bit 0. The transposing V reads
+// (ds_read_b64_tr_b8, all 32 rows x one chunk per 64 lanes) do too: the 8 rows
+// that share r & 3 get 8 different values.
+__device__ __forceinline__ int swz8(int r) {
+  return (((r >> 2) & 3) << 1) | ((r >> 4) & 1);
+}
+__device__ __forceinline__ int tile_pos8(int r, int c) {
+  return (4 * (c >> 3) + (r >> 3)) * 1024 + ((r & 7) * 8 + ((c & 7) ^ swz8(r))) * 16;
+}
+
+typedef int32_t i32x2 __attribute__((ext_vector_type(2)));
+// Transposing 8-bit LDS read: within each 16-lane group, output lane j gets
+// byte (j % 8) of the 8-byte words addressed by source lanes 2*i + j/8,
+// i = 0..7, as its byte i (checked with a GPU probe of the instruction).
+__device__ __forceinline__ i32x2 lds_read_tr8(const lds_char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 __attribute__((address_space(3)))*)p);
+}
+
+// 8 OCP E4M3FN codes (byte e of the two dwords w0, w1 is element e) -> 8 bf16
+// values, exact (every E4M3FN value, NaN included, is a bf16 value): one
+// v_cvt_scalef32_pk_bf16_fp8 at scale 1.0 per pair.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const u32x4 o = {
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, true)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, false)),
+      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w1, 1.0f, true))};
+  return __builtin_bit_cast(bf16x8, o);
+}
+
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
 // operations, not for its outstanding global loads (the tile DMAs stay in
 // flight across it; their completion is waited for with wait_vmcnt).
