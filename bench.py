@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import sys
 import time
@@ -118,7 +119,8 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(w, gidx_np, valid_np, min_seconds: float, k_scale: float, softcap: float = 0.0, sinks=None):
+def cpu_baseline(w, gidx_np, valid_np, min_seconds: float, k_scale: float, softcap: float = 0.0, sinks=None,
+                 q_scale: float = 1.0):
     """The fp64 oracle on the host over a sample of the workload's tokens. FP8
     workloads: the rows the sample reads are quantised by the oracle's own
     quantiser (untimed set-up, as the cache write is untimed on the GPU)."""
@@ -128,7 +130,7 @@ def cpu_baseline(w, gidx_np, valid_np, min_seconds: float, k_scale: float, softc
 
     from oracle import sparse_mla as O
     spec = w.spec
-    qf = O.bf16_bits_to_f64(w.q.cpu().view(torch.int16).numpy().view(np.uint16))
+    qf = O.bf16_bits_to_f64(w.q.cpu().view(torch.int16).numpy().view(np.uint16)) * q_scale
     tokens = np.arange(spec.num_tokens)
     if spec.num_tokens > 64:           # a strided sample of tokens, long rows included
         tokens = np.linspace(spec.num_tokens - 1, 0, 64).astype(int)
@@ -226,6 +228,10 @@ def parse_args(argv=None):
                          "upconvert each request's context to a bf16 workspace first and run the bf16 kernel on it")
     ap.add_argument("--softcap", type=float, default=0.0, help="logit softcap c (c tanh(z / c)); 0 = off")
     ap.add_argument("--sinks", action="store_true", help="one sink logit per head (drawn N(0,1), seeded)")
+    ap.add_argument("--q-scale", type=float, default=1.0,
+                    help="multiply Q by this power of two (exact in bf16): a large factor spreads the logits "
+                         "beyond the 2^64 range of the per-head reference, so the kernel takes its exact-maximum "
+                         "rerun; 1 = the workload as drawn")
     ap.add_argument("--separate-convert", action="store_true",
                     help="run smla_convert_indices as its own kernel in the step instead of in the attention kernel")
     return ap.parse_args(argv)
@@ -239,6 +245,12 @@ def main() -> int:
         return 2
     if args.steps < 1:
         print("--steps must be >= 1", file=sys.stderr)
+        return 2
+    if not (args.q_scale > 0 and math.frexp(args.q_scale)[0] == 0.5):
+        print("--q-scale must be a power of two (the scaled Q stays exact in bf16)", file=sys.stderr)
+        return 2
+    if args.q_scale != 1.0 and args.dcp > 1:
+        print("--q-scale applies to the single-rank workloads only", file=sys.stderr)
         return 2
 
     import torch
@@ -300,7 +312,7 @@ def measure(name: str, args) -> dict:
     w = I.generate(spec, kv_device=dev)
     R = max(1, min(args.rotate, args.steps))
     caches, gscales, kscales = build_caches(spec, w, R, dev)
-    q = w.q.to(dev)
+    q = w.q.to(dev) * args.q_scale
     qn, qr = q[..., :512], (q[..., 512:] if spec.d_rope else None)
     req, bt, loc = w.req_id.to(dev), w.block_table.to(dev), w.topk_local.to(dev)
     T, H, K = spec.num_tokens, spec.heads, spec.topk
@@ -451,13 +463,13 @@ def measure(name: str, args) -> dict:
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, gidx_np, vcnt_np, args.cpu_seconds, kscales[0], args.softcap,
-                           None if sinks is None else sinks.cpu().numpy().astype("float64"))
+                           None if sinks is None else sinks.cpu().numpy().astype("float64"), args.q_scale)
 
     config = {"workload": WORKLOAD_TEXT[name], "name": name, "num_tokens": T, "heads": H,
               "topk": K, "entry": f"smla_{entry}_fwd", "splits": splits, "cache_copies_rotated": R,
               "kv_storage": KV_STORAGE[spec.kv_format],
               "index_conversion": "separate kernel" if args.separate_convert else "in the attention kernel",
-              "softcap": args.softcap, "sinks": bool(args.sinks),
+              "softcap": args.softcap, "sinks": bool(args.sinks), "q_scale": args.q_scale,
               "fp8_prefill": (args.fp8_prefill if entry == "prefill" and spec.kv_format == I.KV_FP8_DS_MLA
                               else None),
               "timing": "HIP graphs of exactly `steps` steps replayed; cold L2/MALL by cache rotation"}
