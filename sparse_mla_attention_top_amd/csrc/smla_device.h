@@ -12,12 +12,9 @@ namespace smla {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) char lds_char;
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
 template <typename F, int... I>
@@ -29,12 +26,7 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-constexpr int kWave = 64;
 constexpr int kDLatent = 512;
-
-__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // Transposing LDS read: within each 16-lane group, output lane j gets element
 // (j % 4) of the 8-byte words addressed by source lanes 4*i + j/4, i = 0..3.
@@ -50,12 +42,6 @@ __device__ __forceinline__ bf16x8 concat_bf16x4(s16x4 lo, s16x4 hi) {
   const bf16x4 a = __builtin_bit_cast(bf16x4, lo);
   const bf16x4 b = __builtin_bit_cast(bf16x4, hi);
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-__device__ __forceinline__ float wave_xor32_max(float v) {
-  // exchange with lane ^ 32 (the other half of the wavefront)
-  float o = __shfl_xor(v, 32, 64);
-  return fmaxf(v, o);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -108,7 +94,8 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const lds_char* p) {
 
 // 8 OCP E4M3FN codes (byte e of the two dwords w0, w1 is element e) -> 8 bf16
 // values, exact (every E4M3FN value, NaN included, is a bf16 value): one
-// v_cvt_scalef32_pk_bf16_fp8 at scale 1.0 per pair.
+// v_cvt_scalef32_pk_bf16_fp8 at scale 1.0 per pair (a GPU probe matched the
+// format's definition on all 256 codes in both halves of the dword).
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   const u32x4 o = {
       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w0, 1.0f, false)),
@@ -148,41 +135,6 @@ __device__ __forceinline__ void dma_4b(const void* gptr, uint32_t lds_base) {
                :
                : "v"(gptr), "s"(lds_base)
                : "m0", "memory");
-}
-
-// 16 OCP E4M3FN bytes (little-endian in 4 dwords, channel c = byte c) -> 16
-// bf16 values: channels 0..7 in lo, 8..15 in hi, two per dword (low half =
-// lower channel). v_cvt_pk_f32_fp8 decodes E4M3FN exactly on gfx950 (all 256
-// codes, NaN included) and every E4M3FN value is exact in bf16, so without a
-// scale the result is exact; SCALED = true multiplies by `scale` in fp32 and
-// rounds to bf16 to nearest-even. The pairs go through a vector float->bf16
-// conversion: reinterpreting the two decoded floats as integers to take their
-// high halves was compiled with element 0 read in place of element 1.
-//
-// Unscaled, each pair takes one v_cvt_scalef32_pk_bf16_fp8 with scale 1.0
-// (E4M3FN -> bf16 directly; a GPU probe matched the format's definition on
-// all 256 codes in both halves of the dword).
-template <bool SCALED>
-__device__ __forceinline__ void e4m3x16_to_bf16(u32x4 raw, float scale, u32x4& lo, u32x4& hi) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  uint32_t outw[8];
-#pragma unroll
-  for (int d = 0; d < 4; d++) {
-    if constexpr (SCALED) {
-      f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[d], false);
-      f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[d], true);
-      a = a * scale;
-      b = b * scale;
-      outw[2 * d] = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2));
-      outw[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2));
-    } else {
-      outw[2 * d] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[d], 1.0f, false));
-      outw[2 * d + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)raw[d], 1.0f, true));
-    }
-  }
-  lo = (u32x4){outw[0], outw[1], outw[2], outw[3]};
-  hi = (u32x4){outw[4], outw[5], outw[6], outw[7]};
 }
 
 // x[i] * sa[i] (i < 4) and x[i] * sb[i - 4] (i >= 4), in fp32, rounded to
