@@ -46,39 +46,35 @@ __device__ __forceinline__ bf16x8 concat_bf16x4(s16x4 lo, s16x4 hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 3-bit swizzle of a tile row: bits 1-2 from (r >> 2) & 3, bit 0 from (r >> 1) & 1.
-__device__ __forceinline__ int swz(int r) {
-  return (((r >> 2) & 3) << 1) | ((r >> 1) & 1);
-}
-
 // Staged cache tile layout (32 rows x NC 16-byte chunks, NC = 8 x segments of
 // 128 bytes). Block 4s + g (1 KB) holds segment s of rows 8g..8g+7; inside
 // it row r's chunk 8s + cc sits at ((r & 7) * 8 + (cc ^ swz(r))) * 16. So a
 // 64-lane global->LDS copy fills one block from 8 whole 128-byte lines (lane
-// l: row 8g + l/8). LDS on gfx950 serves 512 bytes (128 banks) per cycle, 32
-// lanes of a 16-byte read at a time: the K reads (16 rows x 2 adjacent chunks
-// per 32 lanes) fall in 32 distinct 16-byte groups, because the 4 rows that
-// share (r & 3) -- 128 bytes apart -- get 4 different values of swz >> 1, and
-// the two chunks of a pair differ in bit 0. The transposing V reads (4 rows x
-// 2 chunks per 16 lanes) are conflict-free too. (Bit-reversing (r >> 1) & 7
-// instead left the K reads 2-way conflicted: measured with SQ_LDS_BANK_CONFLICT.)
+// l: row 8g + l/8). The swizzle is chosen by measurement (SQ_LDS_BANK_CONFLICT
+// of a probe kernel per access pattern, same addressing as the kernel):
+// swz(r) = r & 6 leaves both the K reads of QK^T (ds_read_b128, rows 16rh +
+// li, chunks 4j + lg) and the transposing V reads of P.V (ds_read_b64_tr_b16)
+// free of bank conflicts. The earlier ((r >> 2) & 3) << 1 | ((r >> 1) & 1)
+// was conflict-free for K but 2-way for V. For the 8-byte reads the counts
+// match a model in which 32 lanes are served per cycle from 256 bytes (64
+// four-byte banks); the 16-byte reads follow no simple model, hence the probe.
+__device__ __forceinline__ int swz(int r) { return r & 6; }
 __device__ __forceinline__ int tile_pos(int r, int c) {
   return (4 * (c >> 3) + (r >> 3)) * 1024 + ((r & 7) * 8 + ((c & 7) ^ swz(r))) * 16;
 }
 
-// FP8 tile layout (32 rows x 32 chunks of 16 E4M3 codes, 16 KB): block
-// 4s + g (1 KB) holds segment s (chunks 8s..8s+7) of rows 8g..8g+7, and row
-// r's chunk 8s + cc sits at ((r & 7) * 8 + (cc ^ swz8(r))) * 16 inside it, so
-// one 64-lane global->LDS copy fills a block from 8 whole 128-byte lines.
-// swz8 takes bits 1-2 from (r >> 2) & 3, as swz does, and bit 0 from
-// (r >> 4) & 1. In the 512-byte LDS model above, the K reads of QK^T
-// (ds_read_b128, 16 rows x 2 adjacent chunks per 32 lanes) fall in 32 distinct
-// 16-byte groups: the 4 rows of the 16 that share r & 3 differ in bits 1-2,
-// and the two chunks of a pair differ in bit 0. The transposing V reads
-// (ds_read_b64_tr_b8, all 32 rows x one chunk per 64 lanes) do too: the 8 rows
-// that share r & 3 get 8 different values.
+// FP8 tile layout (32 rows x 32 chunks of 16 E4M3 codes, 16 KB): the bf16
+// layout at half the bytes, block 4s + g (1 KB) for segment s (chunks
+// 8s..8s+7) of rows 8g..8g+7, row r's chunk 8s + cc at ((r & 7) * 8 + (cc ^
+// swz8(r))) * 16 inside it. swz8(r) = (((r >> 2) & 3) << 1 | ((r >> 1) & 1)) ^
+// (((r >> 4) & 1) << 2), measured free of bank conflicts for the K reads
+// (within a wave, rows 16rh..16rh+15: bit 4 is fixed, so the pattern is a
+// relabelling of chunks of the bf16-style swizzle whose K reads are
+// conflict-free) and for the 8-bit transposing V reads of all 32 rows, where
+// bit 4 separates rows r and r + 16. (Taking bit 0 from row bit 4 instead left
+// both 2-way conflicted.)
 __device__ __forceinline__ int swz8(int r) {
-  return (((r >> 2) & 3) << 1) | ((r >> 4) & 1);
+  return ((((r >> 2) & 3) << 1) | ((r >> 1) & 1)) ^ (((r >> 4) & 1) << 2);
 }
 __device__ __forceinline__ int tile_pos8(int r, int c) {
   return (4 * (c >> 3) + (r >> 3)) * 1024 + ((r & 7) * 8 + ((c & 7) ^ swz8(r))) * 16;
