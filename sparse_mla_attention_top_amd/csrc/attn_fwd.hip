@@ -100,8 +100,9 @@ __device__ __forceinline__ float sum_bf16x2(uint32_t v, float acc) {
 // per-head reference m (base-2 units) fixed at the first tile; p = 2^(t - m)
 // stays finite in bf16/fp32 while t - m <= 64. If a row sum of a pass exceeds
 // 2^64 (so some later score may exceed m + 64) or is not finite, the workgroup
-// restarts: a max-only pass finds the exact per-head maximum, then the full
-// pass runs with it.
+// restarts with a new reference: m + log2 of the pass's largest per-lane row
+// sum (at most 8 above the exact maximum), or, if that sum is not
+// finite or zero, the exact maximum from a max-only pass.
 constexpr float kRefLimit = 18446744073709551616.0f;    // 2^64
 constexpr int kLatKS = kDLatent / 32;                  // k-steps over the 512 latent channels
 constexpr int kLatBytes = kTileRows * kDLatent * 2;    // bf16 latent part of a tile (32 KB)
@@ -169,6 +170,7 @@ smla_attn_kernel(KParams p) {
   __shared__ __attribute__((aligned(16))) char s_p[2 * 4 * 64 * 16];   // P(i) in block i & 1, [mblock][lane]
   __shared__ int s_idx[kMaxTopk];
   __shared__ int s_flag;
+  __shared__ int s_need;    // a flagged pass's own maxima are not usable: a max-only pass is needed
   __shared__ int s_last[8];
 
   lds_char* lat = (lds_char*)s_lat;
@@ -258,7 +260,10 @@ smla_attn_kernel(KParams p) {
   }
   for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
   if (l == 0) s_last[w] = last;
-  if (threadIdx.x == 0) s_flag = 0;
+  if (threadIdx.x == 0) {
+    s_flag = 0;
+    s_need = 0;
+  }
   lds_barrier();
   int nlast = 0;
 #pragma unroll
@@ -495,9 +500,9 @@ smla_attn_kernel(KParams p) {
     //     reuses their sets, so that the fold's VALU reads wait as little as
     //     possible for MFMA results. These reads are still the group formats'
     //     main cost: with the folds left out (timing only) the QK^T of the
-    //     long-context tile took half as long. The scales of group g are read
-    //     at its first pair and used a group later (LDS reads return in order:
-    //     waiting for them does not wait for the code reads issued after them).
+    //     long-context tile took half as long. A fold's scales are read at the
+    //     start of its iteration, before that iteration's code read (LDS reads
+    //     return in order: waiting for them does not wait for the code read).
     auto scores8 = [&](int i, f32x4& r0, f32x4& r1) {
       const lds_char* tb = tile8(i);
       constexpr int NP = kLatKS / 2 + (S::ROPE8 ? 1 : 0);  // k-pairs held as codes
@@ -509,19 +514,16 @@ smla_attn_kernel(KParams p) {
       f32x4 acc[4][2] = {};
       f32x4 t0 = {}, t1 = {};
       [[maybe_unused]] const lds_char* rs = tb + S::SC_AT + 4 * (16 * rh + 4 * lg);   // [group][row] scales
-      [[maybe_unused]] f32x4 gs[2];
       auto read_scales = [&](int g) -> f32x4 { return *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * g); };
-      // fold the sums of group g (sets 2 (g & 1), +1) into t0 / t1 and clear them
-      auto fold = [&](auto g_c) {
+      // fold the sums of group g (sets 2 (g & 1), +1), scaled by gsc, into t0 / t1 and clear them
+      auto fold = [&](auto g_c, const f32x4 gsc) {
         constexpr int g = decltype(g_c)::value, c = 2 * (g & 1);
-        const f32x4 gsc = gs[g & 1];
         t0 += gsc * (acc[c][0] + acc[c + 1][0]);
         t1 += gsc * (acc[c][1] + acc[c + 1][1]);
         acc[c][0] = acc[c][1] = acc[c + 1][0] = acc[c + 1][1] = (f32x4){};
       };
       constexpr int PF = S::GROUP ? 2 : 3;        // code reads kept in flight
       u32x4 a[PF];
-      if constexpr (S::GROUP) gs[0] = read_scales(0);
       [[maybe_unused]] bf16x8 k0, k1;
       if constexpr (S::PACKED) {                   // the bf16 rope part's two k-steps
         k0 = lds_ld128(tb + S::ROPE_AT + kbase[0]);
@@ -553,7 +555,9 @@ smla_attn_kernel(KParams p) {
           chi = e4m3x8_to_bf16x8(cu[2], cu[3]);
         }
         const bf16x8 lo = clo, hi = chi;
-        if constexpr (S::GROUP && (j & 1) == 0 && j > 0) gs[(j / 2) & 1] = read_scales(j / 2);
+        constexpr bool FOLD = S::GROUP && (j & 1) == 1 && j >= 3;   // group (j - 3) / 2 is folded here
+        [[maybe_unused]] f32x4 gsc;
+        if constexpr (FOLD) gsc = read_scales((j - 3) / 2);
         if constexpr (j + PF < NP)
           a[j % PF] = *(const __attribute__((address_space(3))) u32x4*)kaddr(std::integral_constant<int, j + PF>{});
         if constexpr (AHEAD && j + 1 < NP) {
@@ -565,7 +569,7 @@ smla_attn_kernel(KParams p) {
         acc[c][1] = mfma16x16x32(lo, q[1][2 * j], acc[c][1]);
         acc[c + 1][0] = mfma16x16x32(hi, q[0][2 * j + 1], acc[c + 1][0]);
         acc[c + 1][1] = mfma16x16x32(hi, q[1][2 * j + 1], acc[c + 1][1]);
-        if constexpr (S::GROUP && (j & 1) == 1 && j >= 3) fold(std::integral_constant<int, (j - 3) / 2>{});
+        if constexpr (FOLD) fold(std::integral_constant<int, (j - 3) / 2>{}, gsc);
         __builtin_amdgcn_sched_barrier(0);
       });
       if constexpr (S::GROUP) {
@@ -573,7 +577,10 @@ smla_attn_kernel(KParams p) {
         // latent group 3, the rope part is bf16)
         constexpr int GL = S::PACKED ? 3 : (QKS - 1) / 4;
         constexpr int G0 = NP >= 3 ? (NP - 3) / 2 + ((NP - 3) % 2 ? 1 : 0) : 0;   // first group without an in-loop fold
-        static_for<GL - G0 + 1>([&](auto k_c) { fold(std::integral_constant<int, G0 + decltype(k_c)::value>{}); });
+        static_for<GL - G0 + 1>([&](auto k_c) {
+          constexpr int g = G0 + decltype(k_c)::value;
+          fold(std::integral_constant<int, g>{}, read_scales(g));
+        });
         r0 = t0;
         r1 = t1;
       } else {
@@ -724,16 +731,38 @@ smla_attn_kernel(KParams p) {
       float unused[2] = {-INFINITY, -INFINITY};
       if (p.softcap_on) s_pass(std::true_type{}, true, unused);
       else s_pass(std::false_type{}, true, unused);
-      // uniform (after the pass's last barrier). A pass with the exact maximum
-      // is only flagged by a NaN or infinite score: that result stands (NaN
-      // propagates to the output and LSE)
+      // uniform (after the pass's last barrier). The rerun's reference is at
+      // or above every score, so it is only flagged by a NaN or infinite
+      // score: that result stands (NaN propagates to the output and LSE)
       if (!s_flag || attempt == 1) break;
-      // exact per-head maximum, then the full pass again
-      float mx_all[2] = {-INFINITY, -INFINITY};
-      s_pass(std::false_type{}, false, mx_all);
-      wg_max(mx_all);
-      m_ref[0] = cap2(mx_all[0]);
-      m_ref[1] = cap2(mx_all[1]);
+      // a new per-head reference, then the full pass again. The largest
+      // per-lane row sum L of the flagged pass lies between its largest p and
+      // 256 times it (a lane sums 4 of each tile's 32 entries, of at most
+      // 2048), so with m + log2(L) every p of the rerun is at most 1 and the
+      // largest is at least 2^-8 (the scores are already capped). Unless some L is 0,
+      // infinite or NaN: then a max-only pass finds the exact maximum.
+      // Barriers: the exchange and the decision, which the O-waves match.
+      float pmx[2] = {l_lane[0], l_lane[1]};
+      wg_max(pmx);
+      float m_new[2];
+      bool usable = true;
+#pragma unroll
+      for (int nbq = 0; nbq < 2; nbq++) {
+        usable = usable && pmx[nbq] > 0.0f && pmx[nbq] <= 3.4028234663852886e38f;
+        m_new[nbq] = (m_ref[nbq] == -INFINITY ? 0.0f : m_ref[nbq]) + log2f(pmx[nbq]);
+      }
+      if (!usable) s_need = 1;
+      lds_barrier();
+      if (s_need) {                                        // uniform (after the barrier)
+        float mx_all[2] = {-INFINITY, -INFINITY};
+        s_pass(std::false_type{}, false, mx_all);
+        wg_max(mx_all);
+        m_ref[0] = cap2(mx_all[0]);
+        m_ref[1] = cap2(mx_all[1]);
+      } else {
+        m_ref[0] = m_new[0];
+        m_ref[1] = m_new[1];
+      }
       if (threadIdx.x == 0) s_flag = 0;
     }
 
@@ -913,8 +942,12 @@ smla_attn_kernel(KParams p) {
     for (int attempt = 0; attempt < 2; attempt++) {
       o_pass(true, attempt == 0);
       if (!s_flag || attempt == 1) break;                  // uniform (after the pass's last barrier)
-      o_pass(false, false);
-      lds_barrier();                                       // matches the S-waves' final maximum exchange
+      lds_barrier();                                       // matches the S-waves' exchange of the pass's maxima
+      lds_barrier();                                       // s_need is written
+      if (s_need) {
+        o_pass(false, false);
+        lds_barrier();                                     // matches the S-waves' final maximum exchange
+      }
     }
 
     // ---- epilogue (O side)

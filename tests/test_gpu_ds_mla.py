@@ -131,12 +131,15 @@ def test_packed_group_scale_spread_and_zero_groups():
         _run(c, cache, 0.05, entry, stress=True)
 
 
-def test_packed_large_logit_jump():
-    say("packed fp8 large logit jump")
+@pytest.mark.parametrize("alpha", [1.2, 4.0])
+def test_packed_large_logit_jump(alpha):
+    """alpha = 1.2: the rerun's reference from the flagged pass's row sums;
+    alpha = 4: p overflows and a max-only pass finds the maximum."""
+    say(f"packed fp8 large logit jump alpha={alpha}")
     c = I.random_case(T=2, h=32, d_rope=64, topk=128, num_slots=256, seed=100)
     for t in range(2):
         s = int(c.indices[t, 100])
-        c.kv_src[s] = (c.q[t, 0].float() * 4.0).to(torch.bfloat16)
+        c.kv_src[s] = (c.q[t, 0].float() * alpha).to(torch.bfloat16)
     cache = _pack(bits(c.kv_src))
     for entry in ("prefill", "decode"):       # a row of 4 q (values to ~16): the stress allowance
         _run(c, cache, 0.1, entry, stress=True)

@@ -167,13 +167,17 @@ def test_fp8_group_scale_spread_and_zero_groups():
         _run_case(O.KV_FP8_GROUP128, c, codes, scales, 1.0, 0.05, entry, stress=True)
 
 
+@pytest.mark.parametrize("alpha", [1.2, 4.0])
 @pytest.mark.parametrize("kv_format", FMTS)
-def test_fp8_large_logit_jump(kv_format):
-    say(f"fp8 large logit jump fmt={kv_format}")
+def test_fp8_large_logit_jump(kv_format, alpha):
+    """alpha = 1.2: a jump of about 90 (base 2), the rerun's reference comes from
+    the flagged pass's row sums; alpha = 4: about 330, p overflows and a
+    max-only pass finds the maximum."""
+    say(f"fp8 large logit jump fmt={kv_format} alpha={alpha}")
     c = I.random_case(T=2, h=32, d_rope=64, topk=128, num_slots=256, seed=61)
     for t in range(2):
         s = int(c.indices[t, 100])
-        c.kv_src[s] = (c.q[t, 0].float() * 4.0).to(torch.bfloat16)
+        c.kv_src[s] = (c.q[t, 0].float() * alpha).to(torch.bfloat16)
     k_scale = I.per_tensor_scale_from_absmax(c.kv_src) if kv_format == O.KV_FP8_PER_TENSOR else 1.0
     codes, scales = _quantize(bits(c.kv_src), kv_format, k_scale)
     for entry in ("prefill", "decode"):       # a row of 4 q (values to ~16): the stress allowance
