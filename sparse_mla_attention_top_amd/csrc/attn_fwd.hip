@@ -505,85 +505,107 @@ smla_attn_kernel(KParams p) {
     //     return in order: waiting for them does not wait for the code read).
     auto scores8 = [&](int i, f32x4& r0, f32x4& r1) {
       const lds_char* tb = tile8(i);
-      constexpr int NP = kLatKS / 2 + (S::ROPE8 ? 1 : 0);  // k-pairs held as codes
       auto kaddr = [&](auto j_c) -> const lds_char* {
         constexpr int j = decltype(j_c)::value;
         if constexpr (j < kLatKS / 2) return tb + kb8[j & 1] + 4096 * (j >> 1);
         else return tb + kr8;
       };
-      f32x4 acc[4][2] = {};
-      f32x4 t0 = {}, t1 = {};
-      [[maybe_unused]] const lds_char* rs = tb + S::SC_AT + 4 * (16 * rh + 4 * lg);   // [group][row] scales
-      auto read_scales = [&](int g) -> f32x4 { return *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * g); };
-      // fold the sums of group g (sets 2 (g & 1), +1), scaled by gsc, into t0 / t1 and clear them
-      auto fold = [&](auto g_c, const f32x4 gsc) {
-        constexpr int g = decltype(g_c)::value, c = 2 * (g & 1);
-        t0 += gsc * (acc[c][0] + acc[c + 1][0]);
-        t1 += gsc * (acc[c][1] + acc[c + 1][1]);
-        acc[c][0] = acc[c][1] = acc[c + 1][0] = acc[c + 1][1] = (f32x4){};
-      };
-      constexpr int PF = S::GROUP ? 2 : 3;        // code reads kept in flight
-      u32x4 a[PF];
-      [[maybe_unused]] bf16x8 k0, k1;
-      if constexpr (S::PACKED) {                   // the bf16 rope part's two k-steps
-        k0 = lds_ld128(tb + S::ROPE_AT + kbase[0]);
-        k1 = lds_ld128(tb + S::ROPE_AT + kbase[1]);
-      }
-      static_for<PF>([&](auto j_c) {
-        a[decltype(j_c)::value] = *(const __attribute__((address_space(3))) u32x4*)kaddr(j_c);
-      });
-      if constexpr (S::PACKED) {                   // unscaled, straight into t0 / t1
-        t0 = mfma16x16x32(k0, q[0][kLatKS], t0);
-        t1 = mfma16x16x32(k0, q[1][kLatKS], t1);
-        t0 = mfma16x16x32(k1, q[0][kLatKS + 1], t0);
-        t1 = mfma16x16x32(k1, q[1][kLatKS + 1], t1);
-      }
-      // per-tensor: pair j+1 is converted during pair j; group formats (8 more
-      // live registers for the deferred folds): each pair at its own start
-      constexpr bool AHEAD = !S::GROUP;
-      bf16x8 clo, chi;
-      if constexpr (AHEAD) {
-        clo = e4m3x8_to_bf16x8(a[0][0], a[0][1]);
-        chi = e4m3x8_to_bf16x8(a[0][2], a[0][3]);
-      }
-      static_for<NP>([&](auto j_c) {
-        constexpr int j = decltype(j_c)::value;
-        constexpr int c = S::GROUP ? 2 * ((j / 2) & 1) : 0;
-        if constexpr (!AHEAD) {
-          const u32x4 cu = a[j % PF];
-          clo = e4m3x8_to_bf16x8(cu[0], cu[1]);
-          chi = e4m3x8_to_bf16x8(cu[2], cu[3]);
-        }
-        const bf16x8 lo = clo, hi = chi;
-        constexpr bool FOLD = S::GROUP && (j & 1) == 1 && j >= 3;   // group (j - 3) / 2 is folded here
-        [[maybe_unused]] f32x4 gsc;
-        if constexpr (FOLD) gsc = read_scales((j - 3) / 2);
-        if constexpr (j + PF < NP)
-          a[j % PF] = *(const __attribute__((address_space(3))) u32x4*)kaddr(std::integral_constant<int, j + PF>{});
-        if constexpr (AHEAD && j + 1 < NP) {
-          const u32x4 nx = a[(j + 1) % PF];
-          clo = e4m3x8_to_bf16x8(nx[0], nx[1]);
-          chi = e4m3x8_to_bf16x8(nx[2], nx[3]);
-        }
-        acc[c][0] = mfma16x16x32(lo, q[0][2 * j], acc[c][0]);
-        acc[c][1] = mfma16x16x32(lo, q[1][2 * j], acc[c][1]);
-        acc[c + 1][0] = mfma16x16x32(hi, q[0][2 * j + 1], acc[c + 1][0]);
-        acc[c + 1][1] = mfma16x16x32(hi, q[1][2 * j + 1], acc[c + 1][1]);
-        if constexpr (FOLD) fold(std::integral_constant<int, (j - 3) / 2>{}, gsc);
-        __builtin_amdgcn_sched_barrier(0);
-      });
+      auto ld_codes = [&](auto j_c) -> u32x4 { return *(const __attribute__((address_space(3))) u32x4*)kaddr(j_c); };
       if constexpr (S::GROUP) {
-        // the groups not folded in the loop, up to the last one (packed rows:
-        // latent group 3, the rope part is bf16)
-        constexpr int GL = S::PACKED ? 3 : (QKS - 1) / 4;
-        constexpr int G0 = NP >= 3 ? (NP - 3) / 2 + ((NP - 3) % 2 ? 1 : 0) : 0;   // first group without an in-loop fold
-        static_for<GL - G0 + 1>([&](auto k_c) {
-          constexpr int g = G0 + decltype(k_c)::value;
-          fold(std::integral_constant<int, g>{}, read_scales(g));
+        // One accumulator per scale group and head block, all kept to the end
+        // of QK^T, then scaled by the rows' group scales and summed: no VALU
+        // waits for MFMA results inside the contraction. The MFMAs go round
+        // the groups: the first k-pair of latent groups 0..3 (pair 2g), low
+        // then high halves; then their second k-pair (2g + 1) with the E4M3
+        // rope part (group 4, one pair) alongside. An accumulator's next MFMA
+        // comes 8 to 10 MFMAs after its last one. Packed rows: the bf16 rope
+        // part's two k-steps, unscaled, come last.
+        constexpr int NG = 4 + (S::ROPE8 ? 1 : 0);       // groups held as codes
+        f32x4 acc[NG][2] = {};
+        u32x4 c0[4], c1[NG];
+        static_for<4>([&](auto g_c) {
+          constexpr int g = decltype(g_c)::value;
+          c0[g] = ld_codes(std::integral_constant<int, 2 * g>{});
         });
-        r0 = t0;
-        r1 = t1;
+        static_for<4>([&](auto g_c) {
+          constexpr int g = decltype(g_c)::value, j = 2 * g;
+          const bf16x8 lo = e4m3x8_to_bf16x8(c0[g][0], c0[g][1]);
+          acc[g][0] = mfma16x16x32(lo, q[0][2 * j], acc[g][0]);
+          acc[g][1] = mfma16x16x32(lo, q[1][2 * j], acc[g][1]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        // high halves; the second k-pairs' codes are read as registers free up
+        static_for<4>([&](auto g_c) {
+          constexpr int g = decltype(g_c)::value, j = 2 * g;
+          const bf16x8 hi = e4m3x8_to_bf16x8(c0[g][2], c0[g][3]);
+          c1[g] = ld_codes(std::integral_constant<int, j + 1>{});
+          if constexpr (g == 3 && NG == 5) c1[4] = ld_codes(std::integral_constant<int, kLatKS / 2>{});
+          acc[g][0] = mfma16x16x32(hi, q[0][2 * j + 1], acc[g][0]);
+          acc[g][1] = mfma16x16x32(hi, q[1][2 * j + 1], acc[g][1]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        auto ks_of = [](int g) { return g < 4 ? 2 * (2 * g + 1) : kLatKS; };   // first k-step of the second pair
+        [[maybe_unused]] bf16x8 k0, k1;
+        static_for<NG>([&](auto g_c) {
+          constexpr int g = decltype(g_c)::value;
+          const bf16x8 lo = e4m3x8_to_bf16x8(c1[g][0], c1[g][1]);
+          if constexpr (S::PACKED && g == 0) {             // the bf16 rope part's two k-steps
+            k0 = lds_ld128(tb + S::ROPE_AT + kbase[0]);
+            k1 = lds_ld128(tb + S::ROPE_AT + kbase[1]);
+          }
+          acc[g][0] = mfma16x16x32(lo, q[0][ks_of(g)], acc[g][0]);
+          acc[g][1] = mfma16x16x32(lo, q[1][ks_of(g)], acc[g][1]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        static_for<NG>([&](auto g_c) {
+          constexpr int g = decltype(g_c)::value;
+          const bf16x8 hi = e4m3x8_to_bf16x8(c1[g][2], c1[g][3]);
+          acc[g][0] = mfma16x16x32(hi, q[0][ks_of(g) + 1], acc[g][0]);
+          acc[g][1] = mfma16x16x32(hi, q[1][ks_of(g) + 1], acc[g][1]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        f32x4 t0 = {}, t1 = {};
+        if constexpr (S::PACKED) {
+          t0 = mfma16x16x32(k0, q[0][kLatKS], t0);
+          t1 = mfma16x16x32(k0, q[1][kLatKS], t1);
+          t0 = mfma16x16x32(k1, q[0][kLatKS + 1], t0);
+          t1 = mfma16x16x32(k1, q[1][kLatKS + 1], t1);
+        }
+        // scale and sum: rows 16rh + 4lg .. +3 of the [group][row] scale block
+        const lds_char* rs = tb + S::SC_AT + 4 * (16 * rh + 4 * lg);
+        f32x4 u0 = {}, u1 = {};
+        static_for<NG>([&](auto g_c) {
+          constexpr int g = decltype(g_c)::value;
+          const f32x4 gsc = *(const __attribute__((address_space(3))) f32x4*)(rs + 4 * kTileRows * g);
+          u0 += gsc * acc[g][0];
+          u1 += gsc * acc[g][1];
+        });
+        r0 = u0 + t0;
+        r1 = u1 + t1;
       } else {
+        // per-tensor: pair j+1 is converted during pair j
+        constexpr int NP = kLatKS / 2 + (S::ROPE8 ? 1 : 0);  // k-pairs held as codes
+        constexpr int PF = 3;                     // code reads kept in flight
+        f32x4 acc[2][2] = {};
+        u32x4 a[PF];
+        static_for<PF>([&](auto j_c) { a[decltype(j_c)::value] = ld_codes(j_c); });
+        bf16x8 clo = e4m3x8_to_bf16x8(a[0][0], a[0][1]);
+        bf16x8 chi = e4m3x8_to_bf16x8(a[0][2], a[0][3]);
+        static_for<NP>([&](auto j_c) {
+          constexpr int j = decltype(j_c)::value;
+          const bf16x8 lo = clo, hi = chi;
+          if constexpr (j + PF < NP) a[j % PF] = ld_codes(std::integral_constant<int, j + PF>{});
+          if constexpr (j + 1 < NP) {
+            const u32x4 nx = a[(j + 1) % PF];
+            clo = e4m3x8_to_bf16x8(nx[0], nx[1]);
+            chi = e4m3x8_to_bf16x8(nx[2], nx[3]);
+          }
+          acc[0][0] = mfma16x16x32(lo, q[0][2 * j], acc[0][0]);
+          acc[0][1] = mfma16x16x32(lo, q[1][2 * j], acc[0][1]);
+          acc[1][0] = mfma16x16x32(hi, q[0][2 * j + 1], acc[1][0]);
+          acc[1][1] = mfma16x16x32(hi, q[1][2 * j + 1], acc[1][1]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
         r0 = acc[0][0] + acc[1][0];
         r1 = acc[0][1] + acc[1][1];
       }
