@@ -698,7 +698,7 @@ smla_attn_kernel(KParams p) {
         }
         if (i == 0) {                                      // the reference: tile 0's maximum
           wg_max(mx);                                      // (its barrier always runs: the O-waves match it)
-          if (!have_ref) {                                 // a rerun keeps the exact maximum
+          if (!have_ref) {                                 // a rerun keeps the reference it was given
             m_ref[0] = cap2(mx[0]);
             m_ref[1] = cap2(mx[1]);
             have_ref = true;
