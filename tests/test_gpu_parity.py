@@ -326,6 +326,28 @@ def test_large_logit_jump_reruns(alpha):
         _run_case(c, 0.1, entry, stress=True)
 
 
+@pytest.mark.parametrize("qmul,softcap", [(20.0, 0.0), (60.0, 0.0), (20.0, 30.0)])
+def test_reruns_over_many_heads(qmul, softcap):
+    """Q scaled up so that many heads' later scores exceed the tile-0 reference
+    by more than 64 (base 2). With Q x 20 about a sixth of the (head, split)
+    pairs jump that far and their row sums stay finite (the rerun takes its
+    reference from them); with Q x 60 most do and many overflow past 2^128
+    (a max-only pass comes first); softcap 30 bounds the logits. Decode with
+    1 and 2 splits and prefill, against the oracle."""
+    say(f"reruns over many heads qmul={qmul} softcap={softcap}")
+    c = I.random_case(T=4, h=64, d_rope=64, topk=512, num_slots=2048, seed=77)
+    c.q = (c.q.float() * qmul).to(torch.bfloat16)
+    q, kv, idx = c.q.to(DEV), c.kv_src.to(DEV), c.indices.to(DEV)
+    ref = oracle_for(c.q, bits(c.kv_src), c.indices.numpy(), 0.07, softcap=softcap)
+    for entry, splits in (("decode", 1), ("decode", 2), ("prefill", 0)):
+        if entry == "decode":
+            out, lse = PU.decode_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, num_splits=splits, softcap=softcap)
+        else:
+            out, lse = PU.prefill_fwd(q[..., :512], q[..., 512:], kv, idx, 0.07, return_lse=True, softcap=softcap)
+        torch.cuda.synchronize()
+        compare(out, lse, ref, f"reruns x{qmul} softcap={softcap} {entry}/{splits}")
+
+
 def test_deterministic_bitwise():
     say("determinism")
     c = I.random_case(T=8, h=128, d_rope=64, topk=512, num_slots=2048, seed=12)
