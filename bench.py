@@ -28,7 +28,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
-WARM_EAGER = 12                 # unmeasured eager steps between the spin kernel and the timed ones
+COVER_MS = 30.0                 # untimed graph work queued ahead of the event-timed eager steps
+SETTLE_MS = 150.0               # untimed graph work before the timed region (the clock settles)
 WORKLOAD_TEXT = {
     "decode_bf16": "sparse MLA decode, bf16 paged cache [4096,64,576]: 32 requests x 8192 context, "
                    "1 query token each, h=128, top-k=2048 all valid, scale 0.0723, out + LSE",
@@ -101,6 +102,45 @@ def hip_elapsed_ms(a, b) -> float:
     if rc != 0:
         raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
     return ms.value
+
+
+def timed_replays(g_full, g_rem, replays: int, R: int, event_window) -> float:
+    """Seconds for `replays` replays of g_full (R steps each) and one of g_rem,
+    timed in two halves, after SETTLE_MS of untimed replays. A GPU coming out
+    of idle runs a kernel fast for a few ms, then up to ~25% slower, then
+    settles over ~40 ms of continuous work (kernel traces of 600 steps); the
+    timed region starts in the settled state. Between the halves, untimed
+    replays (about COVER_MS of GPU work) keep the GPU busy while the host
+    queues event_window() (the eager, event-timed steps) behind them, so those
+    steps run back to back, in the middle of the timed region and in the same
+    state."""
+    import torch
+    g_full.replay()                                        # untimed: a step-time estimate
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    g_full.replay()
+    torch.cuda.synchronize()
+    est = max(time.perf_counter() - t, 1e-6)
+    for _ in range(max(1, math.ceil(SETTLE_MS * 1e-3 / est))):
+        g_full.replay()
+    torch.cuda.synchronize()
+    half = replays // 2
+    t = time.perf_counter()
+    for _ in range(half):
+        g_full.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t
+    for _ in range(max(1, math.ceil(COVER_MS * 1e-3 / est))):
+        g_full.replay()
+    event_window()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(replays - half):
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    torch.cuda.synchronize()
+    return dt + time.perf_counter() - t
 
 
 def kernel_percentiles(ms_list):
@@ -397,27 +437,11 @@ def measure(name: str, args) -> dict:
         step(0)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)) and torch.equal(lse, ref_lse)
-    g_full.replay()
-    torch.cuda.synchronize()
-
-    t0 = time.perf_counter()
-    for _ in range(replays):
-        g_full.replay()
-    if g_rem is not None:
-        g_rem.replay()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
+    # eager steps, per step: HIP events recorded before and after it on its
+    # stream (the step's duration, with the gaps between its kernels), and the
+    # attention kernel's own start and end timestamps (hipExtLaunchKernel sets
+    # the events the library is given)
     steps = replays * R + rem
-    ms_per_step = dt / steps * 1e3
-    tokens_per_s = T * steps / dt
-
-    # eager steps queued behind a spin kernel: per step, HIP events recorded
-    # before and after it on its stream (the step's duration, with the gaps
-    # between its kernels), and the attention kernel's own start and end
-    # timestamps (hipExtLaunchKernel sets the events the library is given).
-    # WARM_EAGER unmeasured steps run between the spin and the measured ones:
-    # the first launches after the near-idle spin ran up to 15% slower (the
-    # clock coming back), which put the mean kernel time above the graph step.
     n_ev = min(steps, 120)
     mk = lambda: torch.cuda.Event(enable_timing=True)    # noqa: E731
     kev = [(mk(), mk()) for _ in range(n_ev)]
@@ -426,16 +450,19 @@ def measure(name: str, args) -> dict:
         a.record()
         b.record()
     torch.cuda.synchronize()
-    torch.cuda._sleep(50_000_000)
-    for k in range(WARM_EAGER):
-        step(k)
-    for k in range(n_ev):
-        smla.set_timing_events(*kev[k])
-        sev[k][0].record()
-        step(k)
-        sev[k][1].record()
-    smla.set_timing_events(None, None)
-    torch.cuda.synchronize()
+
+    def event_window():
+        for k in range(n_ev):
+            smla.set_timing_events(*kev[k])
+            sev[k][0].record()
+            step(k)
+            sev[k][1].record()
+        smla.set_timing_events(None, None)
+
+    dt = timed_replays(g_full, g_rem, replays, R, event_window)
+    ms_per_step = dt / steps * 1e3
+    tokens_per_s = T * steps / dt
+
     kern_all = [hip_elapsed_ms(a, b) for a, b in kev]
     step_all = [a.elapsed_time(b) for a, b in sev]
     kern_ms = sum(kern_all) / n_ev
@@ -478,7 +505,8 @@ def measure(name: str, args) -> dict:
               "softcap": args.softcap, "sinks": bool(args.sinks), "q_scale": args.q_scale,
               "fp8_prefill": (args.fp8_prefill if entry == "prefill" and spec.kv_format == I.KV_FP8_DS_MLA
                               else None),
-              "timing": "HIP graphs of exactly `steps` steps replayed; cold L2/MALL by cache rotation"}
+              "timing": "HIP graphs of exactly `steps` steps replayed, timed in two halves around the "
+                        "event-timed eager steps; cold L2/MALL by cache rotation"}
     res = {
         "config": config,
         "tokens_per_s": round(tokens_per_s, 1),
@@ -599,29 +627,21 @@ def run_dcp(args) -> int:
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref_o.view(torch.int16)) and torch.equal(lse, ref_l)
     steps = args.steps
-    t0 = time.perf_counter()
-    for _ in range(replays):
-        g.replay()
-    if g_rem is not None:
-        g_rem.replay()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-
-    # the rank's attention kernel alone (kernel timestamps)
+    # the rank's attention kernel alone (kernel timestamps), in the middle of the timed replays
     n_ev = min(steps, 120)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
     for a, b in evs:
         a.record()
         b.record()
     torch.cuda.synchronize()
-    torch.cuda._sleep(50_000_000)
-    for k in range(WARM_EAGER):
-        step(k)
-    for k in range(n_ev):
-        smla.set_timing_events(*evs[k])
-        step(k)
-    smla.set_timing_events(None, None)
-    torch.cuda.synchronize()
+
+    def event_window():
+        for k in range(n_ev):
+            smla.set_timing_events(*evs[k])
+            step(k)
+        smla.set_timing_events(None, None)
+
+    dt = timed_replays(g, g_rem, replays, R, event_window)
     kern_all = [hip_elapsed_ms(a, b) for a, b in evs]
     kern_ms = sum(kern_all) / n_ev
 
