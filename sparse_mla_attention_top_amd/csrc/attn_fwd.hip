@@ -455,12 +455,8 @@ smla_attn_kernel(KParams p) {
     const int kr = 16 * rh + li;
     const int kr8 = S::ROPE_AT + (kr >> 3) * 512 + ((kr & 7) * 4 + (lg ^ (((kr >> 3) & 1) << 1))) * 16;
 
-    // S^T[16 rows x 32 heads] of the wave for tile i (unscaled sums). Lane holds
-    // rows 16rh + 4lg + r (r = 0..3) of heads 32hg + 16nbq + li. Group
-    // format: the k-steps of channel group g = ks / 4 accumulate apart; at the
-    // end of a group its partial sums are scaled by the rows' group scales and
-    // added into t0 / t1 (the wait for those MFMAs is covered by the O-wave on
-    // the same SIMD).
+    // S^T[16 rows x 32 heads] of the wave for tile i (unscaled sums), bf16
+    // cache. Lane holds rows 16rh + 4lg + r (r = 0..3) of heads 32hg + 16nbq + li.
     auto scores = [&](int i, f32x4& r0, f32x4& r1) {
       const lds_char* lb = lat_buf(i);
       const lds_char* rb = rope_buf(i);
@@ -490,19 +486,15 @@ smla_attn_kernel(KParams p) {
       r1 = acc[0][1] + acc[1][1];
     };
     // FP8: per k-pair j one 16-byte read of 16 codes per lane, converted to the
-    // A operands of k-steps 2j (codes 0..7) and 2j+1 (codes 8..15) one pair
-    // ahead of their MFMAs. Accumulator chains acc[set][head block]:
-    //   per-tensor: pair j into sets 0 (k-step 2j) and 1 (k-step 2j+1), 4
-    //     chains (8 measured the same: the O-wave's P.V fills the gaps);
-    //   group formats: group g (pairs 2g, 2g+1) into sets 2 (g & 1) and
-    //     2 (g & 1) + 1. Group g-1's sums are scaled by the rows' group scales
-    //     and folded into t0 / t1 at the end of group g, just before group g+1
-    //     reuses their sets, so that the fold's VALU reads wait as little as
-    //     possible for MFMA results. These reads are still the group formats'
-    //     main cost: with the folds left out (timing only) the QK^T of the
-    //     long-context tile took half as long. A fold's scales are read at the
-    //     start of its iteration, before that iteration's code read (LDS reads
-    //     return in order: waiting for them does not wait for the code read).
+    // A operands of k-steps 2j (codes 0..7) and 2j+1 (codes 8..15).
+    //   per-tensor: each pair converted one pair ahead of its MFMAs, into
+    //     accumulator sets 0 (k-step 2j) and 1 (k-step 2j+1): 4 chains (8
+    //     measured the same: the O-wave's P.V fills the gaps);
+    //   group formats: one accumulator pair per scale group, kept to the end
+    //     of the contraction and then scaled by the rows' group scales (the
+    //     schedule is described at the branch below). Folding each group into
+    //     running sums during the contraction made that VALU wait for MFMA
+    //     results and cost ~4% of the long-context kernel.
     auto scores8 = [&](int i, f32x4& r0, f32x4& r1) {
       const lds_char* tb = tile8(i);
       auto kaddr = [&](auto j_c) -> const lds_char* {
