@@ -338,9 +338,9 @@ def main() -> int:
 
 def measure(name: str, args) -> dict:
     """One workload: HIP graph replays of exactly args.steps steps (whole-job
-    throughput), then per-step and attention-kernel durations from HIP events
-    over eager steps queued behind a spin kernel, the roofline position and
-    the oracle on the host."""
+    throughput, timed in two halves after the clock has settled), per-step and
+    attention-kernel durations from HIP events over eager steps run between
+    the halves, the roofline position and the oracle on the host."""
     import numpy as np
     import torch
 
